@@ -1,0 +1,473 @@
+// hpkv CPU oracle: a plain, slow, deliberately unoptimised statement of what the
+// block-paged KV cache hot path computes. This is TEST INFRASTRUCTURE: only the
+// tests, the smoke check and the CPU-baseline leg of the benchmark may load it.
+// It shares no code, header, table or constant with the HIP library; the two
+// are compared against each other, never built from each other.
+//
+// Sources (web pages, cited by title and section):
+//   [HUR]  "Block-Paged KV Cache" (Hurray format documentation, cookbook):
+//          sections "The three buffers", "Element lookup through the block
+//          table", "Validating the storage invariants".
+//   [INT]  "Paged KV Cache · AI infra interview lesson": sections "Walk the
+//          Shapes First", "Step 1: slot_mapping and store_kvcache",
+//          "Step 2: paged_attention_decode", "Common Pitfalls".
+//   [LLM]  "LLM Inference Engineering & Economics", Chapter 2 (KV cache,
+//          memory hierarchy, continuous batching, and PagedAttention):
+//          sections "What the KV cache actually stores", "Sliding windows,
+//          GQA, and hybrid caches change the equation".
+//
+// Floating point: every score, softmax weight and output is computed in double
+// from inputs widened exactly from their storage type; the result is rounded
+// once, to nearest-even, to the storage type of q.
+//
+// Readings taken where the pages leave a step open (each also listed in the
+// design notes):
+//   * The block table is the CSR pair (block_table, seq_ptr) of [HUR].
+//   * Positions whose logical page is not in the sequence's slice give slot -1.
+//   * Only the first ceil(ctx/page_size) pages of a slice are read ([INT] Step 2
+//     slices the table before indexing); extra pages are ignored.
+//   * ctx_len == 0 gives an all-zero output row (the empty sum of [INT] Step 2).
+//   * A store skips slot -1 and any slot outside [0, num_pages*page_size);
+//     repeated slots resolve last-writer-wins in token order.
+//   * GQA: query head h reads KV head h / (Hq/Hkv) ([INT] Step 2).
+//   * scale multiplies the q.k dot product ([INT] Step 2).
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace {
+
+// Status codes of this oracle (independent of the library's own codes).
+enum : int {
+  ORC_OK = 0,
+  ORC_BAD_ARG = 1,
+  ORC_SEQ_PTR_FIRST = 2,      // seq_ptr[0] != 0
+  ORC_SEQ_PTR_ORDER = 3,      // seq_ptr decreases somewhere
+  ORC_SEQ_PTR_LAST = 4,       // seq_ptr[num_seqs] != block_table length
+  ORC_PAGE_RANGE = 5,         // some block_table entry >= num_pages
+  ORC_CTX_RANGE = 6,          // a context length is negative or exceeds its slice
+  ORC_OUT_OF_RANGE = 7,       // an element lookup coordinate is out of range
+};
+
+// Element storage types understood by the oracle.
+enum : int { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+
+uint64_t read_index(int index_bytes, const void* p, uint64_t i) {
+  if (index_bytes == 4) return static_cast<const uint32_t*>(p)[i];
+  return static_cast<const uint64_t*>(p)[i];
+}
+
+// ---- exact widening of stored elements to double -------------------------
+
+double widen_f32(uint32_t bits) {
+  float f;
+  std::memcpy(&f, &bits, 4);
+  return f;
+}
+
+// bfloat16 is the upper half of an IEEE binary32.
+double widen_bf16(uint16_t bits) { return widen_f32(uint32_t(bits) << 16); }
+
+// IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+double widen_f16(uint16_t bits) {
+  const int sign = bits >> 15;
+  const int expo = (bits >> 10) & 0x1f;
+  const int frac = bits & 0x3ff;
+  double mag;
+  if (expo == 0) {
+    mag = std::ldexp(double(frac), -24);  // subnormal: frac * 2^-24
+  } else if (expo == 31) {
+    mag = frac ? NAN : INFINITY;
+  } else {
+    mag = std::ldexp(double(1024 + frac), expo - 25);
+  }
+  return sign ? -mag : mag;
+}
+
+double load_elem(int dtype, const void* base, uint64_t idx) {
+  if (dtype == ORC_F32) return widen_f32(static_cast<const uint32_t*>(base)[idx]);
+  const uint16_t b = static_cast<const uint16_t*>(base)[idx];
+  return dtype == ORC_BF16 ? widen_bf16(b) : widen_f16(b);
+}
+
+// ---- rounding double -> storage type, to nearest, ties to even -------------
+// A binary floating-point format with `p` significand bits (implicit bit
+// included), smallest normal exponent `emin` and largest exponent `emax`.
+// Values are snapped to the quantum of their binade (the subnormal quantum
+// below 2^emin) with rint, which rounds ties to even in the default mode.
+double round_to_format(double x, int p, int emin, int emax) {
+  if (!std::isfinite(x) || x == 0.0) return x;
+  int e;
+  std::frexp(x, &e);  // |x| in [2^(e-1), 2^e)
+  int lead = e - 1;
+  if (lead < emin) lead = emin;
+  const double quantum = std::ldexp(1.0, lead - (p - 1));
+  const double r = std::rint(x / quantum) * quantum;
+  const double max_finite = std::ldexp(2.0 - std::ldexp(1.0, -(p - 1)), emax);
+  if (std::fabs(r) > max_finite) return std::copysign(INFINITY, x);
+  return r;
+}
+
+uint32_t encode_f32(double x) {
+  const float f = static_cast<float>(round_to_format(x, 24, -126, 127));
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if (std::isnan(x)) u = 0x7fc00000u;
+  return u;
+}
+
+uint16_t encode_bf16(double x) {
+  if (std::isnan(x)) return 0x7fc0;
+  const float f = static_cast<float>(round_to_format(x, 8, -126, 127));  // exact
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+uint16_t encode_f16(double x) {
+  if (std::isnan(x)) return 0x7e00;
+  const double r = round_to_format(x, 11, -14, 15);
+  const uint16_t sign = std::signbit(r) ? 0x8000 : 0;
+  const double a = std::fabs(r);
+  if (std::isinf(a)) return sign | 0x7c00;
+  if (a == 0.0) return sign;
+  int e;
+  std::frexp(a, &e);
+  const int lead = e - 1;
+  if (lead < -14) {  // subnormal: a = frac * 2^-24
+    return sign | static_cast<uint16_t>(std::ldexp(a, 24));
+  }
+  const uint16_t frac = static_cast<uint16_t>(std::ldexp(a, 10 - lead) - 1024.0);
+  return sign | static_cast<uint16_t>((lead + 15) << 10) | frac;
+}
+
+void store_elem(int dtype, void* base, uint64_t idx, double x) {
+  if (dtype == ORC_F32) {
+    static_cast<uint32_t*>(base)[idx] = encode_f32(x);
+  } else if (dtype == ORC_BF16) {
+    static_cast<uint16_t*>(base)[idx] = encode_bf16(x);
+  } else {
+    static_cast<uint16_t*>(base)[idx] = encode_f16(x);
+  }
+}
+
+// Flat page-pool offset of (sequence s, token t, head h, dim e): [HUR] "Element
+// lookup through the block table". The pool is
+// [num_pages, page_size, num_heads, head_dim] row-major; the token's logical
+// page t/page_size is looked up in the sequence's slice of block_table.
+// Returns ORC_OK and writes *flat, or an error code.
+int element_offset(int index_bytes, uint64_t s, uint64_t t, uint64_t h, uint64_t e,
+                   uint64_t page_size, uint64_t num_pages, uint64_t num_heads,
+                   uint64_t head_dim, const void* block_table, uint64_t block_table_len,
+                   const void* seq_ptr, uint64_t num_seqs, uint64_t* flat) {
+  if (page_size == 0 || num_heads == 0 || head_dim == 0) return ORC_BAD_ARG;
+  if (s >= num_seqs || h >= num_heads || e >= head_dim) return ORC_OUT_OF_RANGE;
+  const uint64_t first = read_index(index_bytes, seq_ptr, s);
+  const uint64_t last = read_index(index_bytes, seq_ptr, s + 1);
+  const uint64_t page_in_seq = t / page_size;
+  const uint64_t offset_in_page = t % page_size;
+  if (last < first || page_in_seq >= last - first) return ORC_OUT_OF_RANGE;
+  if (first + page_in_seq >= block_table_len) return ORC_OUT_OF_RANGE;
+  const uint64_t phys = read_index(index_bytes, block_table, first + page_in_seq);
+  if (phys >= num_pages) return ORC_OUT_OF_RANGE;
+  *flat = ((phys * page_size + offset_in_page) * num_heads + h) * head_dim + e;
+  return ORC_OK;
+}
+
+// Row (pool slot) of token t of sequence s: the element offset of (s, t, 0, 0)
+// divided by the row width, i.e. block_table[seq_ptr[s] + t/bs]*bs + t%bs.
+int token_row(int index_bytes, uint64_t s, uint64_t t, uint64_t page_size, uint64_t num_pages,
+              uint64_t num_heads, uint64_t head_dim, const void* block_table,
+              uint64_t block_table_len, const void* seq_ptr, uint64_t num_seqs, uint64_t* row) {
+  uint64_t flat = 0;
+  const int st = element_offset(index_bytes, s, t, 0, 0, page_size, num_pages, num_heads, head_dim,
+                                block_table, block_table_len, seq_ptr, num_seqs, &flat);
+  if (st != ORC_OK) return st;
+  *row = flat / (num_heads * head_dim);
+  return ORC_OK;
+}
+
+struct DecodeArgs {
+  int dtype;
+  int index_bytes;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const void* block_table;
+  uint64_t block_table_len;
+  const void* seq_ptr;
+  const int32_t* context_lens;
+  uint64_t num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, num_pages;
+  double scale;
+  void* out;        // [B, Hq, d] in dtype
+  double* out_f64;  // [B, Hq, d] unrounded, may be null
+};
+
+// One sequence of [INT] "Step 2: paged_attention_decode": gather the first
+// ctx tokens of K and V through the block table, then for every query head
+// take softmax(scale * q.K^T) and weight V with it. Two passes (max, then
+// weighted sums), all in double.
+int decode_one_sequence(const DecodeArgs& a, uint64_t s) {
+  const uint64_t Hq = a.num_q_heads, Hkv = a.num_kv_heads, d = a.head_dim;
+  const uint64_t group = Hq / Hkv;
+  const int32_t n_signed = a.context_lens[s];
+  const uint64_t first = read_index(a.index_bytes, a.seq_ptr, s);
+  const uint64_t last = read_index(a.index_bytes, a.seq_ptr, s + 1);
+  if (n_signed < 0 || last < first) return ORC_CTX_RANGE;
+  const uint64_t n = static_cast<uint64_t>(n_signed);
+  if (n > (last - first) * a.page_size) return ORC_CTX_RANGE;
+
+  std::vector<uint64_t> rows(n);
+  for (uint64_t t = 0; t < n; ++t) {
+    const int st = token_row(a.index_bytes, s, t, a.page_size, a.num_pages, Hkv, d, a.block_table,
+                             a.block_table_len, a.seq_ptr, a.num_seqs, &rows[t]);
+    if (st != ORC_OK) return st;
+  }
+  std::vector<double> z(n), o(d);
+  for (uint64_t h = 0; h < Hq; ++h) {
+    const uint64_t g = h / group;  // consecutive GQA grouping
+    const uint64_t q_base = (s * Hq + h) * d;
+    double zmax = -INFINITY;
+    for (uint64_t t = 0; t < n; ++t) {
+      const uint64_t k_base = (rows[t] * Hkv + g) * d;
+      double dot = 0.0;
+      for (uint64_t e = 0; e < d; ++e)
+        dot += load_elem(a.dtype, a.q, q_base + e) * load_elem(a.dtype, a.k_cache, k_base + e);
+      z[t] = dot * a.scale;
+      zmax = std::max(zmax, z[t]);
+    }
+    double denom = 0.0;
+    std::fill(o.begin(), o.end(), 0.0);
+    for (uint64_t t = 0; t < n; ++t) {
+      const double w = std::exp(z[t] - zmax);
+      denom += w;
+      const uint64_t v_base = (rows[t] * Hkv + g) * d;
+      for (uint64_t e = 0; e < d; ++e) o[e] += w * load_elem(a.dtype, a.v_cache, v_base + e);
+    }
+    for (uint64_t e = 0; e < d; ++e) {
+      const double val = n == 0 ? 0.0 : o[e] / denom;
+      if (a.out) store_elem(a.dtype, a.out, q_base + e, val);
+      if (a.out_f64) a.out_f64[q_base + e] = val;
+    }
+  }
+  return ORC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+// [HUR] "Validating the storage invariants": seq_ptr[0] == 0, seq_ptr never
+// decreases, seq_ptr[num_seqs] equals the block_table length, and every page id
+// is below num_pages. An empty batch (num_seqs == 0, seq_ptr == [0]) passes.
+// When context_lens is given, each length must also be non-negative and fit in
+// its slice (ctx <= pages_in_slice * page_size).
+int orc_validate_index_buffers(int index_bytes, uint64_t num_pages, uint64_t num_seqs,
+                               const void* seq_ptr, const void* block_table,
+                               uint64_t block_table_len, const int32_t* context_lens,
+                               uint64_t page_size) {
+  if ((index_bytes != 4 && index_bytes != 8) || seq_ptr == nullptr) return ORC_BAD_ARG;
+  if (block_table_len > 0 && block_table == nullptr) return ORC_BAD_ARG;
+  if (read_index(index_bytes, seq_ptr, 0) != 0) return ORC_SEQ_PTR_FIRST;
+  for (uint64_t s = 0; s < num_seqs; ++s)
+    if (read_index(index_bytes, seq_ptr, s + 1) < read_index(index_bytes, seq_ptr, s))
+      return ORC_SEQ_PTR_ORDER;
+  if (read_index(index_bytes, seq_ptr, num_seqs) != block_table_len) return ORC_SEQ_PTR_LAST;
+  for (uint64_t k = 0; k < block_table_len; ++k)
+    if (read_index(index_bytes, block_table, k) >= num_pages) return ORC_PAGE_RANGE;
+  if (context_lens != nullptr) {
+    for (uint64_t s = 0; s < num_seqs; ++s) {
+      const uint64_t pages =
+          read_index(index_bytes, seq_ptr, s + 1) - read_index(index_bytes, seq_ptr, s);
+      if (context_lens[s] < 0 || uint64_t(context_lens[s]) > pages * page_size)
+        return ORC_CTX_RANGE;
+    }
+  }
+  return ORC_OK;
+}
+
+// [HUR] "Element lookup through the block table".
+int orc_element_offset(int index_bytes, uint64_t s, uint64_t t, uint64_t h, uint64_t e,
+                       uint64_t page_size, uint64_t num_pages, uint64_t num_heads,
+                       uint64_t head_dim, const void* block_table, uint64_t block_table_len,
+                       const void* seq_ptr, uint64_t num_seqs, uint64_t* flat) {
+  if (block_table == nullptr || seq_ptr == nullptr || flat == nullptr) return ORC_BAD_ARG;
+  if (index_bytes != 4 && index_bytes != 8) return ORC_BAD_ARG;
+  return element_offset(index_bytes, s, t, h, e, page_size, num_pages, num_heads, head_dim,
+                        block_table, block_table_len, seq_ptr, num_seqs, flat);
+}
+
+// [INT] "Step 1": the per-block range emission for one sequence with a plain
+// list of page ids. Positions [start, end) are covered block by block; only
+// the first block may begin part-way in (start % bs) and only the last may end
+// early (end - i*bs). start >= end yields nothing. Returns the number of slots
+// written to out (at most out_cap), or -1 on bad arguments or a missing page.
+int64_t orc_compute_slot_mapping(const int64_t* block_table, int64_t block_table_len,
+                                 int64_t start, int64_t end, int64_t block_size, int64_t* out,
+                                 int64_t out_cap) {
+  if (block_size <= 0 || start < 0) return -1;
+  if (start >= end) return 0;
+  const int64_t start_block = start / block_size;
+  const int64_t end_block = (end + block_size - 1) / block_size;
+  if (end_block > block_table_len) return -1;
+  int64_t count = 0;
+  for (int64_t i = start_block; i < end_block; ++i) {
+    const int64_t base = block_table[i] * block_size;
+    const int64_t lo = (i == start_block) ? start % block_size : 0;
+    const int64_t hi = (i == end_block - 1) ? end - i * block_size : block_size;
+    for (int64_t slot = base + lo; slot < base + hi; ++slot) {
+      if (count >= out_cap) return -1;
+      out[count++] = slot;
+    }
+  }
+  return count;
+}
+
+// [INT] "Walk the Shapes First" / "Step 1" per-token rule over the CSR table:
+// new-token row i of sequence s (cu_new[s] <= i < cu_new[s+1]) sits at position
+// p = start_pos[s] + (i - cu_new[s]), and its slot is
+// block_table[seq_ptr[s] + p/bs]*bs + p%bs. A position whose page is not in the
+// sequence's slice gets -1 (reading: no slot).
+int orc_slot_mapping(int index_bytes, const void* block_table, uint64_t block_table_len,
+                     const void* seq_ptr, uint64_t num_seqs, uint64_t page_size,
+                     const int32_t* start_pos, const int64_t* cu_new, int64_t* slots) {
+  if (page_size == 0 || seq_ptr == nullptr || start_pos == nullptr || cu_new == nullptr)
+    return ORC_BAD_ARG;
+  for (uint64_t s = 0; s < num_seqs; ++s) {
+    const uint64_t first = read_index(index_bytes, seq_ptr, s);
+    const uint64_t last = read_index(index_bytes, seq_ptr, s + 1);
+    for (int64_t i = cu_new[s]; i < cu_new[s + 1]; ++i) {
+      const int64_t p = int64_t(start_pos[s]) + (i - cu_new[s]);
+      int64_t slot = -1;
+      if (p >= 0 && last >= first) {
+        const uint64_t page_in_seq = uint64_t(p) / page_size;
+        if (page_in_seq < last - first && first + page_in_seq < block_table_len) {
+          const uint64_t phys = read_index(index_bytes, block_table, first + page_in_seq);
+          slot = int64_t(phys * page_size + uint64_t(p) % page_size);
+        }
+      }
+      slots[i] = slot;
+    }
+  }
+  return ORC_OK;
+}
+
+// [INT] "Step 1": store_kvcache. The caches are viewed as
+// [num_pages*page_size, num_heads*head_dim]; every new-token row whose slot is
+// not -1 is copied bit for bit into that slot, for K and for V. Token order,
+// last writer wins. Slots outside the pool are skipped and counted.
+int64_t orc_store_kvcache(uint64_t elem_size, const void* key, const void* value, void* k_cache,
+                          void* v_cache, const int64_t* slots, uint64_t num_tokens,
+                          uint64_t page_size, uint64_t num_pages, uint64_t num_heads,
+                          uint64_t head_dim) {
+  const uint64_t row_bytes = num_heads * head_dim * elem_size;
+  const int64_t num_slots = int64_t(num_pages * page_size);
+  int64_t skipped_invalid = 0;
+  for (uint64_t i = 0; i < num_tokens; ++i) {
+    const int64_t slot = slots[i];
+    if (slot == -1) continue;
+    if (slot < 0 || slot >= num_slots) {
+      ++skipped_invalid;
+      continue;
+    }
+    std::memcpy(static_cast<char*>(k_cache) + uint64_t(slot) * row_bytes,
+                static_cast<const char*>(key) + i * row_bytes, row_bytes);
+    std::memcpy(static_cast<char*>(v_cache) + uint64_t(slot) * row_bytes,
+                static_cast<const char*>(value) + i * row_bytes, row_bytes);
+  }
+  return skipped_invalid;
+}
+
+// [INT] "Step 2": paged_attention_decode for a batch, one query per sequence.
+// q and out are [B, Hq, d]; the caches are [num_pages, page_size, Hkv, d].
+// `out` (storage dtype, nullable) receives the rounded result and `out_f64`
+// (nullable) the unrounded double result. Sequences are spread round-robin over
+// `num_threads` host threads (a timing convenience; each sequence is computed
+// by the same single-threaded routine). Returns ORC_OK or the first error.
+int orc_paged_attention_decode(int dtype, int index_bytes, const void* q, const void* k_cache,
+                               const void* v_cache, const void* block_table,
+                               uint64_t block_table_len, const void* seq_ptr,
+                               const int32_t* context_lens, uint64_t num_seqs,
+                               uint64_t num_q_heads, uint64_t num_kv_heads, uint64_t head_dim,
+                               uint64_t page_size, uint64_t num_pages, double scale, void* out,
+                               double* out_f64, int num_threads) {
+  if (dtype != ORC_F32 && dtype != ORC_F16 && dtype != ORC_BF16) return ORC_BAD_ARG;
+  if (index_bytes != 4 && index_bytes != 8) return ORC_BAD_ARG;
+  if (num_kv_heads == 0 || head_dim == 0 || page_size == 0) return ORC_BAD_ARG;
+  if (num_q_heads % num_kv_heads != 0) return ORC_BAD_ARG;
+  DecodeArgs a{dtype,       index_bytes,  q,           k_cache,      v_cache,
+               block_table, block_table_len, seq_ptr, context_lens, num_seqs,
+               num_q_heads, num_kv_heads, head_dim,    page_size,    num_pages,
+               scale,       out,          out_f64};
+  if (num_threads < 1) num_threads = 1;
+  std::vector<int> status(num_threads, ORC_OK);
+  auto work = [&](int k) {
+    for (uint64_t s = uint64_t(k); s < num_seqs; s += uint64_t(num_threads)) {
+      const int st = decode_one_sequence(a, s);
+      if (st != ORC_OK && status[k] == ORC_OK) status[k] = st;
+    }
+  };
+  if (num_threads == 1) {
+    work(0);
+  } else {
+    std::vector<std::thread> pool;
+    for (int k = 0; k < num_threads; ++k) pool.emplace_back(work, k);
+    for (auto& th : pool) th.join();
+  }
+  for (int st : status)
+    if (st != ORC_OK) return st;
+  return ORC_OK;
+}
+
+// Textbook softmax attention for one query over K/V held contiguously
+// ([L, Hkv, d], token-major, never read through a page pool): the dense
+// reference that [INT] "Step 2" checks the paged gather against. Query head h
+// reads KV head h / (Hq/Hkv). q is [Hq, d]; out is [Hq, d] in double.
+int orc_dense_attention(int dtype, const void* q, const void* K, const void* V, uint64_t L,
+                        uint64_t num_q_heads, uint64_t num_kv_heads, uint64_t head_dim,
+                        double scale, double* out) {
+  if (num_kv_heads == 0 || num_q_heads % num_kv_heads != 0) return ORC_BAD_ARG;
+  const uint64_t group = num_q_heads / num_kv_heads;
+  std::vector<double> logits(L), weights(L);
+  for (uint64_t h = 0; h < num_q_heads; ++h) {
+    const uint64_t g = h / group;
+    for (uint64_t t = 0; t < L; ++t) {
+      double acc = 0.0;
+      for (uint64_t e = 0; e < head_dim; ++e)
+        acc += load_elem(dtype, q, h * head_dim + e) *
+               load_elem(dtype, K, (t * num_kv_heads + g) * head_dim + e);
+      logits[t] = acc * scale;
+    }
+    double m = -INFINITY;
+    for (uint64_t t = 0; t < L; ++t) m = std::max(m, logits[t]);
+    double total = 0.0;
+    for (uint64_t t = 0; t < L; ++t) {
+      weights[t] = std::exp(logits[t] - m);
+      total += weights[t];
+    }
+    for (uint64_t e = 0; e < head_dim; ++e) {
+      double acc = 0.0;
+      for (uint64_t t = 0; t < L; ++t)
+        acc += weights[t] * load_elem(dtype, V, (t * num_kv_heads + g) * head_dim + e);
+      out[h * head_dim + e] = L == 0 ? 0.0 : acc / total;
+    }
+  }
+  return ORC_OK;
+}
+
+// Rounds doubles to a storage type (exposed so tests can pin the rounding on
+// its own: ties-to-even, subnormals, overflow to infinity).
+void orc_round_to_dtype(int dtype, const double* x, uint64_t n, void* out) {
+  for (uint64_t i = 0; i < n; ++i) store_elem(dtype, out, i, x[i]);
+}
+
+// Widens stored elements to double (pinned the same way).
+void orc_widen_dtype(int dtype, const void* x, uint64_t n, double* out) {
+  for (uint64_t i = 0; i < n; ++i) out[i] = load_elem(dtype, x, i);
+}
+
+}  // extern "C"
