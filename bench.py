@@ -1,0 +1,265 @@
+"""Throughput of the block-paged KV cache hot path on one MI355X.
+
+A step is one pass of the whole path over one synthetic batch (one layer):
+slot mapping of the new tokens, store of their K/V rows into the page pools,
+then paged decode attention of every sequence (partition + reduce kernels).
+Default workload: the Llama-2-7B-shaped layer (Hq = Hkv = 32, d = 128,
+16-token pages, 64 sequences with ctx ~ U{512..4096}, bf16, u32 tables), one
+new token per sequence stored at position ctx-1 before decoding.
+
+Printed: ONE JSON line with
+  value        KV bytes the decode must read per step (sum ctx * 2 * Hkv * d * b)
+               divided by the step time, in GB/s (1e9 B/s);
+  roofline     the partition kernel alone (the dominant kernel), timed per
+               launch with HIP events on the launch stream: algorithmic bytes
+               per launch (KV + q + out + block-table entries + lengths)
+               over its mean duration, against the 8 TB/s HBM peak;
+  cpu_baseline the CPU oracle (double precision, plain loops) running the same
+               step on host copies of the same inputs, timed on the host.
+Inputs are resident in HBM before timing starts; nothing is skipped inside the
+timed region.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode: achieved KV HBM GB/s (% of peak) + sequences/s per layer"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_hpkv_amd", "csrc", "hpkv_decode.hip")
+
+WORKLOAD_TEXT = {
+    "llama7b": "Llama-2-7B-shaped layer decode step: Hq=Hkv=32, d=128, bs=16, 64 seqs, "
+               "ctx~U{512..4096}",
+    "gqa": "GQA layer decode step: Hq=32, Hkv=8, d=128, bs=16, 256 seqs, ctx log-U[128,8192]",
+    "qwen3": "Qwen3-0.6B-shaped layer decode step: Hq=16, Hkv=8, d=128, bs=256, 128 seqs, "
+             "ctx~U{1..16384}, 5% dropped slots",
+    "prefix": "prefix-sharing layer: 32 groups x 16 seqs share 2048-token prefixes, chunked "
+              "prefill of U{64..1024}-token tails, then decode",
+    "tiny": "tiny fp32 step: bs=4, Hq=4, Hkv=2, d=8, ctx [1,4,11]",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="llama7b", choices=sorted(workloads.WORKLOADS))
+    p.add_argument("--dtype", default=None, choices=["bf16", "f16", "f32"])
+    p.add_argument("--index", default=None, choices=["u32", "u64"])
+    p.add_argument("--roofline-launches", type=int, default=50)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    return p.parse_args()
+
+
+def make_workload(args):
+    w = workloads.WORKLOADS[args.workload]()
+    if args.dtype:
+        w = w.with_dtype(args.dtype)
+    if args.index:
+        w = w.with_index(args.index)
+    return w
+
+
+class Step:
+    """Pre-allocated device state for repeated steps of one workload."""
+
+    def __init__(self, w, t):
+        import paged_kv_cache_hpkv_amd as hpkv
+        self.hpkv, self.w, self.t = hpkv, w, t
+        dev = t.q.device
+        self.bt = torch.from_numpy(w.block_table).to(dev)
+        self.sp = torch.from_numpy(w.seq_ptr).to(dev)
+        self.ctx = torch.from_numpy(w.context_lens).to(dev)
+        self.chunks = [(torch.from_numpy(s).to(dev), torch.from_numpy(c).to(dev),
+                        torch.empty(int(c[-1]), dtype=torch.int64, device=dev))
+                       for s, c in w.chunks]
+        self.drop = None if w.drop_mask is None else torch.from_numpy(w.drop_mask).to(dev)
+        self.out = torch.empty_like(t.q)
+        self.ws = hpkv.alloc_workspace(t.q, t.k_cache, w.max_context_len)
+
+    def __call__(self):
+        h, w, t = self.hpkv, self.w, self.t
+        for c, (start, cu, slots) in enumerate(self.chunks):
+            h.hpkv_slot_mapping(self.bt, self.sp, w.page_size, start, cu, slots)
+            if self.drop is not None and c == 0:
+                slots.masked_fill_(self.drop, -1)
+            h.hpkv_store_kvcache(t.new_keys[c], t.new_values[c], t.k_cache, t.v_cache, slots)
+        h.hpkv_paged_attention_decode(t.q, t.k_cache, t.v_cache, self.bt, self.sp, self.ctx,
+                                      w.scale, w.max_context_len, self.ws, self.out)
+
+    def partitions_only(self):
+        w, t = self.w, self.t
+        self.hpkv.hpkv_paged_attention_decode_partitions(
+            t.q, t.k_cache, t.v_cache, self.bt, self.sp, self.ctx, w.scale, w.max_context_len,
+            self.ws, self.out)
+
+
+def algorithmic_decode_bytes(w):
+    """Bytes the partition kernel must move: KV rows, q, out, table entries, lengths."""
+    b = torch.tensor([], dtype=w.torch_dtype).element_size()
+    idx = w.block_table.dtype.itemsize
+    ctx = w.context_lens.astype(np.int64)
+    pages = -(-ctx // w.page_size)
+    per_seq = 2 * w.num_q_heads * w.head_dim * b + 4 + 2 * idx
+    return int(w.kv_bytes_logical() + pages.sum() * idx + per_seq * w.num_seqs)
+
+
+def recorded_traffic():
+    """HBM bytes per partition launch from committed counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(DECODE_SRC, "rb") as f:
+            src_hash = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != src_hash:
+        return None
+    return rec
+
+
+def cpu_baseline(w, t, out_gpu):
+    """The oracle on the same step (host copies), all host threads."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from paths import decode_errors, host_bits, host_threads, oracle_step  # noqa: E402
+    # host copies of the step's inputs (the store already ran on the GPU, so
+    # the pools hold the post-store state; the oracle's store rewrites the
+    # same rows with the same bits)
+    h = dict(q=host_bits(t.q), k_cache=host_bits(t.k_cache), v_cache=host_bits(t.v_cache),
+             new_keys=[host_bits(x) for x in t.new_keys],
+             new_values=[host_bits(x) for x in t.new_values])
+    threads = host_threads()
+    t0 = time.perf_counter()
+    _, _, out64 = oracle_step(w, h, threads)
+    dt = time.perf_counter() - t0
+    max_err, ratio, finite = decode_errors(w.dtype, host_bits(out_gpu), out64)
+    return dict(value=round(w.kv_bytes_logical() / dt / 1e9, 4), unit="GB/s", cores=threads,
+                kind="oracle",
+                sample=f"the full timed step (slot mapping, store, decode of all {w.num_seqs} "
+                       f"sequences) once, double precision, {threads} host threads, "
+                       f"{dt:.2f} s"), dict(max_abs_err=max_err, within_tolerance=ratio <= 1.0
+                                            and finite)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has "
+              "no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_workload(args)
+    t = workloads.make_tensors(w, dev)
+    step = Step(w, t)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # dominant kernel alone: per-launch HIP events on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.roofline_launches)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.roofline_launches)]
+    for i in range(args.roofline_launches):
+        starts[i].record(stream)
+        step.partitions_only()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    part_ms = float(np.mean(durs))
+    alg = algorithmic_decode_bytes(w)
+    achieved = alg / (part_ms * 1e-3) / 1e9
+    step()  # leave `out` holding a full decode for the parity check below
+    torch.cuda.synchronize()
+
+    kv = w.kv_bytes_logical()
+    value = kv / (ms_per_step * 1e-3) / 1e9
+    rec = recorded_traffic()
+    b = torch.tensor([], dtype=w.torch_dtype).element_size()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_TEXT.get(w.name, w.name),
+            "global_batch": w.num_seqs,
+            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "page_size": w.page_size, "index": w.index,
+            "sum_ctx_tokens": int(w.context_lens.astype(np.int64).sum()),
+            "kv_bytes_per_step": kv,
+            "kv_bytes_unique_pages": w.kv_bytes_unique() if w.name == "prefix" else kv,
+            "bytes_per_elem": b,
+            "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "sequences_per_s_per_layer": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+            "wall_s_timed_region": round(t_wall, 4),
+        },
+        "roofline": {
+            "kernel": "decode_partition_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if rec is None else rec.get("hbm_bytes_per_launch"),
+            "algorithmic_bytes_per_launch": alg,
+            "mean_launch_ms": round(part_ms, 5),
+            "launches": args.roofline_launches,
+        },
+    }
+    if rec is not None:
+        line["roofline"]["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)"
+    if not args.no_cpu_baseline:
+        cb, parity = cpu_baseline(w, t, step.out)
+        line["cpu_baseline"] = cb
+        line["parity_vs_oracle"] = parity
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

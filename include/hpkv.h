@@ -1,0 +1,245 @@
+/*
+ * hpkv — block-paged KV cache hot path for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libhpkv.so. Plain pointers and sizes only.
+ *
+ * Data model ("Block-Paged KV Cache", Hurray format documentation, section
+ * "The three buffers"):
+ *   page pool    K and V each [num_pages, page_size, num_kv_heads, head_dim],
+ *                row-major, fully packed, one layer. A "slot" is one token row
+ *                of the pool: slot = page * page_size + offset_in_page, and the
+ *                row holds num_kv_heads * head_dim elements.
+ *   block_table  physical page id of every logical page, all sequences
+ *                concatenated (CSR); element type u32 or u64 (index_type).
+ *   seq_ptr      num_seqs + 1 offsets into block_table, same element type;
+ *                sequence s owns block_table[seq_ptr[s] .. seq_ptr[s+1]).
+ * Token t of sequence s lives in slot
+ *   block_table[seq_ptr[s] + t / page_size] * page_size + t % page_size
+ * ("Block-Paged KV Cache", section "Element lookup through the block table";
+ * "Paged KV Cache · AI infra interview lesson", section "Walk the Shapes
+ * First"). Two table entries may name the same page (shared prefixes); reads
+ * through aliased entries see the same bytes.
+ *
+ * Conventions for every entry point:
+ *   - Return value: HPKV_OK (0) or a negative hpkv_status. Argument checks run
+ *     on the host before any HIP call; on error nothing is launched and no
+ *     output is touched.
+ *   - Device entry points take device pointers owned by the caller and enqueue
+ *     work on `stream` (a hipStream_t; NULL means the null stream). They
+ *     return once the work is enqueued; they never allocate, free or
+ *     synchronise. Launch failures are reported as HPKV_ERR_HIP.
+ *   - Host entry points (validate, element offset) take host pointers and
+ *     never touch the GPU.
+ *   - Contents of device index buffers are not checked by the device entry
+ *     points (call hpkv_validate_index_buffers on host copies first, as the
+ *     Hurray page recommends before shipping a descriptor). The kernels still
+ *     never read or write outside the buffers described by the sizes passed;
+ *     malformed contents give the documented fallback results below.
+ */
+#ifndef HPKV_H_
+#define HPKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HPKV_OK = 0,
+  HPKV_ERR_NULL = -1,          /* a required pointer is NULL */
+  HPKV_ERR_INVALID_ARG = -2,   /* a size or enum argument is out of range */
+  HPKV_ERR_INVALID_INDEX = -3, /* index buffer contents break an invariant (host checks) */
+  HPKV_ERR_UNSUPPORTED = -4,   /* valid but not implemented (e.g. head_dim shape) */
+  HPKV_ERR_HIP = -5,           /* the HIP runtime reported an error at launch */
+  HPKV_ERR_WORKSPACE = -6      /* workspace missing or too small */
+} hpkv_status;
+
+/* Element type of block_table and seq_ptr ("Block-Paged KV Cache", section
+ * "Building a descriptor": 32-bit indices, or 64-bit for huge pools). */
+typedef enum { HPKV_INDEX_U32 = 0, HPKV_INDEX_U64 = 1 } hpkv_index_type;
+
+/* Element type of q, out, new K/V rows and the page pools. */
+typedef enum { HPKV_F32 = 0, HPKV_F16 = 1, HPKV_BF16 = 2 } hpkv_dtype;
+
+/* Static description of a status code (never NULL). */
+const char* hpkv_status_string(int status);
+
+/* ---------------------------------------------------------------------------
+ * hpkv_validate_index_buffers  (host)
+ *
+ * Checks the storage invariants of "Block-Paged KV Cache", section
+ * "Validating the storage invariants": seq_ptr[0] == 0, seq_ptr
+ * non-decreasing, seq_ptr[num_seqs] == block_table_len, and every
+ * block_table entry < num_pages. num_seqs == 0 with seq_ptr == {0} is valid.
+ * When context_lens (host, num_seqs entries) is non-NULL, each length must
+ * also satisfy 0 <= ctx <= (seq_ptr[s+1] - seq_ptr[s]) * page_size.
+ *   seq_ptr      host, num_seqs + 1 entries of index_type
+ *   block_table  host, block_table_len entries (may be NULL if len == 0)
+ * Returns HPKV_OK, HPKV_ERR_INVALID_INDEX on a broken invariant, or an
+ * argument error.
+ * ------------------------------------------------------------------------- */
+int hpkv_validate_index_buffers(int index_type, uint64_t num_pages, uint64_t num_seqs,
+                                const void* seq_ptr, const void* block_table,
+                                uint64_t block_table_len, const int32_t* context_lens,
+                                uint32_t page_size);
+
+/* ---------------------------------------------------------------------------
+ * hpkv_element_offset  (host)
+ *
+ * Flat page-pool offset (in elements) of logical element
+ * (sequence s, token t, head h, dim d):
+ *   ((block_table[seq_ptr[s] + t/page_size] * page_size + t%page_size)
+ *      * num_heads + h) * head_dim + d
+ * ("Block-Paged KV Cache", section "Element lookup through the block table").
+ * Host pointers. Writes *flat_out and returns HPKV_OK, or returns
+ * HPKV_ERR_INVALID_INDEX when s, the token's page, h, d or the page id is out
+ * of range.
+ * ------------------------------------------------------------------------- */
+int hpkv_element_offset(int index_type, uint64_t s, uint64_t t, uint32_t h, uint32_t d,
+                        uint32_t page_size, uint64_t num_pages, uint32_t num_heads,
+                        uint32_t head_dim, const void* block_table, uint64_t block_table_len,
+                        const void* seq_ptr, uint64_t num_seqs, uint64_t* flat_out);
+
+/* ---------------------------------------------------------------------------
+ * hpkv_validate_shape  (host)
+ *
+ * The logical tensor of a block-paged cache is rank 3,
+ * [total_tokens, num_heads, head_dim] ("Block-Paged KV Cache", section
+ * "Building a descriptor"). Returns HPKV_OK for rank 3 with non-zero heads and
+ * dims, HPKV_ERR_INVALID_ARG otherwise. dims: host array of `rank` entries.
+ * ------------------------------------------------------------------------- */
+int hpkv_validate_shape(uint32_t rank, const uint64_t* dims);
+
+/* ---------------------------------------------------------------------------
+ * hpkv_slot_mapping  (device)
+ *
+ * Pool slot of every new token ("Paged KV Cache · AI infra interview lesson",
+ * section "Step 1: slot_mapping and store_kvcache", and "Walk the Shapes
+ * First"): new-token row i of sequence s, cu_new[s] <= i < cu_new[s+1], is at
+ * position p = start_pos[s] + (i - cu_new[s]) and gets
+ *   slots[i] = block_table[seq_ptr[s] + p/page_size] * page_size + p%page_size.
+ * A chunk may start part-way into a page (prefix hit, second half of a
+ * chunked prefill). A position whose page is not in the sequence's slice, or
+ * whose block_table index is >= block_table_len, gets -1 (the skip value).
+ *   block_table  device, block_table_len entries of index_type
+ *   seq_ptr      device, num_seqs + 1 entries of index_type
+ *   start_pos    device int32 [num_seqs]
+ *   cu_new       device int64 [num_seqs + 1], cu_new[0] == 0,
+ *                non-decreasing, cu_new[num_seqs] == num_new
+ *   slots        device int64 [num_new], written
+ * num_seqs == 0 or num_new == 0 launches nothing.
+ * ------------------------------------------------------------------------- */
+int hpkv_slot_mapping(int index_type, const void* block_table, uint64_t block_table_len,
+                      const void* seq_ptr, uint32_t num_seqs, uint32_t page_size,
+                      const int32_t* start_pos, const int64_t* cu_new, uint64_t num_new,
+                      int64_t* slots, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * hpkv_store_kvcache  (device)
+ *
+ * Scatter of freshly computed rows into the pools ("Paged KV Cache · AI infra
+ * interview lesson", section "Step 1: slot_mapping and store_kvcache"): for
+ * every i < num_tokens with slots[i] != -1, K row i (num_kv_heads*head_dim
+ * elements of key) is copied bit for bit to slot slots[i] of k_cache, and
+ * likewise value -> v_cache. Slots < 0 or >= num_pages*page_size are skipped.
+ * Two rows with the same slot race (undefined which one lands); callers must
+ * not alias writable slots.
+ *   key, value        device [num_tokens, num_kv_heads, head_dim] of dtype
+ *   k_cache, v_cache  device [num_pages, page_size, num_kv_heads, head_dim]
+ *   slots             device int64 [num_tokens]
+ * num_tokens == 0 launches nothing.
+ * ------------------------------------------------------------------------- */
+int hpkv_store_kvcache(int dtype, const void* key, const void* value, void* k_cache,
+                       void* v_cache, const int64_t* slots, uint64_t num_tokens,
+                       uint32_t page_size, uint64_t num_pages, uint32_t num_kv_heads,
+                       uint32_t head_dim, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * hpkv_paged_attention_decode_workspace_size  (host)
+ *
+ * Bytes of device workspace hpkv_paged_attention_decode needs for a batch of
+ * num_seqs sequences no longer than max_context_len tokens (the split-context
+ * partials: one fp32 (max, sum) pair and one fp32 head_dim vector per
+ * sequence, query head and context partition). 0 on invalid arguments.
+ * ------------------------------------------------------------------------- */
+size_t hpkv_paged_attention_decode_workspace_size(int dtype, uint32_t num_seqs,
+                                                  uint32_t num_q_heads, uint32_t head_dim,
+                                                  uint32_t page_size, uint32_t max_context_len);
+
+/* Context tokens covered by one split-context partition (a library constant
+ * for the given arguments; exposed for accounting and tests). */
+uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t head_dim,
+                                                      uint32_t page_size);
+
+/* ---------------------------------------------------------------------------
+ * hpkv_paged_attention_decode  (device)
+ *
+ * Single-query paged decode attention ("Paged KV Cache · AI infra interview
+ * lesson", section "Step 2: paged_attention_decode"; the cached step
+ * Attn(q_t, [K_1..t], [V_1..t]) of "LLM Inference Engineering & Economics",
+ * Chapter 2, section "What the KV cache actually stores"). For every
+ * sequence s and query head h, with n = context_lens[s] and KV head
+ * g = h / (num_q_heads / num_kv_heads) (GQA, consecutive grouping):
+ *   z_t   = scale * dot(q[s,h,:], K[token t of s, g, :])      t < n
+ *   out[s,h,:] = sum_t softmax(z)_t * V[token t of s, g, :]
+ * K/V rows are gathered through the block table; only the first
+ * ceil(n/page_size) pages of the slice and only rows t < n are read (rows past
+ * the context in the last page are never loaded, so their contents, NaN
+ * included, do not matter). n == 0 gives zeros.
+ * Arithmetic: fp32 dot products and online softmax, fp32 accumulation, one
+ * rounding (nearest-even) to dtype at the end.
+ *   q, out            device [num_seqs, num_q_heads, head_dim] of dtype
+ *   k_cache, v_cache  device pools of dtype
+ *   block_table, seq_ptr  device, as above
+ *   context_lens      device int32 [num_seqs]
+ *   max_context_len   host upper bound of context_lens (sizes the launch)
+ *   workspace         device, >= hpkv_paged_attention_decode_workspace_size
+ *                     bytes (contents need no initialisation)
+ * Requirements: q, k_cache, v_cache and workspace 16-byte aligned
+ * (HPKV_ERR_INVALID_ARG otherwise); num_q_heads % num_kv_heads == 0;
+ * head_dim * sizeof(dtype) a
+ * multiple of 16 bytes with head_dim * sizeof(dtype) / 16 a power of two
+ * <= 64 (bf16/f16: head_dim in {8,16,32,64,128,256}; f32: {4,...,256}),
+ * otherwise HPKV_ERR_UNSUPPORTED.
+ * Malformed contents (caller error): a sequence with n < 0,
+ * n > max_context_len, n beyond its slice, or a page id >= num_pages in the
+ * pages it reads, gets NaN in all its outputs.
+ * Two kernels are enqueued: the split-context partition pass, then the
+ * log-sum-exp reduce (skipped per sequence when one partition covers it).
+ * ------------------------------------------------------------------------- */
+int hpkv_paged_attention_decode(int dtype, int index_type, const void* q, const void* k_cache,
+                                const void* v_cache, const void* block_table,
+                                uint64_t block_table_len, const void* seq_ptr,
+                                const int32_t* context_lens, uint32_t num_seqs,
+                                uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                                uint32_t page_size, uint64_t num_pages, float scale,
+                                uint32_t max_context_len, void* workspace, size_t workspace_bytes,
+                                void* out, void* stream);
+
+/* The two launches of hpkv_paged_attention_decode, separately: the partition
+ * pass (writes `out` for sequences covered by one partition, partials for the
+ * rest) and the reduce (merges the partials into `out`). Calling them in this
+ * order on one stream with the same arguments is equivalent to
+ * hpkv_paged_attention_decode. Used to time the kernels one by one. */
+int hpkv_paged_attention_decode_partitions(int dtype, int index_type, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const void* block_table, uint64_t block_table_len,
+                                           const void* seq_ptr, const int32_t* context_lens,
+                                           uint32_t num_seqs, uint32_t num_q_heads,
+                                           uint32_t num_kv_heads, uint32_t head_dim,
+                                           uint32_t page_size, uint64_t num_pages, float scale,
+                                           uint32_t max_context_len, void* workspace,
+                                           size_t workspace_bytes, void* out, void* stream);
+int hpkv_paged_attention_decode_reduce(int dtype, const int32_t* context_lens, uint32_t num_seqs,
+                                       uint32_t num_q_heads, uint32_t head_dim,
+                                       uint32_t page_size, uint32_t max_context_len,
+                                       void* workspace, size_t workspace_bytes, void* out,
+                                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HPKV_H_ */

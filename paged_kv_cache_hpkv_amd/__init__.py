@@ -1,0 +1,244 @@
+"""Python binding of libhpkv.so, the gfx950 block-paged KV cache library.
+
+Argument marshalling only: every function below forwards to the C entry point
+of the same name declared in include/hpkv.h, passing tensor data pointers,
+sizes read from tensor shapes and the current HIP stream. All computation runs
+in the library's HIP kernels; there is no CPU fallback. Importing works
+without a GPU (the library loads; host-only helpers run), but the library must
+have been built: a missing libhpkv.so raises at import.
+
+Device tensors are torch tensors on a ROCm device. Index tensors
+(block_table, seq_ptr) may be 32- or 64-bit (signed or unsigned); their width
+selects HPKV_INDEX_U32 / HPKV_INDEX_U64.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhpkv.so")
+
+OK = 0
+ERR_NULL = -1
+ERR_INVALID_ARG = -2
+ERR_INVALID_INDEX = -3
+ERR_UNSUPPORTED = -4
+ERR_HIP = -5
+ERR_WORKSPACE = -6
+
+F32, F16, BF16 = 0, 1, 2
+INDEX_U32, INDEX_U64 = 0, 1
+
+_DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+
+EXPORTED = [
+    "hpkv_status_string", "hpkv_validate_index_buffers", "hpkv_element_offset",
+    "hpkv_validate_shape", "hpkv_slot_mapping", "hpkv_store_kvcache",
+    "hpkv_paged_attention_decode_workspace_size", "hpkv_paged_attention_decode_partition_tokens",
+    "hpkv_paged_attention_decode", "hpkv_paged_attention_decode_partitions",
+    "hpkv_paged_attention_decode_reduce",
+]
+
+
+class HpkvError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python paged_kv_cache_hpkv_amd/build.py` (there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, u32, u64, f32 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint64,
+                              ctypes.c_float)
+    sz = ctypes.c_size_t
+    sig = {
+        "hpkv_status_string": ([i32], ctypes.c_char_p),
+        "hpkv_validate_index_buffers": ([i32, u64, u64, vp, vp, u64, vp, u32], i32),
+        "hpkv_element_offset": ([i32, u64, u64, u32, u32, u32, u64, u32, u32, vp, u64, vp, u64,
+                                 vp], i32),
+        "hpkv_validate_shape": ([u32, vp], i32),
+        "hpkv_slot_mapping": ([i32, vp, u64, vp, u32, u32, vp, vp, u64, vp, vp], i32),
+        "hpkv_store_kvcache": ([i32, vp, vp, vp, vp, vp, u64, u32, u64, u32, u32, vp], i32),
+        "hpkv_paged_attention_decode_workspace_size": ([i32, u32, u32, u32, u32, u32], sz),
+        "hpkv_paged_attention_decode_partition_tokens": ([i32, u32, u32], u32),
+        "hpkv_paged_attention_decode": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, u32, u32, u32,
+                                         u32, u32, u64, f32, u32, vp, sz, vp, vp], i32),
+        "hpkv_paged_attention_decode_partitions": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, u32,
+                                                    u32, u32, u32, u32, u64, f32, u32, vp, sz,
+                                                    vp, vp], i32),
+        "hpkv_paged_attention_decode_reduce": ([i32, vp, u32, u32, u32, u32, u32, vp, sz, vp, vp],
+                                               i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.hpkv_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != OK:
+        raise HpkvError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    dev = next((t.device for t in tensors if t is not None and t.is_cuda), None)
+    if dev is None:
+        raise ValueError("device entry points need tensors on a ROCm device")
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _index_type(t):
+    if t.element_size() == 4:
+        return INDEX_U32
+    if t.element_size() == 8:
+        return INDEX_U64
+    raise TypeError(f"index tensors must be 32- or 64-bit, got {t.dtype}")
+
+
+def _contig(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors passed to libhpkv must be contiguous")
+
+
+# ---------------------------------------------------------------- host helpers
+
+def _np_ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def hpkv_validate_index_buffers(seq_ptr, block_table, num_pages, context_lens=None, page_size=0):
+    """Host check of the storage invariants; returns the status code."""
+    import numpy as np
+    seq_ptr = np.ascontiguousarray(seq_ptr)
+    block_table = np.ascontiguousarray(block_table, dtype=seq_ptr.dtype)
+    it = INDEX_U64 if seq_ptr.dtype.itemsize == 8 else INDEX_U32
+    ctx = None if context_lens is None else np.ascontiguousarray(context_lens, dtype=np.int32)
+    return lib.hpkv_validate_index_buffers(it, num_pages, len(seq_ptr) - 1, _np_ptr(seq_ptr),
+                                           _np_ptr(block_table), len(block_table), _np_ptr(ctx),
+                                           page_size)
+
+
+def hpkv_element_offset(s, t, h, d, page_size, num_pages, num_heads, head_dim, block_table,
+                        seq_ptr):
+    """Host lookup of one element's flat pool offset: (status, offset)."""
+    import numpy as np
+    seq_ptr = np.ascontiguousarray(seq_ptr)
+    block_table = np.ascontiguousarray(block_table, dtype=seq_ptr.dtype)
+    it = INDEX_U64 if seq_ptr.dtype.itemsize == 8 else INDEX_U32
+    out = ctypes.c_uint64(0)
+    st = lib.hpkv_element_offset(it, s, t, h, d, page_size, num_pages, num_heads, head_dim,
+                                 _np_ptr(block_table), len(block_table), _np_ptr(seq_ptr),
+                                 len(seq_ptr) - 1, ctypes.byref(out))
+    return st, int(out.value)
+
+
+def hpkv_validate_shape(dims):
+    arr = (ctypes.c_uint64 * max(1, len(dims)))(*dims)
+    return lib.hpkv_validate_shape(len(dims), arr)
+
+
+def hpkv_paged_attention_decode_workspace_size(dtype, num_seqs, num_q_heads, head_dim, page_size,
+                                               max_context_len):
+    return int(lib.hpkv_paged_attention_decode_workspace_size(
+        _DTYPE_CODE[dtype], num_seqs, num_q_heads, head_dim, page_size, max_context_len))
+
+
+def hpkv_paged_attention_decode_partition_tokens(dtype, head_dim, page_size):
+    return int(lib.hpkv_paged_attention_decode_partition_tokens(_DTYPE_CODE[dtype], head_dim,
+                                                                page_size))
+
+
+# -------------------------------------------------------------- device entry points
+
+def hpkv_slot_mapping(block_table, seq_ptr, page_size, start_pos, cu_new, slots, stream=None):
+    """slots[i] for every new token (int64, -1 where the page is missing)."""
+    _contig(block_table, seq_ptr, start_pos, cu_new, slots)
+    assert start_pos.dtype == torch.int32 and cu_new.dtype == torch.int64
+    assert slots.dtype == torch.int64
+    it = _index_type(seq_ptr)
+    assert block_table.element_size() == seq_ptr.element_size()
+    _check("hpkv_slot_mapping", lib.hpkv_slot_mapping(
+        it, _ptr(block_table), block_table.numel(), _ptr(seq_ptr), seq_ptr.numel() - 1,
+        page_size, _ptr(start_pos), _ptr(cu_new), slots.numel(), _ptr(slots),
+        _stream(stream, slots)))
+
+
+def hpkv_store_kvcache(key, value, k_cache, v_cache, slots, stream=None):
+    """Scatter key/value rows [N, Hkv, d] into the pools [num_pages, bs, Hkv, d]."""
+    _contig(key, value, k_cache, v_cache, slots)
+    assert key.dtype == value.dtype == k_cache.dtype == v_cache.dtype
+    assert slots.dtype == torch.int64
+    num_pages, bs, hkv, d = k_cache.shape
+    _check("hpkv_store_kvcache", lib.hpkv_store_kvcache(
+        _DTYPE_CODE[k_cache.dtype], _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+        _ptr(slots), slots.numel(), bs, num_pages, hkv, d, _stream(stream, k_cache)))
+
+
+def _decode_args(q, k_cache, v_cache, block_table, seq_ptr, context_lens, scale, max_context_len,
+                 workspace, out):
+    _contig(q, k_cache, v_cache, block_table, seq_ptr, context_lens, workspace, out)
+    assert q.dtype == k_cache.dtype == v_cache.dtype == out.dtype
+    assert context_lens.dtype == torch.int32
+    assert block_table.element_size() == seq_ptr.element_size()
+    B, hq, d = q.shape
+    num_pages, bs, hkv, d2 = k_cache.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (_DTYPE_CODE[q.dtype], _index_type(seq_ptr), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_table), block_table.numel(), _ptr(seq_ptr), _ptr(context_lens), B, hq, hkv,
+            d, bs, num_pages, float(scale), int(max_context_len), _ptr(workspace), ws_bytes,
+            _ptr(out))
+
+
+def hpkv_paged_attention_decode(q, k_cache, v_cache, block_table, seq_ptr, context_lens, scale,
+                                max_context_len, workspace, out, stream=None):
+    """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over each sequence's pages."""
+    args = _decode_args(q, k_cache, v_cache, block_table, seq_ptr, context_lens, scale,
+                        max_context_len, workspace, out)
+    _check("hpkv_paged_attention_decode",
+           lib.hpkv_paged_attention_decode(*args, _stream(stream, q)))
+
+
+def hpkv_paged_attention_decode_partitions(q, k_cache, v_cache, block_table, seq_ptr,
+                                           context_lens, scale, max_context_len, workspace, out,
+                                           stream=None):
+    args = _decode_args(q, k_cache, v_cache, block_table, seq_ptr, context_lens, scale,
+                        max_context_len, workspace, out)
+    _check("hpkv_paged_attention_decode_partitions",
+           lib.hpkv_paged_attention_decode_partitions(*args, _stream(stream, q)))
+
+
+def hpkv_paged_attention_decode_reduce(context_lens, page_size, max_context_len, workspace, out,
+                                       stream=None):
+    _contig(context_lens, workspace, out)
+    B, hq, d = out.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hpkv_paged_attention_decode_reduce", lib.hpkv_paged_attention_decode_reduce(
+        _DTYPE_CODE[out.dtype], _ptr(context_lens), B, hq, d, page_size, int(max_context_len),
+        _ptr(workspace), ws_bytes, _ptr(out), _stream(stream, out)))
+
+
+def alloc_workspace(q, k_cache, max_context_len):
+    """Device workspace (uint8) sized for a decode call, or None if none is needed."""
+    B, hq, d = q.shape
+    n = hpkv_paged_attention_decode_workspace_size(q.dtype, B, hq, d, k_cache.shape[1],
+                                                   max_context_len)
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None

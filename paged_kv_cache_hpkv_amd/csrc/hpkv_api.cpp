@@ -1,0 +1,332 @@
+// Host side of libhpkv.so: argument checks, host-only helpers and kernel
+// launches behind the C ABI declared in include/hpkv.h. Every check runs
+// before the first HIP call, so malformed calls fail without touching the GPU.
+#include "hpkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include "hpkv_internal.h"
+
+namespace {
+
+using hpkv::DecodeKernelArgs;
+using hpkv::ReduceKernelArgs;
+
+// Context tokens per split-context partition. 512 tokens keep a sequence of
+// the Llama/GQA shapes at a handful of partitions (enough workgroups to fill
+// 256 CUs at batch 64) while the partials stay ~1-2 % of the KV bytes.
+constexpr uint32_t kPartTokens = 512;
+static_assert(kPartTokens <= hpkv::kMaxPartTokens, "partition larger than the LDS row table");
+
+bool valid_dtype(int dt) { return dt == HPKV_F32 || dt == HPKV_F16 || dt == HPKV_BF16; }
+bool valid_index(int it) { return it == HPKV_INDEX_U32 || it == HPKV_INDEX_U64; }
+
+uint64_t read_index(int it, const void* p, uint64_t i) {
+  return it == HPKV_INDEX_U64 ? static_cast<const uint64_t*>(p)[i]
+                              : static_cast<const uint32_t*>(p)[i];
+}
+
+// head_dim * bytes must split into 16-byte lane chunks whose count is a power
+// of two no larger than a wavefront, and head_dim must be a compiled size.
+bool decode_head_dim_supported(int dtype, uint32_t head_dim) {
+  switch (head_dim) {
+    case 8: case 16: case 32: case 64: case 128: case 256: break;
+    default: return false;
+  }
+  const uint32_t lanes = head_dim * uint32_t(hpkv::dtype_bytes(dtype)) / 16;
+  return lanes >= 1 && lanes <= 64 && (lanes & (lanes - 1)) == 0;
+}
+
+uint32_t max_parts_for(uint32_t max_context_len) {
+  return max_context_len == 0 ? 1u : (max_context_len + kPartTokens - 1) / kPartTokens;
+}
+
+struct WorkspaceLayout {
+  size_t ml_offset, o_offset, bytes;
+};
+
+WorkspaceLayout workspace_layout(uint32_t num_seqs, uint32_t num_q_heads, uint32_t head_dim,
+                                 uint32_t max_context_len) {
+  const uint64_t mp = max_parts_for(max_context_len);
+  WorkspaceLayout w{0, 0, 0};
+  if (mp <= 1) return w;  // every sequence fits one partition: no partials
+  const uint64_t rows = uint64_t(num_seqs) * num_q_heads * mp;
+  const uint64_t ml_bytes = (rows * sizeof(float2) + 255) & ~uint64_t(255);
+  w.ml_offset = 0;
+  w.o_offset = ml_bytes;
+  w.bytes = ml_bytes + rows * head_dim * sizeof(float);
+  return w;
+}
+
+// Shared checks and argument packing of the decode entry points.
+int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache,
+                   const void* v_cache, const void* block_table, uint64_t block_table_len,
+                   const void* seq_ptr, const int32_t* context_lens, uint32_t num_seqs,
+                   uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                   uint32_t page_size, uint64_t num_pages, float scale, uint32_t max_context_len,
+                   void* workspace, size_t workspace_bytes, void* out, DecodeKernelArgs* a,
+                   uint64_t* num_workgroups) {
+  if (!valid_dtype(dtype) || !valid_index(index_type)) return HPKV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return HPKV_OK;
+  if (!q || !k_cache || !v_cache || !seq_ptr || !context_lens || !out) return HPKV_ERR_NULL;
+  if (block_table_len > 0 && !block_table) return HPKV_ERR_NULL;
+  if (num_q_heads == 0 || num_kv_heads == 0 || head_dim == 0 || page_size == 0 ||
+      num_pages == 0)
+    return HPKV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return HPKV_ERR_INVALID_ARG;
+  if (page_size > 0x7fffffffu || max_context_len > 0x7fffffffu) return HPKV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return HPKV_ERR_INVALID_ARG;  // NaN scale
+  if (!decode_head_dim_supported(dtype, head_dim)) return HPKV_ERR_UNSUPPORTED;
+  // q, K and V are read with 16-byte vector loads
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(v_cache)) % 16 != 0)
+    return HPKV_ERR_INVALID_ARG;
+  const WorkspaceLayout w = workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len);
+  if (w.bytes > 0 && (!workspace || workspace_bytes < w.bytes)) return HPKV_ERR_WORKSPACE;
+  if (w.bytes > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return HPKV_ERR_INVALID_ARG;
+
+  const uint32_t group = num_q_heads / num_kv_heads;
+  const uint32_t gt = hpkv::heads_per_workgroup(group);
+  const uint32_t max_parts = max_parts_for(max_context_len);
+  const uint64_t head_tiles = uint64_t(num_kv_heads) * (group / gt);
+  const uint64_t nwg = head_tiles * max_parts * num_seqs;
+  if (nwg > 0xffffffffull / 256) return HPKV_ERR_UNSUPPORTED;  // launch grid limit
+
+  a->q = q;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->out = out;
+  a->block_table = block_table;
+  a->seq_ptr = seq_ptr;
+  a->context_lens = context_lens;
+  a->ws_ml = w.bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + w.ml_offset)
+                     : nullptr;
+  a->ws_o = w.bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + w.o_offset)
+                    : nullptr;
+  a->block_table_len = block_table_len;
+  a->num_pages = num_pages;
+  a->num_seqs = num_seqs;
+  a->num_q_heads = num_q_heads;
+  a->num_kv_heads = num_kv_heads;
+  a->page_size = page_size;
+  a->group = group;
+  a->head_tiles = uint32_t(head_tiles);
+  a->max_parts = max_parts;
+  a->part_tokens = kPartTokens;
+  a->max_context_len = max_context_len;
+  a->page_div = hpkv::make_fastdiv(page_size);
+  a->scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  a->idx64 = index_type == HPKV_INDEX_U64;
+  *num_workgroups = nwg;
+  return 1;  // ready to launch
+}
+
+ReduceKernelArgs reduce_args(const DecodeKernelArgs& a, uint32_t head_dim) {
+  ReduceKernelArgs r;
+  r.context_lens = a.context_lens;
+  r.ws_o = a.ws_o;
+  r.ws_ml = a.ws_ml;
+  r.out = a.out;
+  r.num_seqs = a.num_seqs;
+  r.num_q_heads = a.num_q_heads;
+  r.head_dim = head_dim;
+  r.max_parts = a.max_parts;
+  r.part_tokens = a.part_tokens;
+  r.max_context_len = a.max_context_len;
+  return r;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? HPKV_OK : HPKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hpkv_status_string(int status) {
+  switch (status) {
+    case HPKV_OK: return "ok";
+    case HPKV_ERR_NULL: return "a required pointer is NULL";
+    case HPKV_ERR_INVALID_ARG: return "invalid size or enum argument";
+    case HPKV_ERR_INVALID_INDEX: return "index buffer contents break an invariant";
+    case HPKV_ERR_UNSUPPORTED: return "unsupported shape";
+    case HPKV_ERR_HIP: return "HIP runtime error at launch";
+    case HPKV_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int hpkv_validate_index_buffers(int index_type, uint64_t num_pages, uint64_t num_seqs,
+                                const void* seq_ptr, const void* block_table,
+                                uint64_t block_table_len, const int32_t* context_lens,
+                                uint32_t page_size) {
+  if (!valid_index(index_type)) return HPKV_ERR_INVALID_ARG;
+  if (!seq_ptr || (block_table_len > 0 && !block_table)) return HPKV_ERR_NULL;
+  if (context_lens && page_size == 0) return HPKV_ERR_INVALID_ARG;
+  if (read_index(index_type, seq_ptr, 0) != 0) return HPKV_ERR_INVALID_INDEX;
+  for (uint64_t s = 0; s < num_seqs; ++s)
+    if (read_index(index_type, seq_ptr, s + 1) < read_index(index_type, seq_ptr, s))
+      return HPKV_ERR_INVALID_INDEX;
+  if (read_index(index_type, seq_ptr, num_seqs) != block_table_len) return HPKV_ERR_INVALID_INDEX;
+  for (uint64_t k = 0; k < block_table_len; ++k)
+    if (read_index(index_type, block_table, k) >= num_pages) return HPKV_ERR_INVALID_INDEX;
+  if (context_lens) {
+    for (uint64_t s = 0; s < num_seqs; ++s) {
+      const uint64_t pages =
+          read_index(index_type, seq_ptr, s + 1) - read_index(index_type, seq_ptr, s);
+      if (context_lens[s] < 0 || uint64_t(context_lens[s]) > pages * page_size)
+        return HPKV_ERR_INVALID_INDEX;
+    }
+  }
+  return HPKV_OK;
+}
+
+int hpkv_element_offset(int index_type, uint64_t s, uint64_t t, uint32_t h, uint32_t d,
+                        uint32_t page_size, uint64_t num_pages, uint32_t num_heads,
+                        uint32_t head_dim, const void* block_table, uint64_t block_table_len,
+                        const void* seq_ptr, uint64_t num_seqs, uint64_t* flat_out) {
+  if (!valid_index(index_type)) return HPKV_ERR_INVALID_ARG;
+  if (!block_table || !seq_ptr || !flat_out) return HPKV_ERR_NULL;
+  if (page_size == 0 || num_heads == 0 || head_dim == 0) return HPKV_ERR_INVALID_ARG;
+  if (s >= num_seqs || h >= num_heads || d >= head_dim) return HPKV_ERR_INVALID_INDEX;
+  const uint64_t first = read_index(index_type, seq_ptr, s);
+  const uint64_t last = read_index(index_type, seq_ptr, s + 1);
+  const uint64_t page = t / page_size;
+  if (last < first || page >= last - first || first + page >= block_table_len)
+    return HPKV_ERR_INVALID_INDEX;
+  const uint64_t phys = read_index(index_type, block_table, first + page);
+  if (phys >= num_pages) return HPKV_ERR_INVALID_INDEX;
+  *flat_out = ((phys * page_size + t % page_size) * num_heads + h) * head_dim + d;
+  return HPKV_OK;
+}
+
+int hpkv_validate_shape(uint32_t rank, const uint64_t* dims) {
+  if (rank != 3) return HPKV_ERR_INVALID_ARG;
+  if (!dims) return HPKV_ERR_NULL;
+  if (dims[1] == 0 || dims[2] == 0) return HPKV_ERR_INVALID_ARG;
+  return HPKV_OK;
+}
+
+int hpkv_slot_mapping(int index_type, const void* block_table, uint64_t block_table_len,
+                      const void* seq_ptr, uint32_t num_seqs, uint32_t page_size,
+                      const int32_t* start_pos, const int64_t* cu_new, uint64_t num_new,
+                      int64_t* slots, void* stream) {
+  if (!valid_index(index_type)) return HPKV_ERR_INVALID_ARG;
+  if (page_size == 0) return HPKV_ERR_INVALID_ARG;
+  if (num_seqs == 0 || num_new == 0) return HPKV_OK;
+  if (!seq_ptr || !start_pos || !cu_new || !slots) return HPKV_ERR_NULL;
+  if (block_table_len > 0 && !block_table) return HPKV_ERR_NULL;
+  if (num_new > (uint64_t(0x7fffffff) * 256)) return HPKV_ERR_UNSUPPORTED;
+  return hip_status(hpkv::launch_slot_mapping(
+      index_type == HPKV_INDEX_U64, block_table, block_table_len, seq_ptr, num_seqs, page_size,
+      start_pos, cu_new, num_new, slots, static_cast<hipStream_t>(stream)));
+}
+
+int hpkv_store_kvcache(int dtype, const void* key, const void* value, void* k_cache,
+                       void* v_cache, const int64_t* slots, uint64_t num_tokens,
+                       uint32_t page_size, uint64_t num_pages, uint32_t num_kv_heads,
+                       uint32_t head_dim, void* stream) {
+  if (!valid_dtype(dtype)) return HPKV_ERR_INVALID_ARG;
+  if (page_size == 0 || num_pages == 0 || num_kv_heads == 0 || head_dim == 0)
+    return HPKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return HPKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !slots) return HPKV_ERR_NULL;
+  const uint64_t row_bytes = uint64_t(num_kv_heads) * head_dim * hpkv::dtype_bytes(dtype);
+  const uint64_t num_slots = num_pages * page_size;
+  if (num_slots > uint64_t(INT64_MAX) / row_bytes) return HPKV_ERR_INVALID_ARG;
+  // widest copy unit that divides the row and every base address
+  const uintptr_t align = reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value) |
+                          reinterpret_cast<uintptr_t>(k_cache) |
+                          reinterpret_cast<uintptr_t>(v_cache) | uintptr_t(row_bytes);
+  const int chunk = (align % 16 == 0) ? 16 : (align % 4 == 0) ? 4 : 2;
+  return hip_status(hpkv::launch_store(chunk, key, value, k_cache, v_cache, slots, num_tokens,
+                                       row_bytes / chunk, int64_t(num_slots),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t head_dim,
+                                                      uint32_t page_size) {
+  (void)dtype;
+  (void)head_dim;
+  (void)page_size;
+  return kPartTokens;
+}
+
+size_t hpkv_paged_attention_decode_workspace_size(int dtype, uint32_t num_seqs,
+                                                  uint32_t num_q_heads, uint32_t head_dim,
+                                                  uint32_t page_size, uint32_t max_context_len) {
+  if (!valid_dtype(dtype) || page_size == 0) return 0;
+  return workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len).bytes;
+}
+
+int hpkv_paged_attention_decode_partitions(int dtype, int index_type, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const void* block_table, uint64_t block_table_len,
+                                           const void* seq_ptr, const int32_t* context_lens,
+                                           uint32_t num_seqs, uint32_t num_q_heads,
+                                           uint32_t num_kv_heads, uint32_t head_dim,
+                                           uint32_t page_size, uint64_t num_pages, float scale,
+                                           uint32_t max_context_len, void* workspace,
+                                           size_t workspace_bytes, void* out, void* stream) {
+  DecodeKernelArgs a;
+  uint64_t nwg = 0;
+  const int st = prepare_decode(dtype, index_type, q, k_cache, v_cache, block_table,
+                                block_table_len, seq_ptr, context_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, page_size, num_pages, scale,
+                                max_context_len, workspace, workspace_bytes, out, &a, &nwg);
+  if (st <= 0) return st;
+  return hip_status(
+      hpkv::launch_decode_partitions(dtype, head_dim, a, nwg, static_cast<hipStream_t>(stream)));
+}
+
+int hpkv_paged_attention_decode_reduce(int dtype, const int32_t* context_lens, uint32_t num_seqs,
+                                       uint32_t num_q_heads, uint32_t head_dim,
+                                       uint32_t page_size, uint32_t max_context_len,
+                                       void* workspace, size_t workspace_bytes, void* out,
+                                       void* stream) {
+  if (!valid_dtype(dtype)) return HPKV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return HPKV_OK;
+  if (!context_lens || !out) return HPKV_ERR_NULL;
+  if (num_q_heads == 0 || head_dim == 0 || page_size == 0) return HPKV_ERR_INVALID_ARG;
+  if (max_context_len > 0x7fffffffu) return HPKV_ERR_INVALID_ARG;
+  if (!decode_head_dim_supported(dtype, head_dim)) return HPKV_ERR_UNSUPPORTED;
+  const WorkspaceLayout w = workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len);
+  if (w.bytes == 0) return HPKV_OK;  // single partition: nothing to merge
+  if (!workspace || workspace_bytes < w.bytes) return HPKV_ERR_WORKSPACE;
+  ReduceKernelArgs r;
+  r.context_lens = context_lens;
+  r.ws_ml = reinterpret_cast<const float2*>(static_cast<char*>(workspace) + w.ml_offset);
+  r.ws_o = reinterpret_cast<const float*>(static_cast<char*>(workspace) + w.o_offset);
+  r.out = out;
+  r.num_seqs = num_seqs;
+  r.num_q_heads = num_q_heads;
+  r.head_dim = head_dim;
+  r.max_parts = max_parts_for(max_context_len);
+  r.part_tokens = kPartTokens;
+  r.max_context_len = max_context_len;
+  return hip_status(hpkv::launch_decode_reduce(dtype, r, static_cast<hipStream_t>(stream)));
+}
+
+int hpkv_paged_attention_decode(int dtype, int index_type, const void* q, const void* k_cache,
+                                const void* v_cache, const void* block_table,
+                                uint64_t block_table_len, const void* seq_ptr,
+                                const int32_t* context_lens, uint32_t num_seqs,
+                                uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                                uint32_t page_size, uint64_t num_pages, float scale,
+                                uint32_t max_context_len, void* workspace, size_t workspace_bytes,
+                                void* out, void* stream) {
+  DecodeKernelArgs a;
+  uint64_t nwg = 0;
+  const int st = prepare_decode(dtype, index_type, q, k_cache, v_cache, block_table,
+                                block_table_len, seq_ptr, context_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, page_size, num_pages, scale,
+                                max_context_len, workspace, workspace_bytes, out, &a, &nwg);
+  if (st <= 0) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hpkv::launch_decode_partitions(dtype, head_dim, a, nwg, s);
+  if (e != hipSuccess) return HPKV_ERR_HIP;
+  if (a.max_parts > 1) e = hpkv::launch_decode_reduce(dtype, reduce_args(a, head_dim), s);
+  return hip_status(e);
+}
+
+}  // extern "C"

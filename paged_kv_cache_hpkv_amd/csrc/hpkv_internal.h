@@ -1,0 +1,92 @@
+// Internal interface between the host entry points (hpkv_api.cpp) and the
+// gfx950 kernels (*.hip). Not installed; the public ABI is include/hpkv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hpkv {
+
+// Element storage types, same numbering as hpkv_dtype.
+enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : 2; }
+
+// Largest split-context partition the decode kernel's LDS row table holds.
+constexpr uint32_t kMaxPartTokens = 1024;
+
+// Division by a runtime divisor 1 <= d < 2^31 for numerators n < 2^31:
+// n / d == (n * mul) >> shift with shift = 31 + ceil(log2 d) and
+// mul = ceil(2^shift / d) (< 2^32). Exact because the rounding excess of mul
+// times n stays below 2^shift.
+struct FastDiv {
+  uint32_t mul;
+  uint32_t shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint32_t shift = 31 + l;
+  const unsigned __int128 num = (unsigned __int128)1 << shift;
+  const uint64_t mul = uint64_t((num + d - 1) / d);
+  return FastDiv{uint32_t(mul), shift};
+}
+
+struct DecodeKernelArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  void* out;
+  const void* block_table;
+  const void* seq_ptr;
+  const int32_t* context_lens;
+  float* ws_o;       // [B, Hq, max_parts, head_dim] unnormalised partial outputs
+  float2* ws_ml;     // [B, Hq, max_parts] (running max in log2 units, sum of weights)
+  uint64_t block_table_len;
+  uint64_t num_pages;
+  uint32_t num_seqs;
+  uint32_t num_q_heads;
+  uint32_t num_kv_heads;
+  uint32_t page_size;
+  uint32_t group;       // num_q_heads / num_kv_heads
+  uint32_t head_tiles;  // num_kv_heads * (group / heads per workgroup)
+  uint32_t max_parts;
+  uint32_t part_tokens;
+  uint32_t max_context_len;
+  FastDiv page_div;
+  float scale_log2;     // scale * log2(e): scores are kept in base-2 units
+  int idx64;            // block_table / seq_ptr hold u64 (else u32)
+};
+
+struct ReduceKernelArgs {
+  const int32_t* context_lens;
+  const float* ws_o;
+  const float2* ws_ml;
+  void* out;
+  uint32_t num_seqs;
+  uint32_t num_q_heads;
+  uint32_t head_dim;
+  uint32_t max_parts;
+  uint32_t part_tokens;
+  uint32_t max_context_len;
+};
+
+// Query heads served by one workgroup for a GQA group of `group` heads.
+uint32_t heads_per_workgroup(uint32_t group);
+
+hipError_t launch_slot_mapping(bool idx64, const void* block_table, uint64_t block_table_len,
+                               const void* seq_ptr, uint32_t num_seqs, uint32_t page_size,
+                               const int32_t* start_pos, const int64_t* cu_new, uint64_t num_new,
+                               int64_t* slots, hipStream_t stream);
+
+hipError_t launch_store(int chunk_bytes, const void* key, const void* value, void* k_cache,
+                        void* v_cache, const int64_t* slots, uint64_t num_tokens,
+                        uint64_t row_chunks, int64_t num_slots, hipStream_t stream);
+
+hipError_t launch_decode_partitions(int dtype, uint32_t head_dim, const DecodeKernelArgs& a,
+                                    uint64_t num_workgroups, hipStream_t stream);
+
+hipError_t launch_decode_reduce(int dtype, const ReduceKernelArgs& a, hipStream_t stream);
+
+}  // namespace hpkv

@@ -1,0 +1,126 @@
+"""Runs one step of the paged KV cache path on the GPU library and on the
+oracle, from the same seeded inputs, for the parity tests and the smoke check.
+
+A step is: slot mapping of the new tokens (per chunk), the store of their K/V
+rows, then decode of every sequence. Inputs come from workloads.py. Pool rows
+outside every sequence's context are poisoned with NaN first (the rows that
+are in use are listed by the oracle's slot mapping over [0, ctx)), so a kernel
+that reads past the context or into an unreferenced page shows NaN.
+"""
+import os
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_hpkv_amd as hpkv
+import workloads
+
+TOL_ABS = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
+TOL_REL = {"f32": 1e-5, "f16": 0.0, "bf16": 0.0}
+
+
+def host_threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    """Host copy of a tensor's storage (bf16 carried as uint16 bit patterns)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def used_slots(w: workloads.Workload) -> np.ndarray:
+    B = w.num_seqs
+    cu = np.zeros(B + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(w.context_lens.astype(np.int64))
+    return oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, np.zeros(B, np.int32), cu)
+
+
+def poison_unused(w: workloads.Workload, t: workloads.Tensors):
+    dev = t.k_cache.device
+    mask = torch.ones(w.num_pages * w.page_size, dtype=torch.bool, device=dev)
+    mask[torch.from_numpy(used_slots(w)).to(dev)] = False
+    for pool in (t.k_cache, t.v_cache):
+        pool.view(w.num_pages * w.page_size, -1)[mask] = float("nan")
+
+
+def host_inputs(t: workloads.Tensors):
+    return dict(q=host_bits(t.q), k_cache=host_bits(t.k_cache), v_cache=host_bits(t.v_cache),
+                new_keys=[host_bits(x) for x in t.new_keys],
+                new_values=[host_bits(x) for x in t.new_values])
+
+
+def gpu_step(w: workloads.Workload, t: workloads.Tensors, max_context_len=None):
+    """Runs slot mapping + store + decode through libhpkv; returns slots and out."""
+    dev = t.q.device
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sp = torch.from_numpy(w.seq_ptr).to(dev)
+    ctx = torch.from_numpy(w.context_lens).to(dev)
+    slots_out = []
+    for c, (start, cu) in enumerate(w.chunks):
+        slots = torch.empty(int(cu[-1]), dtype=torch.int64, device=dev)
+        hpkv.hpkv_slot_mapping(bt, sp, w.page_size, torch.from_numpy(start).to(dev),
+                               torch.from_numpy(cu).to(dev), slots)
+        slots_out.append(slots.cpu().numpy())
+        if w.drop_mask is not None and c == 0:
+            slots[torch.from_numpy(w.drop_mask).to(dev)] = -1
+        hpkv.hpkv_store_kvcache(t.new_keys[c], t.new_values[c], t.k_cache, t.v_cache, slots)
+    mcl = w.max_context_len if max_context_len is None else max_context_len
+    out = torch.empty_like(t.q)
+    ws = hpkv.alloc_workspace(t.q, t.k_cache, mcl)
+    hpkv.hpkv_paged_attention_decode(t.q, t.k_cache, t.v_cache, bt, sp, ctx, w.scale, mcl, ws,
+                                     out)
+    torch.cuda.synchronize(dev)
+    return slots_out, out
+
+
+def oracle_step(w: workloads.Workload, h: dict, threads=None):
+    """The same step on the oracle, in place on the host copies `h`."""
+    slots_out = []
+    for c, (start, cu) in enumerate(w.chunks):
+        slots = oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, start, cu)
+        slots_out.append(slots.copy())
+        if w.drop_mask is not None and c == 0:
+            slots[w.drop_mask] = -1
+        oracle.store_kvcache(h["new_keys"][c], h["new_values"][c], h["k_cache"], h["v_cache"],
+                             slots)
+    out, out64 = oracle.paged_attention_decode(w.dtype, h["q"], h["k_cache"], h["v_cache"],
+                                               w.block_table, w.seq_ptr, w.context_lens, w.scale,
+                                               threads or host_threads())
+    return slots_out, out, out64
+
+
+def decode_errors(dtype, got_bits, ref64):
+    """(max abs error, max of error / allowed); fails on non-finite output."""
+    got = oracle.widen_dtype(dtype, got_bits)
+    err = np.abs(got - ref64)
+    allowed = TOL_ABS[dtype] + TOL_REL[dtype] * np.abs(ref64)
+    return float(np.nanmax(err)) if err.size else 0.0, \
+        float(np.max(err / allowed)) if err.size else 0.0, bool(np.isfinite(got).all())
+
+
+def check_step(w: workloads.Workload, device="cuda", seed_poison=True, verbose=True):
+    """Full parity check of one workload; returns a dict of measured errors."""
+    if verbose:
+        print(f"[parity] {w.name} {w.dtype} {w.index} B={w.num_seqs} Hq={w.num_q_heads} "
+              f"Hkv={w.num_kv_heads} d={w.head_dim} bs={w.page_size} pages={w.num_pages}",
+              flush=True)
+    t = workloads.make_tensors(w, device)
+    if seed_poison:
+        poison_unused(w, t)
+    h = host_inputs(t)
+    g_slots, g_out = gpu_step(w, t)
+    o_slots, o_out, o_out64 = oracle_step(w, h)
+    for gs, os_ in zip(g_slots, o_slots):
+        np.testing.assert_array_equal(gs, os_)  # slot mapping: bit-exact
+    for name in ("k_cache", "v_cache"):  # store: whole pools byte-for-byte
+        g_pool = host_bits(getattr(t, name))
+        assert g_pool.tobytes() == h[name].tobytes(), f"{name} differs after store"
+    max_err, worst_ratio, finite = decode_errors(w.dtype, host_bits(g_out), o_out64)
+    assert finite, "non-finite decode output"
+    assert worst_ratio <= 1.0, f"decode error {max_err} above tolerance"
+    return dict(max_err=max_err, worst_ratio=worst_ratio, out=g_out, oracle_out=o_out,
+                oracle_out64=o_out64, tensors=t)

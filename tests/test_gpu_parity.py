@@ -1,0 +1,249 @@
+"""GPU parity of libhpkv against the CPU oracle (needs an MI355X).
+
+Each case runs the whole path (slot mapping per chunk, store, decode) through
+the C ABI on seeded inputs and the same step on the oracle, then requires:
+slots bit-exact, both pools byte-for-byte identical after the store, and
+decode within |gpu - ref| <= 2e-2 (bf16/f16) or 1e-5 + 1e-5|ref| (f32), ref
+being the oracle's double result. Pool rows outside every context are NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_hpkv_amd as hpkv
+import workloads
+from paths import check_step, decode_errors, gpu_step, host_bits, host_inputs, oracle_step, \
+    poison_unused
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("bs", [4, 16, 256])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_tiny_step(bs, dtype):
+    r = check_step(workloads.tiny(bs=bs, dtype=dtype))
+    print(f"max err {r['max_err']:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("dtype,index", [("bf16", "u32"), ("bf16", "u64"), ("f16", "u32")])
+def test_llama7b_layer(dtype, index):
+    r = check_step(workloads.llama7b(dtype=dtype, index=index))
+    print(f"max err {r['max_err']:.3e}", flush=True)
+
+
+def test_gqa_layer():
+    r = check_step(workloads.gqa())
+    print(f"max err {r['max_err']:.3e}", flush=True)
+
+
+def test_qwen3_layer_with_dropped_slots():
+    w = workloads.qwen3()
+    assert w.drop_mask.any() and not w.drop_mask.all()
+    r = check_step(w)
+    print(f"max err {r['max_err']:.3e}", flush=True)
+
+
+def test_prefix_sharing_chunked_prefill():
+    w = workloads.prefix()
+    # some chunk starts mid-page, and aliased prefix pages exist
+    starts = np.concatenate([s for s, _ in w.chunks])
+    assert np.any(starts % w.page_size != 0)
+    assert w.kv_bytes_unique() < w.kv_bytes_logical()
+    r = check_step(w)
+    print(f"max err {r['max_err']:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(16, 2, 64, "bf16"), (4, 4, 256, "f16"),
+                                            (8, 2, 32, "f32"), (6, 2, 16, "bf16"),
+                                            (32, 2, 128, "bf16"), (3, 3, 8, "bf16"),
+                                            (8, 1, 256, "f32")])
+def test_other_head_shapes(hq, hkv, d, dtype):
+    rng = np.random.default_rng(hq * 1000 + d)
+    ctx = rng.integers(1, 1500, size=5).astype(np.int32)
+    ctx[0] = 1
+    base = workloads.llama7b(dtype=dtype, seed=7, batch=5)
+    num_pages, sp, bt = workloads._random_pool_tables(rng, ctx, 16, "u32")
+    w = workloads.Workload(f"shape{hq}x{hkv}x{d}", dtype, "u32", hq, hkv, d, 16, num_pages, ctx,
+                           sp, bt, d ** -0.5, chunks=workloads._decode_step_chunks(ctx), seed=7)
+    del base
+    r = check_step(w)
+    print(f"max err {r['max_err']:.3e}", flush=True)
+
+
+def _decode(w, t, out=None, max_context_len=None, bt=None, sp=None):
+    dev = t.q.device
+    bt = torch.from_numpy(w.block_table if bt is None else bt).to(dev)
+    sp = torch.from_numpy(w.seq_ptr if sp is None else sp).to(dev)
+    ctx = torch.from_numpy(w.context_lens).to(dev)
+    mcl = w.max_context_len if max_context_len is None else max_context_len
+    out = torch.empty_like(t.q) if out is None else out
+    ws = hpkv.alloc_workspace(t.q, t.k_cache, mcl)
+    hpkv.hpkv_paged_attention_decode(t.q, t.k_cache, t.v_cache, bt, sp, ctx, w.scale, mcl, ws, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_determinism_index_width_and_page_permutation():
+    w = workloads.gqa(batch=48)
+    t = workloads.make_tensors(w, "cuda")
+    poison_unused(w, t)
+    a = host_bits(_decode(w, t))
+    b = host_bits(_decode(w, t))
+    assert a.tobytes() == b.tobytes()  # run to run
+    w64 = w.with_index("u64")
+    c = host_bits(_decode(w64, t))
+    assert a.tobytes() == c.tobytes()  # u32 and u64 tables
+    perm = torch.randperm(w.num_pages, generator=torch.Generator().manual_seed(0))
+    inv = torch.argsort(perm).numpy()
+    t.k_cache = t.k_cache[perm.cuda()].contiguous()
+    t.v_cache = t.v_cache[perm.cuda()].contiguous()
+    bt2 = inv[w.block_table.astype(np.int64)].astype(np.uint32)
+    d = host_bits(_decode(w, t, bt=bt2))
+    assert a.tobytes() == d.tobytes()  # physical placement does not matter
+
+
+def test_single_partition_path_and_larger_max_context():
+    """A generous max_context_len (more, empty partitions) gives identical bits."""
+    w = workloads.gqa(batch=32)
+    t = workloads.make_tensors(w, "cuda")
+    poison_unused(w, t)
+    a = host_bits(_decode(w, t))
+    b = host_bits(_decode(w, t, max_context_len=w.max_context_len + 3000))
+    assert a.tobytes() == b.tobytes()
+    short = workloads.Workload(**{**w.__dict__})
+    short.context_lens = np.minimum(w.context_lens, 300).astype(np.int32)
+    assert hpkv.hpkv_paged_attention_decode_workspace_size(
+        torch.bfloat16, w.num_seqs, w.num_q_heads, w.head_dim, w.page_size, 300) == 0
+    h = host_inputs(t)
+    got = host_bits(_decode(short, t))
+    _, ref64 = oracle.paged_attention_decode("bf16", h["q"], h["k_cache"], h["v_cache"],
+                                             short.block_table, short.seq_ptr,
+                                             short.context_lens, short.scale, 8)
+    err, ratio, finite = decode_errors("bf16", got, ref64)
+    assert finite and ratio <= 1.0
+
+
+def test_closed_forms_on_gpu():
+    w = workloads.tiny(bs=16, dtype="bf16")
+    w.context_lens = np.array([1, 0, 35], dtype=np.int32)
+    w.chunks = []
+    t = workloads.make_tensors(w, "cuda")
+    poison_unused(w, t)
+    out = host_bits(_decode(w, t))
+    # ctx = 1: the output is v_0 exactly (every head of the group)
+    page0 = int(w.block_table[int(w.seq_ptr[0])])
+    v0 = host_bits(t.v_cache[page0, 0])  # [Hkv, d]
+    np.testing.assert_array_equal(out[0], np.repeat(v0, 2, axis=0))
+    # ctx = 0: zeros
+    np.testing.assert_array_equal(oracle.widen_dtype("bf16", out[1]), 0.0)
+    # q = 0: the mean of V
+    t.q.zero_()
+    h = host_inputs(t)
+    out = host_bits(_decode(w, t))
+    _, ref64 = oracle.paged_attention_decode("bf16", h["q"], h["k_cache"], h["v_cache"],
+                                             w.block_table, w.seq_ptr, w.context_lens, w.scale, 1)
+    err, ratio, finite = decode_errors("bf16", out, ref64)
+    assert finite and ratio <= 1.0
+
+
+def test_malformed_contents_give_nan_only_where_broken():
+    w = workloads.gqa(batch=8)
+    t = workloads.make_tensors(w, "cuda")
+    poison_unused(w, t)
+    good = host_bits(_decode(w, t)).copy()
+    bad = workloads.Workload(**{**w.__dict__})
+    bad.context_lens = w.context_lens.copy()
+    sp = w.seq_ptr.astype(np.int64)
+    cap = (sp[2] - sp[1]) * w.page_size
+    bad.context_lens[1] = cap + 1                       # beyond its slice
+    bad.context_lens[3] = -5                            # negative
+    bt = w.block_table.copy()
+    bt[sp[5]] = w.num_pages + 7                         # a page id past the pool
+    out = host_bits(_decode(bad, t, bt=bt, max_context_len=w.max_context_len + 64))
+    outf = oracle.widen_dtype("bf16", out)
+    for s in (1, 3, 5):
+        assert np.isnan(outf[s]).all(), s
+    for s in (0, 2, 4, 6, 7):
+        assert out[s].tobytes() == good[s].tobytes(), s
+    # a length above max_context_len is refused the same way
+    over = workloads.Workload(**{**w.__dict__})
+    over.context_lens = w.context_lens.copy()
+    out = host_bits(_decode(over, t, max_context_len=int(w.context_lens[0]) - 1))
+    assert np.isnan(oracle.widen_dtype("bf16", out[0])).all()
+
+
+def test_store_unaligned_rows_and_slot_edges():
+    """Row widths that are not a multiple of 16 bytes; -1, invalid and repeated-free slots."""
+    dev = "cuda"
+    rng = np.random.default_rng(2)
+    for hkv, d, dt in [(1, 6, torch.float16), (3, 5, torch.bfloat16), (2, 3, torch.float32),
+                       (8, 128, torch.bfloat16)]:
+        num_pages, bs = 7, 4
+        kc = torch.randn(num_pages, bs, hkv, d, device=dev).to(dt)
+        vc = torch.randn(num_pages, bs, hkv, d, device=dev).to(dt)
+        n = 20
+        slots = torch.from_numpy(rng.permutation(num_pages * bs)[:n].astype(np.int64))
+        slots[3] = -1
+        slots[7] = num_pages * bs + 2   # past the pool: skipped
+        slots[9] = -9                   # negative: skipped
+        key = torch.randn(n, hkv, d, device=dev).to(dt)
+        val = torch.randn(n, hkv, d, device=dev).to(dt)
+        hk, hv = host_bits(kc).copy(), host_bits(vc).copy()
+        hpkv.hpkv_store_kvcache(key, val, kc, vc, slots.to(dev))
+        torch.cuda.synchronize()
+        invalid = oracle.store_kvcache(host_bits(key), host_bits(val), hk, hv, slots.numpy())
+        assert invalid == 2
+        assert host_bits(kc).tobytes() == hk.tobytes()
+        assert host_bits(vc).tobytes() == hv.tobytes()
+
+
+def test_slot_mapping_edges():
+    dev = "cuda"
+    tables = [[3, 1], [], [4], [0, 2, 5]]
+    for index in (np.uint32, np.uint64):
+        sp = np.zeros(5, dtype=np.int64)
+        sp[1:] = np.cumsum([len(t) for t in tables])
+        bt = np.array([p for t in tables for p in t], dtype=index)
+        sp = sp.astype(index)
+        start = np.array([2, 0, 3, 9], dtype=np.int32)
+        counts = np.array([9, 2, 0, 4])
+        cu = np.zeros(5, dtype=np.int64)
+        cu[1:] = np.cumsum(counts)
+        slots = torch.empty(int(cu[-1]), dtype=torch.int64, device=dev)
+        hpkv.hpkv_slot_mapping(torch.from_numpy(bt).to(dev), torch.from_numpy(sp).to(dev), 4,
+                               torch.from_numpy(start).to(dev), torch.from_numpy(cu).to(dev),
+                               slots)
+        want = oracle.slot_mapping(bt, sp, 4, start, cu)
+        np.testing.assert_array_equal(slots.cpu().numpy(), want)
+        assert (want == -1).sum() >= 3  # past the slice, and the empty table
+
+
+def test_partition_and_reduce_entry_points_match_decode():
+    w = workloads.gqa(batch=16)
+    t = workloads.make_tensors(w, "cuda")
+    poison_unused(w, t)
+    ref = host_bits(_decode(w, t))
+    dev = t.q.device
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sp = torch.from_numpy(w.seq_ptr).to(dev)
+    ctx = torch.from_numpy(w.context_lens).to(dev)
+    out = torch.full_like(t.q, float("nan"))
+    ws = hpkv.alloc_workspace(t.q, t.k_cache, w.max_context_len)
+    hpkv.hpkv_paged_attention_decode_partitions(t.q, t.k_cache, t.v_cache, bt, sp, ctx, w.scale,
+                                                w.max_context_len, ws, out)
+    hpkv.hpkv_paged_attention_decode_reduce(ctx, w.page_size, w.max_context_len, ws, out)
+    torch.cuda.synchronize()
+    assert host_bits(out).tobytes() == ref.tobytes()
+
+
+def test_empty_batch_is_a_no_op():
+    dev = "cuda"
+    q = torch.empty(0, 4, 128, dtype=torch.bfloat16, device=dev)
+    kc = torch.zeros(2, 16, 2, 128, dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q)
+    hpkv.hpkv_paged_attention_decode(q, kc, kc, torch.zeros(0, dtype=torch.int32, device=dev),
+                                     torch.zeros(1, dtype=torch.int32, device=dev),
+                                     torch.zeros(0, dtype=torch.int32, device=dev), 0.1, 0, None,
+                                     out)
+    torch.cuda.synchronize()
