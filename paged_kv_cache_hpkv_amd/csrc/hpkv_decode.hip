@@ -52,58 +52,59 @@ struct Elem {
   static constexpr int bytes = DT == kF32 ? 4 : 2;
 };
 
+// Reinterprets a 32-bit word as a pair of 16-bit floats. (Written with memcpy:
+// hipcc 7.2 miscompiles __builtin_bit_cast applied to an element of an
+// ext_vector_type value, reading element 0 instead.)
+template <typename V>
+__device__ inline V as_pair(uint32_t w) {
+  V r;
+  __builtin_memcpy(&r, &w, sizeof(r));
+  return r;
+}
+
 // fp32 dot product of one 16-byte chunk of K with the matching chunk of q.
 template <int DT>
 __device__ inline float dot16(const u32x4 k, const u32x4 q) {
+  const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+  const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+  float a = 0.0f;
   if constexpr (DT == kBF16) {
-    float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.x),
-                                              __builtin_bit_cast(bf16x2, q.x), 0.0f, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.y),
-                                        __builtin_bit_cast(bf16x2, q.y), a, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.z),
-                                        __builtin_bit_cast(bf16x2, q.z), a, false);
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.w),
-                                           __builtin_bit_cast(bf16x2, q.w), a, false);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a = __builtin_amdgcn_fdot2_f32_bf16(as_pair<bf16x2>(kw[i]), as_pair<bf16x2>(qw[i]), a,
+                                          false);
   } else if constexpr (DT == kF16) {
-    float a = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, k.x),
-                                     __builtin_bit_cast(f16x2, q.x), 0.0f, false);
-    a = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, k.y), __builtin_bit_cast(f16x2, q.y), a,
-                               false);
-    a = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, k.z), __builtin_bit_cast(f16x2, q.z), a,
-                               false);
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, k.w), __builtin_bit_cast(f16x2, q.w),
-                                  a, false);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a = __builtin_amdgcn_fdot2(as_pair<f16x2>(kw[i]), as_pair<f16x2>(qw[i]), a, false);
   } else {
-    float a = __uint_as_float(k.x) * __uint_as_float(q.x);
-    a = fmaf(__uint_as_float(k.y), __uint_as_float(q.y), a);
-    a = fmaf(__uint_as_float(k.z), __uint_as_float(q.z), a);
-    return fmaf(__uint_as_float(k.w), __uint_as_float(q.w), a);
+    a = __uint_as_float(kw[0]) * __uint_as_float(qw[0]);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) a = fmaf(__uint_as_float(kw[i]), __uint_as_float(qw[i]), a);
   }
+  return a;
 }
 
 // Widens one 16-byte chunk to 16/bytes floats.
 template <int DT>
 __device__ inline void widen16(const u32x4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   if constexpr (DT == kBF16) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = __uint_as_float(w[i] << 16);
       f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   } else if constexpr (DT == kF16) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+      const f16x2 h = as_pair<f16x2>(w[i]);
       f[2 * i] = float(h.x);
       f[2 * i + 1] = float(h.y);
     }
   } else {
-    f[0] = __uint_as_float(v.x);
-    f[1] = __uint_as_float(v.y);
-    f[2] = __uint_as_float(v.z);
-    f[3] = __uint_as_float(v.w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
   }
 }
 
