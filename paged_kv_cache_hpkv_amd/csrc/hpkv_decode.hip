@@ -30,8 +30,9 @@
 //    otherwise the partition writes (max, sum, unnormalised vector) and the
 //    reduce kernel merges the partitions.
 //  * Rows at or past the context length are never loaded: their lanes reuse
-//    the address of the last valid row and their values are replaced by
-//    zeros, so NaN garbage in unused rows cannot reach the accumulators.
+//    the address of the last valid row (finite data) and their score is -inf,
+//    so their weight is exactly 0 and NaN garbage in unused rows cannot reach
+//    the accumulators.
 #include <math.h>
 
 #include "hpkv_internal.h"
@@ -44,8 +45,23 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                // waves per workgroup of the reduce kernel
 constexpr int kThreads = kWave * kWaves;
+
+// Launch shape of the partition kernel: waves per workgroup, token rows each
+// lane loads per tile (NLOAD, each row CPL 16-byte chunks of K and of V),
+// non-temporal loads, the minimum waves per SIMD the register budget must
+// allow, and CPL, the 16-byte chunks of a row one lane owns. A larger CPL
+// puts fewer lanes on a row, so the per-token softmax bookkeeping and the
+// cross-lane reduction of q.k are repeated on fewer lanes.
+template <int NW_, int NLOAD_, bool NT_, int MINW_, int CPL_ = 1>
+struct Tune {
+  static constexpr int NW = NW_;
+  static constexpr int NLOAD = NLOAD_;
+  static constexpr bool NT = NT_;
+  static constexpr int MINW = MINW_;
+  static constexpr int CPL = CPL_;
+};
 
 template <int DT>
 struct Elem {
@@ -146,6 +162,17 @@ __device__ inline void store_out(void* out, uint64_t idx, float x) {
   }
 }
 
+// 16-byte global load; non-temporal loads stream K/V past the caches.
+template <bool NONTEMPORAL>
+__device__ inline u32x4 load16(const char* p) {
+  const u32x4* v = reinterpret_cast<const u32x4*>(p);
+  if constexpr (NONTEMPORAL) {
+    return __builtin_nontemporal_load(v);
+  } else {
+    return *v;
+  }
+}
+
 __device__ inline uint32_t fastdiv(uint32_t n, FastDiv d) {
   return uint32_t((uint64_t(n) * d.mul) >> d.shift);
 }
@@ -164,19 +191,27 @@ __device__ inline uint32_t num_parts(int32_t n, uint32_t part_tokens) {
   return n <= 0 ? 1u : (uint32_t(n) + part_tokens - 1) / part_tokens;
 }
 
-template <int DT, int D, int GT, int NLOAD>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(const DecodeKernelArgs a) {
+template <int DT, int D, int GT, class TU>
+__global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel(
+    const DecodeKernelArgs a) {
+  constexpr int NW = TU::NW;
+  constexpr int NTH = NW * kWave;    // threads per workgroup
+  constexpr int NLOAD = TU::NLOAD;
   constexpr int EB = Elem<DT>::bytes;
-  constexpr int EPL = 16 / EB;       // elements per lane per load
-  constexpr int LPR = D / EPL;       // lanes per token row
+  constexpr int EPL = 16 / EB;       // elements per 16-byte chunk
+  constexpr int CPR = D / EPL;       // chunks per token row
+  constexpr int CPL = TU::CPL < CPR ? TU::CPL : CPR;  // chunks per lane
+  constexpr int LPR = CPR / CPL;     // lanes per token row
   constexpr int RPL = kWave / LPR;   // token rows per wave load
   constexpr int TT = RPL * NLOAD;    // tokens per wave tile
-  static_assert(LPR >= 1 && LPR <= kWave && (LPR & (LPR - 1)) == 0, "unsupported head_dim");
+  constexpr int VPL = CPL * EPL;     // elements of a row per lane
+  static_assert(CPR % CPL == 0 && LPR <= kWave && (LPR & (LPR - 1)) == 0,
+                "unsupported head_dim");
 
   __shared__ uint64_t s_row[kMaxPartTokens];
-  __shared__ float s_m[kWaves][GT];
-  __shared__ float s_l[kWaves][GT];
-  __shared__ float s_acc[kWaves][GT][D];
+  __shared__ float s_m[NW][GT];
+  __shared__ float s_l[NW][GT];
+  __shared__ float s_acc[NW][GT][D];
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid % kWave;
@@ -198,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   const uint64_t out_row0 = uint64_t(s) * a.num_q_heads + h0;  // first (s, h) row of the tile
   if (length_is_bad(n, a.max_context_len)) {
     if (part == 0)
-      for (uint32_t i = tid; i < GT * D; i += kThreads) store_out<DT>(a.out, out_row0 * D + i, NAN);
+      for (uint32_t i = tid; i < GT * D; i += NTH) store_out<DT>(a.out, out_row0 * D + i, NAN);
     return;
   }
 
@@ -213,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   // Resolve each token of the partition to its pool row (element offset of
   // head g's row), once per workgroup.
   int bad_page = 0;
-  for (uint32_t i = tid; i < cnt; i += kThreads) {
+  for (uint32_t i = tid; i < cnt; i += NTH) {
     const uint32_t t = p0 + i;
     const uint32_t lp = fastdiv(t, a.page_div);
     const uint32_t off = t - lp * a.page_size;
@@ -228,10 +263,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
 
   if (bad) {  // malformed index buffers: NaN result for this partition
     if (nparts == 1) {
-      for (uint32_t i = tid; i < GT * D; i += kThreads)
+      for (uint32_t i = tid; i < GT * D; i += NTH)
         store_out<DT>(a.out, out_row0 * D + i, NAN);
     } else {
-      for (uint32_t i = tid; i < GT * D; i += kThreads) {
+      for (uint32_t i = tid; i < GT * D; i += NTH) {
         const uint64_t r = (out_row0 + i / D) * a.max_parts + part;
         a.ws_o[r * D + i % D] = NAN;
         if (i % D == 0) a.ws_ml[r] = make_float2(NAN, NAN);
@@ -241,42 +276,41 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   }
 
   const uint32_t row = lane / LPR;  // which row of a wave load this lane reads
-  const uint32_t c = lane % LPR;    // which 16-byte chunk of that row
+  const uint32_t c = lane % LPR;    // lane's chunks of that row: j*LPR + c, j < CPL
 
-  u32x4 qv[GT];
+  u32x4 qv[GT][CPL];
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
-    const char* qp = static_cast<const char*>(a.q) + ((out_row0 + hh) * D + c * EPL) * EB;
-    qv[hh] = *reinterpret_cast<const u32x4*>(qp);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const char* qp = static_cast<const char*>(a.q) +
+                       ((out_row0 + hh) * D + (j * LPR + c) * EPL) * EB;
+      qv[hh][j] = *reinterpret_cast<const u32x4*>(qp);
+    }
   }
 
-  float m[GT], l[GT], acc[GT][EPL];
+  float m[GT], l[GT], acc[GT][VPL];
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
     m[hh] = -INFINITY;
     l[hh] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.0f;
+    for (int e = 0; e < VPL; ++e) acc[hh][e] = 0.0f;
   }
 
   const char* kbase = static_cast<const char*>(a.k_cache) + c * 16;
   const char* vbase = static_cast<const char*>(a.v_cache) + c * 16;
 
-  for (uint32_t tb = wave * TT; tb < cnt; tb += kWaves * TT) {
-    u32x4 kr[NLOAD], vr[NLOAD];
+  for (uint32_t tb = wave * TT; tb < cnt; tb += NW * TT) {
+    u32x4 kr[NLOAD][CPL], vr[NLOAD][CPL];
 #pragma unroll
     for (int k = 0; k < NLOAD; ++k) {
       const uint32_t li = tb + k * RPL + row;
       const uint64_t off = s_row[li < cnt ? li : cnt - 1] * EB;
-      kr[k] = *reinterpret_cast<const u32x4*>(kbase + off);
-      vr[k] = *reinterpret_cast<const u32x4*>(vbase + off);
-    }
 #pragma unroll
-    for (int k = 0; k < NLOAD; ++k) {
-      if (tb + k * RPL + row >= cnt) {
-        kr[k] = u32x4{0, 0, 0, 0};
-        vr[k] = u32x4{0, 0, 0, 0};
-      }
+      for (int j = 0; j < CPL; ++j) kr[k][j] = load16<TU::NT>(kbase + off + j * LPR * 16);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) vr[k][j] = load16<TU::NT>(vbase + off + j * LPR * 16);
     }
 
     float sc[GT][NLOAD];
@@ -285,7 +319,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
       const bool valid = tb + k * RPL + row < cnt;
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) {
-        const float z = row_sum<LPR>(dot16<DT>(kr[k], qv[hh])) * a.scale_log2;
+        float part_dot = dot16<DT>(kr[k][0], qv[hh][0]);
+#pragma unroll
+        for (int j = 1; j < CPL; ++j) part_dot += dot16<DT>(kr[k][j], qv[hh][j]);
+        const float z = row_sum<LPR>(part_dot) * a.scale_log2;
         sc[hh][k] = valid ? z : -INFINITY;
       }
     }
@@ -301,19 +338,27 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
       const float corr = __builtin_amdgcn_exp2f(m[hh] - mu[hh]);
       l[hh] *= corr;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[hh][e] *= corr;
+      for (int e = 0; e < VPL; ++e) acc[hh][e] *= corr;
       m[hh] = mn;
     }
 #pragma unroll
     for (int k = 0; k < NLOAD; ++k) {
-      float vf[EPL];
-      widen16<DT>(vr[k], vf);
+      float p[GT];
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) {
-        const float p = __builtin_amdgcn_exp2f(sc[hh][k] - mu[hh]);
-        l[hh] += p;
+        p[hh] = __builtin_amdgcn_exp2f(sc[hh][k] - mu[hh]);
+        l[hh] += p[hh];
+      }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(p, vf[e], acc[hh][e]);
+      for (int j = 0; j < CPL; ++j) {
+        float vf[EPL];
+        widen16<DT>(vr[k][j], vf);
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            acc[hh][j * EPL + e] = fmaf(p[hh], vf[e], acc[hh][j * EPL + e]);
+        }
       }
     }
   }
@@ -331,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
       const float fb = __builtin_amdgcn_exp2f(mo - mref);
       l[hh] = l[hh] * fa + lo * fb;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
+      for (int e = 0; e < VPL; ++e) {
         const float ao = __shfl_xor(acc[hh][e], sh);
         acc[hh][e] = acc[hh][e] * fa + ao * fb;
       }
@@ -342,7 +387,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][hh][c * EPL + e] = acc[hh][e];
+      for (int j = 0; j < CPL; ++j) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          s_acc[wave][hh][(j * LPR + c) * EPL + e] = acc[hh][j * EPL + e];
+      }
       if (c == 0) {
         s_m[wave][hh] = m[hh];
         s_l[wave][hh] = l[hh];
@@ -352,15 +401,15 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   __syncthreads();
 
   // Merge the waves and write the result or the partial.
-  for (uint32_t i = tid; i < GT * D; i += kThreads) {
+  for (uint32_t i = tid; i < GT * D; i += NTH) {
     const uint32_t hh = i / D, e = i % D;
     float mx = s_m[0][hh];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, s_m[w][hh]);
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, s_m[w][hh]);
     const float mref = mx == -INFINITY ? 0.0f : mx;
     float L = 0.0f, O = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = __builtin_amdgcn_exp2f(s_m[w][hh] - mref);
       L = fmaf(s_l[w][hh], f, L);
       O = fmaf(s_acc[w][hh][e], f, O);
@@ -376,7 +425,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
 }
 
 // One wave per (sequence, query head) with more than one partition: merges the
-// partitions with the log-sum-exp rule, normalises and rounds to dtype.
+// partitions with the log-sum-exp rule, normalises and rounds to dtype. Lane j
+// reads partition j's (max, sum) so the partials are fetched in parallel; the
+// weights are then shared through the wave's lanes.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const ReduceKernelArgs a) {
   const uint32_t lane = threadIdx.x % kWave;
@@ -388,11 +439,21 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const ReduceKer
   const uint32_t nparts = num_parts(n, a.part_tokens);
   if (nparts <= 1) return;
   const float2* ml = a.ws_ml + sh * a.max_parts;
-  float mx = -INFINITY;
-  for (uint32_t j = 0; j < nparts; ++j) mx = fmaxf(mx, ml[j].x);
-  float L = 0.0f;
-  for (uint32_t j = 0; j < nparts; ++j) L = fmaf(ml[j].y, __builtin_amdgcn_exp2f(ml[j].x - mx), L);
   const float* o = a.ws_o + sh * a.max_parts * a.head_dim;
+  // global max over partitions
+  float mx = -INFINITY;
+  for (uint32_t j = lane; j < nparts; j += kWave) mx = fmaxf(mx, ml[j].x);
+#pragma unroll
+  for (int sft = 32; sft >= 1; sft >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sft));
+  // total weight
+  float L = 0.0f;
+  for (uint32_t j = lane; j < nparts; j += kWave) {
+    const float2 v = ml[j];
+    L = fmaf(v.y, __builtin_amdgcn_exp2f(v.x - mx), L);
+  }
+#pragma unroll
+  for (int sft = 32; sft >= 1; sft >>= 1) L += __shfl_xor(L, sft);
+  // weighted sum of the partial vectors, partitions in order
   for (uint32_t e = lane; e < a.head_dim; e += kWave) {
     float O = 0.0f;
     for (uint32_t j = 0; j < nparts; ++j)
@@ -401,11 +462,20 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const ReduceKer
   }
 }
 
+// Launch shapes measured on MI355X (bf16, d=128): for one query head per KV
+// head the kernel streams at the HBM ceiling with 8 row loads per lane in
+// flight; wider GQA tiles are VALU-heavy and run best with fewer loads per
+// tile and the register budget capped for 4 waves per SIMD.
+template <int DT, int D, int GT>
+struct DefaultTune {
+  using type = Tune<4, GT == 1 ? 8 : 4, true, GT >= 8 ? 2 : 4>;
+};
+
 template <int DT, int D, int GT>
 hipError_t launch_pd(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
-  constexpr int NLOAD = GT >= 8 ? 4 : 8;
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, GT, NLOAD>), dim3(uint32_t(nwg)),
-                     dim3(kThreads), 0, stream, a);
+  using TU = typename DefaultTune<DT, D, GT>::type;
+  hipLaunchKernelGGL((decode_partition_kernel<DT, D, GT, TU>), dim3(uint32_t(nwg)),
+                     dim3(TU::NW * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
