@@ -43,6 +43,9 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kWaves = 4;                // waves per workgroup of the reduce kernel
@@ -191,6 +194,112 @@ __device__ inline uint32_t num_parts(int32_t n, uint32_t part_tokens) {
   return n <= 0 ? 1u : (uint32_t(n) + part_tokens - 1) / part_tokens;
 }
 
+// Workgroup-level description of one partition's work.
+struct Partition {
+  uint32_t s;          // sequence
+  uint32_t g;          // KV head
+  uint32_t part;       // partition index within the sequence
+  uint32_t nparts;     // partitions of the sequence
+  uint32_t cnt;        // tokens of this partition
+  uint64_t out_row0;   // first (sequence, query head) row of the head tile
+};
+
+// Decodes the workgroup index into (sequence, KV head, query-head tile,
+// partition), checks the sequence's length and table slice, and resolves each
+// token of the partition to the element offset of head g's row in the pool
+// (s_row). Returns false when the workgroup has nothing (more) to do; for a
+// malformed sequence it has then already written the NaN result.
+template <int DT, int D, int GT, int NTH>
+__device__ inline bool setup_partition(const DecodeKernelArgs& a, uint64_t* s_row, Partition& w) {
+  const uint32_t tid = threadIdx.x;
+  uint32_t bid = blockIdx.x;
+  const uint32_t ht = bid % a.head_tiles;
+  bid /= a.head_tiles;
+  w.part = bid % a.max_parts;
+  w.s = bid / a.max_parts;
+  const uint32_t tiles_per_group = a.group / GT;
+  w.g = ht / tiles_per_group;
+  const uint32_t h0 = w.g * a.group + (ht % tiles_per_group) * GT;
+
+  const int32_t n = a.context_lens[w.s];
+  w.nparts = num_parts(n, a.part_tokens);
+  if (w.part >= w.nparts) return false;
+
+  w.out_row0 = uint64_t(w.s) * a.num_q_heads + h0;
+  if (length_is_bad(n, a.max_context_len)) {
+    if (w.part == 0)
+      for (uint32_t i = tid; i < GT * D; i += NTH) store_out<DT>(a.out, w.out_row0 * D + i, NAN);
+    return false;
+  }
+
+  const uint64_t first = read_idx(a.seq_ptr, w.s, a.idx64);
+  const uint64_t last = read_idx(a.seq_ptr, uint64_t(w.s) + 1, a.idx64);
+  bool bad = first > last || last > a.block_table_len ||
+             uint64_t(n) > (last - first) * uint64_t(a.page_size);
+
+  const uint32_t p0 = w.part * a.part_tokens;
+  w.cnt = bad || n == 0 ? 0u : min(uint32_t(n) - p0, a.part_tokens);
+
+  int bad_page = 0;
+  for (uint32_t i = tid; i < w.cnt; i += NTH) {
+    const uint32_t t = p0 + i;
+    const uint32_t lp = fastdiv(t, a.page_div);
+    const uint32_t off = t - lp * a.page_size;
+    uint64_t phys = read_idx(a.block_table, first + lp, a.idx64);
+    if (phys >= a.num_pages) {
+      bad_page = 1;
+      phys = 0;
+    }
+    s_row[i] = ((phys * a.page_size + off) * a.num_kv_heads + w.g) * uint64_t(D);
+  }
+  bad = __syncthreads_or(bad_page) != 0 || bad;
+
+  if (bad) {  // malformed index buffers: NaN result for this partition
+    if (w.nparts == 1) {
+      for (uint32_t i = tid; i < GT * D; i += NTH)
+        store_out<DT>(a.out, w.out_row0 * D + i, NAN);
+    } else {
+      for (uint32_t i = tid; i < GT * D; i += NTH) {
+        const uint64_t r = (w.out_row0 + i / D) * a.max_parts + w.part;
+        a.ws_o[r * D + i % D] = NAN;
+        if (i % D == 0) a.ws_ml[r] = make_float2(NAN, NAN);
+      }
+    }
+    return false;
+  }
+  return true;
+}
+
+// Merges the waves' (max, sum, vector) triples for each query head of the
+// tile (log-sum-exp rule) and writes the normalised result, or the partial of
+// this partition when the sequence has several.
+template <int DT, int D, int GT, int NW>
+__device__ inline void finish_partition(const DecodeKernelArgs& a, const Partition& w,
+                                        const float (*s_m)[GT], const float (*s_l)[GT],
+                                        const float (*s_acc)[GT][D]) {
+  for (uint32_t i = threadIdx.x; i < GT * D; i += NW * kWave) {
+    const uint32_t hh = i / D, e = i % D;
+    float mx = s_m[0][hh];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) mx = fmaxf(mx, s_m[v][hh]);
+    const float mref = mx == -INFINITY ? 0.0f : mx;
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float f = __builtin_amdgcn_exp2f(s_m[v][hh] - mref);
+      L = fmaf(s_l[v][hh], f, L);
+      O = fmaf(s_acc[v][hh][e], f, O);
+    }
+    if (w.nparts == 1) {
+      store_out<DT>(a.out, (w.out_row0 + hh) * D + e, L > 0.0f ? O / L : 0.0f);
+    } else {
+      const uint64_t r = (w.out_row0 + hh) * a.max_parts + w.part;
+      a.ws_o[r * D + e] = O;
+      if (e == 0) a.ws_ml[r] = make_float2(mx, L);
+    }
+  }
+}
+
 template <int DT, int D, int GT, class TU>
 __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel(
     const DecodeKernelArgs a) {
@@ -213,67 +322,12 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
   __shared__ float s_l[NW][GT];
   __shared__ float s_acc[NW][GT][D];
 
-  const uint32_t tid = threadIdx.x;
-  const uint32_t lane = tid % kWave;
-  const uint32_t wave = tid / kWave;
-
-  uint32_t bid = blockIdx.x;
-  const uint32_t ht = bid % a.head_tiles;
-  bid /= a.head_tiles;
-  const uint32_t part = bid % a.max_parts;
-  const uint32_t s = bid / a.max_parts;
-  const uint32_t tiles_per_group = a.group / GT;
-  const uint32_t g = ht / tiles_per_group;
-  const uint32_t h0 = g * a.group + (ht % tiles_per_group) * GT;
-
-  const int32_t n = a.context_lens[s];
-  const uint32_t nparts = num_parts(n, a.part_tokens);
-  if (part >= nparts) return;
-
-  const uint64_t out_row0 = uint64_t(s) * a.num_q_heads + h0;  // first (s, h) row of the tile
-  if (length_is_bad(n, a.max_context_len)) {
-    if (part == 0)
-      for (uint32_t i = tid; i < GT * D; i += NTH) store_out<DT>(a.out, out_row0 * D + i, NAN);
-    return;
-  }
-
-  const uint64_t first = read_idx(a.seq_ptr, s, a.idx64);
-  const uint64_t last = read_idx(a.seq_ptr, uint64_t(s) + 1, a.idx64);
-  bool bad = first > last || last > a.block_table_len ||
-             uint64_t(n) > (last - first) * uint64_t(a.page_size);
-
-  const uint32_t p0 = part * a.part_tokens;
-  const uint32_t cnt = bad || n == 0 ? 0u : min(uint32_t(n) - p0, a.part_tokens);
-
-  // Resolve each token of the partition to its pool row (element offset of
-  // head g's row), once per workgroup.
-  int bad_page = 0;
-  for (uint32_t i = tid; i < cnt; i += NTH) {
-    const uint32_t t = p0 + i;
-    const uint32_t lp = fastdiv(t, a.page_div);
-    const uint32_t off = t - lp * a.page_size;
-    uint64_t phys = read_idx(a.block_table, first + lp, a.idx64);
-    if (phys >= a.num_pages) {
-      bad_page = 1;
-      phys = 0;
-    }
-    s_row[i] = ((phys * a.page_size + off) * a.num_kv_heads + g) * uint64_t(D);
-  }
-  bad = __syncthreads_or(bad_page) != 0 || bad;
-
-  if (bad) {  // malformed index buffers: NaN result for this partition
-    if (nparts == 1) {
-      for (uint32_t i = tid; i < GT * D; i += NTH)
-        store_out<DT>(a.out, out_row0 * D + i, NAN);
-    } else {
-      for (uint32_t i = tid; i < GT * D; i += NTH) {
-        const uint64_t r = (out_row0 + i / D) * a.max_parts + part;
-        a.ws_o[r * D + i % D] = NAN;
-        if (i % D == 0) a.ws_ml[r] = make_float2(NAN, NAN);
-      }
-    }
-    return;
-  }
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t wave = threadIdx.x / kWave;
+  Partition w;
+  if (!setup_partition<DT, D, GT, NTH>(a, s_row, w)) return;
+  const uint32_t cnt = w.cnt;
+  const uint64_t out_row0 = w.out_row0;
 
   const uint32_t row = lane / LPR;  // which row of a wave load this lane reads
   const uint32_t c = lane % LPR;    // lane's chunks of that row: j*LPR + c, j < CPL
@@ -400,28 +454,239 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
   }
   __syncthreads();
 
-  // Merge the waves and write the result or the partial.
-  for (uint32_t i = tid; i < GT * D; i += NTH) {
-    const uint32_t hh = i / D, e = i % D;
-    float mx = s_m[0][hh];
+  finish_partition<DT, D, GT, NW>(a, w, s_m, s_l, s_acc);
+}
+
+
+// ---------------------------------------------------------------------------
+// GQA groups of 4 or more query heads: q.K^T and P.V on the matrix cores.
+//
+// Per wave and 32-token tile (two 16-token groups), with v_mfma_f32_16x16x32
+// (bf16 or f16 inputs, fp32 accumulate; lane layout: A[l%16][8(l/16)+e],
+// B[8(l/16)+e][l%16], D[4(l/16)+r][l%16]):
+//   * K and V rows are loaded row-major (16-byte lane loads, whole rows per
+//     group of lanes, the pattern that streams at the HBM ceiling) and
+//     written to this wave's LDS tile, rows padded by 16 bytes so the operand
+//     reads below hit distinct banks;
+//   * scores: S^T[token][head] = K Q^T, A = K read back per token row, B = q
+//     (columns are the tile's query heads, unused columns zero). Lane l ends
+//     with tokens 16g+4(l/16)+r of head l%16;
+//   * online softmax per head in base 2; the running max is shared by the four
+//     lanes holding the head (shuffles across lane quarters);
+//   * P.V: O^T[d][head] = V^T P^T. The contraction index k = 8(l/16)+j is
+//     mapped to token 16(j/4)+4(l/16)+(j%4), which is exactly where the scores
+//     already sit, so P needs no data movement; V^T is gathered from LDS in
+//     the same token order. P is rounded to the input type for the matrix
+//     cores and the softmax denominator sums the rounded weights.
+// The next tile's loads are issued before the current tile is computed.
+// ---------------------------------------------------------------------------
+
+template <typename V>
+__device__ inline V as_vec(const u32x4 w) {
+  V r;
+  __builtin_memcpy(&r, &w, sizeof(r));
+  return r;
+}
+
+template <int DT>
+__device__ inline f32x4 mfma_16x16x32(const u32x4 a, const u32x4 b, const f32x4 c) {
+  if constexpr (DT == kBF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_vec<bf16x8>(a), as_vec<bf16x8>(b), c, 0, 0,
+                                                   0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_vec<f16x8>(a), as_vec<f16x8>(b), c, 0, 0, 0);
+  }
+}
+
+// fp32 -> 16-bit input type, round to nearest even; returns the bits.
+template <int DT>
+__device__ inline uint32_t round16(float x) {
+  if constexpr (DT == kBF16) {
+    const uint32_t u = __float_as_uint(x);  // x is a finite softmax weight in [0, 1]
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  } else {
+    const _Float16 h = _Float16(x);
+    uint16_t b;
+    __builtin_memcpy(&b, &h, 2);
+    return b;
+  }
+}
+
+template <int DT>
+__device__ inline float widen_bits16(uint32_t b) {
+  if constexpr (DT == kBF16) {
+    return __uint_as_float(b << 16);
+  } else {
+    const uint16_t h16 = uint16_t(b);
+    _Float16 h;
+    __builtin_memcpy(&h, &h16, 2);
+    return float(h);
+  }
+}
+
+template <int DT, int D, int GT, class TU>
+__global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_kernel(
+    const DecodeKernelArgs a) {
+  static_assert(DT != kF32 && D % 32 == 0 && D <= 128 && GT <= 16, "unsupported shape");
+  constexpr int NW = TU::NW;
+  constexpr int NTH = NW * kWave;
+  constexpr int CPR = D / 8;       // 16-byte chunks per token row
+  constexpr int LPR = CPR;         // lanes per row in the row-major loads
+  constexpr int RPL = kWave / LPR; // rows per wave load
+  constexpr int TT = 32;           // tokens per tile
+  constexpr int NL = TT / RPL;     // wave loads per tile, for K and for V
+  constexpr int ROWB = D * 2 + 16; // LDS bytes per tile row (16-byte pad)
+  constexpr int KS = D / 32;       // score MFMAs per 16 tokens (d steps)
+  constexpr int NB = D / 16;       // P.V MFMAs per tile (16-column blocks of d)
+
+  __shared__ uint64_t s_row[kMaxPartTokens];
+  __shared__ __attribute__((aligned(16))) char s_tile[NW][2][TT * ROWB];
+  __shared__ float s_m[NW][GT];
+  __shared__ float s_l[NW][GT];
+  static_assert(sizeof(float) * GT * D <= 2 * TT * ROWB, "merge buffer must fit the tiles");
+
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t wave = threadIdx.x / kWave;
+  Partition w;
+  if (!setup_partition<DT, D, GT, NTH>(a, s_row, w)) return;
+  const uint32_t cnt = w.cnt;
+
+  const uint32_t q4 = lane / 16;   // lane quarter
+  const uint32_t col = lane % 16;  // MFMA column: query head of the tile (valid if < GT)
+
+  u32x4 qop[KS];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, s_m[w][hh]);
-    const float mref = mx == -INFINITY ? 0.0f : mx;
-    float L = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = __builtin_amdgcn_exp2f(s_m[w][hh] - mref);
-      L = fmaf(s_l[w][hh], f, L);
-      O = fmaf(s_acc[w][hh][e], f, O);
-    }
-    if (nparts == 1) {
-      store_out<DT>(a.out, (out_row0 + hh) * D + e, L > 0.0f ? O / L : 0.0f);
-    } else {
-      const uint64_t r = (out_row0 + hh) * a.max_parts + part;
-      a.ws_o[r * D + e] = O;
-      if (e == 0) a.ws_ml[r] = make_float2(mx, L);
+  for (int ks = 0; ks < KS; ++ks) {
+    qop[ks] = u32x4{0, 0, 0, 0};
+    if (col < GT) {
+      const char* qp = static_cast<const char*>(a.q) + ((w.out_row0 + col) * D + 32 * ks + 8 * q4) * 2;
+      qop[ks] = *reinterpret_cast<const u32x4*>(qp);
     }
   }
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY, l = 0.0f;  // running max (base 2) and weight sum of head `col`
+
+  const uint32_t lr = lane / LPR, lc = lane % LPR;  // row-major load: row, 16-byte chunk
+  char* kt = s_tile[wave][0];
+  char* vt = s_tile[wave][1];
+  const char* kbase = static_cast<const char*>(a.k_cache) + lc * 16;
+  const char* vbase = static_cast<const char*>(a.v_cache) + lc * 16;
+
+  uint32_t tb = wave * TT;
+  if (tb < cnt) {
+    u32x4 kr[NL], vr[NL];
+    auto load_tile = [&](uint32_t t0) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const uint32_t li = t0 + i * RPL + lr;
+        const uint64_t off = s_row[li < cnt ? li : cnt - 1] * 2;
+        kr[i] = load16<TU::NT>(kbase + off);
+        vr[i] = load16<TU::NT>(vbase + off);
+      }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const uint32_t r = i * RPL + lr;
+        *reinterpret_cast<u32x4*>(kt + r * ROWB + lc * 16) = kr[i];
+        *reinterpret_cast<u32x4*>(vt + r * ROWB + lc * 16) = vr[i];
+      }
+    };
+    load_tile(tb);
+    store_tile();
+    while (true) {
+      const uint32_t tn = tb + NW * TT;
+      const bool has_next = tn < cnt;
+      if (has_next) load_tile(tn);
+
+      // scores of tokens 16g + 4*q4 + r for head `col`
+      f32x4 sacc[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        sacc[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 kop =
+              *reinterpret_cast<const u32x4*>(kt + (16 * g + col) * ROWB + (32 * ks + 8 * q4) * 2);
+          sacc[g] = mfma_16x16x32<DT>(kop, qop[ks], sacc[g]);
+        }
+      }
+      float z[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t t = 16 * (j / 4) + 4 * q4 + (j % 4);
+        const float zz = sacc[j / 4][j % 4] * a.scale_log2;
+        z[j] = tb + t < cnt ? zz : -INFINITY;
+      }
+      float mt = z[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mt = fmaxf(mt, z[j]);
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m, mt);
+      const float mu = mn == -INFINITY ? 0.0f : mn;
+      const float corr = __builtin_amdgcn_exp2f(m - mu);
+      m = mn;
+      l *= corr;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) acc[n] *= corr;
+
+      uint32_t pw[4];
+      float psum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const uint32_t b0 = round16<DT>(__builtin_amdgcn_exp2f(z[j] - mu));
+        const uint32_t b1 = round16<DT>(__builtin_amdgcn_exp2f(z[j + 1] - mu));
+        psum += widen_bits16<DT>(b0) + widen_bits16<DT>(b1);
+        pw[j / 2] = b0 | (b1 << 16);
+      }
+      if (col >= GT) {
+        pw[0] = pw[1] = pw[2] = pw[3] = 0u;
+        psum = 0.0f;
+      }
+      l += psum;
+      const u32x4 pop = u32x4{pw[0], pw[1], pw[2], pw[3]};
+
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        uint32_t vw[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const uint32_t t0 = 16 * (j / 4) + 4 * q4 + (j % 4);
+          const uint32_t e = (16 * n + col) * 2;
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(vt + t0 * ROWB + e);
+          const uint32_t hi = *reinterpret_cast<const uint16_t*>(vt + (t0 + 1) * ROWB + e);
+          vw[j / 2] = lo | (hi << 16);
+        }
+        acc[n] = mfma_16x16x32<DT>(u32x4{vw[0], vw[1], vw[2], vw[3]}, pop, acc[n]);
+      }
+      if (!has_next) break;
+      store_tile();
+      tb = tn;
+    }
+  }
+
+  // the four lane quarters hold disjoint tokens of each head: add their sums
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  __syncthreads();  // every wave is done with its tile before the tiles become merge space
+  float(*s_acc)[GT][D] = reinterpret_cast<float(*)[GT][D]>(&s_tile[0][0][0]);
+  if (col < GT) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_acc[wave][col][16 * n + 4 * q4 + r] = acc[n][r];
+    }
+    if (q4 == 0) {
+      s_m[wave][col] = m;
+      s_l[wave][col] = l;
+    }
+  }
+  __syncthreads();
+  finish_partition<DT, D, GT, NW>(a, w, s_m, s_l, s_acc);
 }
 
 // One wave per (sequence, query head) with more than one partition: merges the
@@ -479,9 +744,36 @@ hipError_t launch_pd(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream
   return hipGetLastError();
 }
 
+// Matrix-core path: 16-bit inputs, head_dim a multiple of 32 up to 128, and
+// at least 4 query heads per KV head (below that the VALU kernel already
+// streams at the bandwidth ceiling).
+bool mfma_eligible(int dtype, uint32_t head_dim, uint32_t group) {
+  return dtype != kF32 && (head_dim == 32 || head_dim == 64 || head_dim == 128) &&
+         group % 4 == 0;
+}
+
+template <int DT, int D, int GT>
+hipError_t launch_pm(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
+  using TU = Tune<4, 0, true, 2>;
+  hipLaunchKernelGGL((decode_partition_mfma_kernel<DT, D, GT, TU>), dim3(uint32_t(nwg)),
+                     dim3(TU::NW * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int DT, int D>
 hipError_t launch_d(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
-  switch (heads_per_workgroup(a.group)) {
+  const uint32_t gt = heads_per_workgroup(DT, D, a.group);
+  if constexpr (DT != kF32 && D >= 32 && D <= 128) {
+    if (mfma_eligible(DT, D, a.group)) {
+      switch (gt) {
+        case 4: return launch_pm<DT, D, 4>(a, nwg, stream);
+        case 8: return launch_pm<DT, D, 8>(a, nwg, stream);
+        case 16: return launch_pm<DT, D, 16>(a, nwg, stream);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
+  switch (gt) {
     case 1: return launch_pd<DT, D, 1>(a, nwg, stream);
     case 2: return launch_pd<DT, D, 2>(a, nwg, stream);
     case 4: return launch_pd<DT, D, 4>(a, nwg, stream);
@@ -506,7 +798,8 @@ hipError_t launch_dt(uint32_t head_dim, const DecodeKernelArgs& a, uint64_t nwg,
 
 }  // namespace
 
-uint32_t heads_per_workgroup(uint32_t group) {
+uint32_t heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group) {
+  if (mfma_eligible(dtype, head_dim, group)) return group % 16 == 0 ? 16 : group % 8 == 0 ? 8 : 4;
   if (group % 8 == 0) return 8;
   if (group % 4 == 0) return 4;
   if (group % 2 == 0) return 2;

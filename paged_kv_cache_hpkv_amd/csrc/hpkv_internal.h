@@ -13,7 +13,7 @@ enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : 2; }
 
 // Largest split-context partition the decode kernel's LDS row table holds.
-constexpr uint32_t kMaxPartTokens = 1024;
+constexpr uint32_t kMaxPartTokens = 512;
 
 // Division by a runtime divisor 1 <= d < 2^31 for numerators n < 2^31:
 // n / d == (n * mul) >> shift with shift = 31 + ceil(log2 d) and
@@ -72,8 +72,9 @@ struct ReduceKernelArgs {
   uint32_t max_context_len;
 };
 
-// Query heads served by one workgroup for a GQA group of `group` heads.
-uint32_t heads_per_workgroup(uint32_t group);
+// Query heads served by one decode workgroup for a GQA group of `group` heads
+// (the matrix-core path takes up to 16 heads of a group at once).
+uint32_t heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group);
 
 hipError_t launch_slot_mapping(bool idx64, const void* block_table, uint64_t block_table_len,
                                const void* seq_ptr, uint32_t num_seqs, uint32_t page_size,

@@ -32,8 +32,9 @@ def test_llama7b_layer(dtype, index):
     print(f"max err {r['max_err']:.3e}", flush=True)
 
 
-def test_gqa_layer():
-    r = check_step(workloads.gqa())
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_gqa_layer(dtype):
+    r = check_step(workloads.gqa(dtype=dtype))
     print(f"max err {r['max_err']:.3e}", flush=True)
 
 
@@ -57,16 +58,17 @@ def test_prefix_sharing_chunked_prefill():
 @pytest.mark.parametrize("hq,hkv,d,dtype", [(16, 2, 64, "bf16"), (4, 4, 256, "f16"),
                                             (8, 2, 32, "f32"), (6, 2, 16, "bf16"),
                                             (32, 2, 128, "bf16"), (3, 3, 8, "bf16"),
-                                            (8, 1, 256, "f32")])
+                                            (8, 1, 256, "f32"), (8, 2, 32, "f16"),
+                                            (16, 4, 128, "f16"), (16, 2, 64, "f16"),
+                                            (24, 2, 128, "bf16"), (32, 1, 64, "f16"),
+                                            (8, 2, 256, "bf16")])
 def test_other_head_shapes(hq, hkv, d, dtype):
     rng = np.random.default_rng(hq * 1000 + d)
     ctx = rng.integers(1, 1500, size=5).astype(np.int32)
     ctx[0] = 1
-    base = workloads.llama7b(dtype=dtype, seed=7, batch=5)
     num_pages, sp, bt = workloads._random_pool_tables(rng, ctx, 16, "u32")
     w = workloads.Workload(f"shape{hq}x{hkv}x{d}", dtype, "u32", hq, hkv, d, 16, num_pages, ctx,
                            sp, bt, d ** -0.5, chunks=workloads._decode_step_chunks(ctx), seed=7)
-    del base
     r = check_step(w)
     print(f"max err {r['max_err']:.3e}", flush=True)
 
