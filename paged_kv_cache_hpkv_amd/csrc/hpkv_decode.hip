@@ -204,19 +204,23 @@ struct Partition {
   uint64_t out_row0;   // first (sequence, query head) row of the head tile
 };
 
-// Decodes the workgroup index into (sequence, KV head, query-head tile,
-// partition), checks the sequence's length and table slice, and resolves each
+// Decodes the workgroup index into (query-head tile, sequence, partition),
+// checks the sequence's length and table slice, and resolves each
 // token of the partition to the element offset of head g's row in the pool
 // (s_row). Returns false when the workgroup has nothing (more) to do; for a
 // malformed sequence it has then already written the NaN result.
 template <int DT, int D, int GT, int NTH>
 __device__ inline bool setup_partition(const DecodeKernelArgs& a, uint64_t* s_row, Partition& w) {
   const uint32_t tid = threadIdx.x;
+  // Grid order: head tile fastest, then sequence, then partition. Every
+  // sequence has a partition 0, so the first num_seqs*head_tiles workgroups
+  // all carry work; the higher partitions, empty for short sequences, are
+  // dispatched last where their early exit overlaps the tail of the launch.
   uint32_t bid = blockIdx.x;
   const uint32_t ht = bid % a.head_tiles;
   bid /= a.head_tiles;
-  w.part = bid % a.max_parts;
-  w.s = bid / a.max_parts;
+  w.s = bid % a.num_seqs;
+  w.part = bid / a.num_seqs;
   const uint32_t tiles_per_group = a.group / GT;
   w.g = ht / tiles_per_group;
   const uint32_t h0 = w.g * a.group + (ht % tiles_per_group) * GT;
