@@ -204,40 +204,59 @@ struct Partition {
   uint64_t out_row0;   // first (sequence, query head) row of the head tile
 };
 
-// Decodes the workgroup index into (query-head tile, sequence, partition),
-// checks the sequence's length and table slice, and resolves each
-// token of the partition to the element offset of head g's row in the pool
-// (s_row). Returns false when the workgroup has nothing (more) to do; for a
-// malformed sequence it has then already written the NaN result.
-template <int DT, int D, int GT, int NTH>
-__device__ inline bool setup_partition(const DecodeKernelArgs& a, uint64_t* s_row, Partition& w) {
-  const uint32_t tid = threadIdx.x;
-  // Grid order: head tile fastest, then sequence, then partition. Every
-  // sequence has a partition 0, so the first num_seqs*head_tiles workgroups
-  // all carry work; the higher partitions, empty for short sequences, are
-  // dispatched last where their early exit overlaps the tail of the launch.
+// One work item: sequence, partition, KV head g and the first query head h0
+// of the tile it serves.
+struct WorkItem {
+  uint32_t s, part, g, h0;
+};
+
+// Grid order: head tile fastest, then sequence, then partition. Every
+// sequence has a partition 0, so the first num_seqs*head_tiles workgroups all
+// carry work; the higher partitions, empty for short sequences, are
+// dispatched last where their early exit overlaps the tail of the launch.
+// Tile ht serves query heads [h0, h0 + GT) of KV head g.
+template <int GT>
+__device__ inline WorkItem grid_item(const DecodeKernelArgs& a) {
   uint32_t bid = blockIdx.x;
   const uint32_t ht = bid % a.head_tiles;
   bid /= a.head_tiles;
-  w.s = bid % a.num_seqs;
-  w.part = bid / a.num_seqs;
+  WorkItem it;
+  it.s = bid % a.num_seqs;
+  it.part = bid / a.num_seqs;
   const uint32_t tiles_per_group = a.group / GT;
-  w.g = ht / tiles_per_group;
-  const uint32_t h0 = w.g * a.group + (ht % tiles_per_group) * GT;
+  it.g = ht / tiles_per_group;
+  it.h0 = it.g * a.group + (ht % tiles_per_group) * GT;
+  return it;
+}
 
+// Checks the item's sequence length and table slice, and resolves each token
+// of the partition to the element offset of head g's row in the pool (s_row).
+// Returns false when the workgroup has nothing (more) to do; for a malformed
+// sequence it has then already written the NaN result of its NH query heads
+// h0 .. h0+NH-1.
+template <int DT, int D, int NH, int NTH>
+__device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem& it,
+                                       uint64_t* s_row, Partition& w) {
+  const uint32_t tid = threadIdx.x;
+  w.s = it.s;
+  w.part = it.part;
+  w.g = it.g;
+  const uint32_t h0 = it.h0;
+
+  // the length and the table slice bounds are independent loads: issue both
   const int32_t n = a.context_lens[w.s];
+  const uint64_t first = read_idx(a.seq_ptr, w.s, a.idx64);
+  const uint64_t last = read_idx(a.seq_ptr, uint64_t(w.s) + 1, a.idx64);
   w.nparts = num_parts(n, a.part_tokens);
   if (w.part >= w.nparts) return false;
 
   w.out_row0 = uint64_t(w.s) * a.num_q_heads + h0;
   if (length_is_bad(n, a.max_context_len)) {
     if (w.part == 0)
-      for (uint32_t i = tid; i < GT * D; i += NTH) store_out<DT>(a.out, w.out_row0 * D + i, NAN);
+      for (uint32_t i = tid; i < NH * D; i += NTH) store_out<DT>(a.out, w.out_row0 * D + i, NAN);
     return false;
   }
 
-  const uint64_t first = read_idx(a.seq_ptr, w.s, a.idx64);
-  const uint64_t last = read_idx(a.seq_ptr, uint64_t(w.s) + 1, a.idx64);
   bool bad = first > last || last > a.block_table_len ||
              uint64_t(n) > (last - first) * uint64_t(a.page_size);
 
@@ -260,10 +279,10 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, uint64_t* s_ro
 
   if (bad) {  // malformed index buffers: NaN result for this partition
     if (w.nparts == 1) {
-      for (uint32_t i = tid; i < GT * D; i += NTH)
+      for (uint32_t i = tid; i < NH * D; i += NTH)
         store_out<DT>(a.out, w.out_row0 * D + i, NAN);
     } else {
-      for (uint32_t i = tid; i < GT * D; i += NTH) {
+      for (uint32_t i = tid; i < NH * D; i += NTH) {
         const uint64_t r = (w.out_row0 + i / D) * a.max_parts + w.part;
         a.ws_o[r * D + i % D] = NAN;
         if (i % D == 0) a.ws_ml[r] = make_float2(NAN, NAN);
@@ -329,7 +348,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t wave = threadIdx.x / kWave;
   Partition w;
-  if (!setup_partition<DT, D, GT, NTH>(a, s_row, w)) return;
+  if (!setup_partition<DT, D, GT, NTH>(a, grid_item<GT>(a), s_row, w)) return;
   const uint32_t cnt = w.cnt;
   const uint64_t out_row0 = w.out_row0;
 
@@ -463,6 +482,104 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
 
 
 // ---------------------------------------------------------------------------
+// One query head per KV head (MHA), head-parallel: the 16-lane row groups of a
+// wave take RPL adjacent KV heads of the same token, so every wave load reads
+// one token's rows of those heads as one contiguous span, and the NW waves of
+// the workgroup together read the token's rows of HB = NW*RPL heads. Each
+// wave walks all tokens of the partition for its heads, so no merge across
+// waves or row groups is needed: each row group writes its head's result.
+// ---------------------------------------------------------------------------
+template <int DT, int D, class TU>
+__global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_hp_kernel(
+    const DecodeKernelArgs a) {
+  constexpr int NW = TU::NW;
+  constexpr int NTH = NW * kWave;
+  constexpr int NLOAD = TU::NLOAD;   // tokens per tile
+  constexpr int EB = Elem<DT>::bytes;
+  constexpr int EPL = 16 / EB;
+  constexpr int LPR = D / EPL;       // lanes per head row
+  constexpr int RPL = kWave / LPR;   // heads per wave
+  constexpr int HB = NW * RPL;       // heads per workgroup
+  static_assert(LPR >= 1 && LPR <= kWave && (LPR & (LPR - 1)) == 0, "unsupported head_dim");
+
+  __shared__ uint64_t s_row[kMaxPartTokens];
+
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t wave = threadIdx.x / kWave;
+  uint32_t bid = blockIdx.x;
+  WorkItem it;
+  const uint32_t hb = bid % a.head_tiles;  // head block
+  bid /= a.head_tiles;
+  it.s = bid % a.num_seqs;
+  it.part = bid / a.num_seqs;
+  it.g = hb * HB;
+  it.h0 = it.g;
+  Partition w;
+  if (!setup_partition<DT, D, HB, NTH>(a, it, s_row, w)) return;
+  const uint32_t cnt = w.cnt;
+
+  const uint32_t hw = wave * RPL + lane / LPR;  // head of this row group within the block
+  const uint32_t c = lane % LPR;
+  const uint64_t orow = w.out_row0 + hw;         // (sequence, query head) row
+
+  const u32x4 qv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
+                                                   (orow * D + c * EPL) * EB);
+  float m = -INFINITY, l = 0.0f, acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+
+  const uint64_t lane_off = (uint64_t(hw) * D + c * EPL) * EB;
+  const char* kbase = static_cast<const char*>(a.k_cache) + lane_off;
+  const char* vbase = static_cast<const char*>(a.v_cache) + lane_off;
+
+  for (uint32_t tb = 0; tb < cnt; tb += NLOAD) {
+    u32x4 kr[NLOAD], vr[NLOAD];
+#pragma unroll
+    for (int k = 0; k < NLOAD; ++k) {
+      const uint32_t t = tb + k;
+      const uint64_t off = s_row[t < cnt ? t : cnt - 1] * EB;
+      kr[k] = load16<TU::NT>(kbase + off);
+      vr[k] = load16<TU::NT>(vbase + off);
+    }
+    float sc[NLOAD];
+#pragma unroll
+    for (int k = 0; k < NLOAD; ++k) {
+      const float z = row_sum<LPR>(dot16<DT>(kr[k], qv)) * a.scale_log2;
+      sc[k] = tb + k < cnt ? z : -INFINITY;
+    }
+    float mt = sc[0];
+#pragma unroll
+    for (int k = 1; k < NLOAD; ++k) mt = fmaxf(mt, sc[k]);
+    const float mn = fmaxf(m, mt);  // tb < cnt: at least sc[0] is finite
+    const float corr = __builtin_amdgcn_exp2f(m - mn);
+    l *= corr;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= corr;
+    m = mn;
+#pragma unroll
+    for (int k = 0; k < NLOAD; ++k) {
+      const float p = __builtin_amdgcn_exp2f(sc[k] - mn);
+      l += p;
+      float vf[EPL];
+      widen16<DT>(vr[k], vf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+    }
+  }
+
+  if (w.nparts == 1) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      store_out<DT>(a.out, orow * D + c * EPL + e, l > 0.0f ? acc[e] / l : 0.0f);
+  } else {
+    const uint64_t r = orow * a.max_parts + w.part;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a.ws_o[r * D + c * EPL + e] = acc[e];
+    if (c == 0) a.ws_ml[r] = make_float2(m, l);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // GQA groups of 4 or more query heads: q.K^T and P.V on the matrix cores.
 //
 // Per wave and 32-token tile (two 16-token groups), with v_mfma_f32_16x16x32
@@ -552,7 +669,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_k
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t wave = threadIdx.x / kWave;
   Partition w;
-  if (!setup_partition<DT, D, GT, NTH>(a, s_row, w)) return;
+  if (!setup_partition<DT, D, GT, NTH>(a, grid_item<GT>(a), s_row, w)) return;
   const uint32_t cnt = w.cnt;
 
   const uint32_t q4 = lane / 16;   // lane quarter
@@ -732,12 +849,12 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const ReduceKer
 }
 
 // Launch shapes measured on MI355X (bf16, d=128): for one query head per KV
-// head the kernel streams at the HBM ceiling with 8 row loads per lane in
-// flight; wider GQA tiles are VALU-heavy and run best with fewer loads per
-// tile and the register budget capped for 4 waves per SIMD.
+// head the kernel streams at the HBM ceiling with 8-wave workgroups and 8 row
+// loads per lane in flight; wider GQA tiles are VALU-heavy and run best with
+// fewer loads per tile and the register budget capped for 4 waves per SIMD.
 template <int DT, int D, int GT>
 struct DefaultTune {
-  using type = Tune<4, GT == 1 ? 8 : 4, true, GT >= 8 ? 2 : 4>;
+  using type = Tune<GT == 1 ? 8 : 4, GT == 1 ? 8 : 4, true, GT >= 8 ? 2 : 4>;
 };
 
 template <int DT, int D, int GT>
@@ -758,7 +875,7 @@ bool mfma_eligible(int dtype, uint32_t head_dim, uint32_t group) {
 
 template <int DT, int D, int GT>
 hipError_t launch_pm(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
-  using TU = Tune<4, 0, true, 2>;
+  using TU = Tune<2, 0, true, 2>;  // 2-wave workgroups: more of them resident per CU
   hipLaunchKernelGGL((decode_partition_mfma_kernel<DT, D, GT, TU>), dim3(uint32_t(nwg)),
                      dim3(TU::NW * kWave), 0, stream, a);
   return hipGetLastError();
