@@ -826,25 +826,36 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const ReduceKer
   if (nparts <= 1) return;
   const float2* ml = a.ws_ml + sh * a.max_parts;
   const float* o = a.ws_o + sh * a.max_parts * a.head_dim;
-  // global max over partitions
+  // global max over partitions: lane j holds partition j, j + 64, ...
   float mx = -INFINITY;
   for (uint32_t j = lane; j < nparts; j += kWave) mx = fmaxf(mx, ml[j].x);
 #pragma unroll
   for (int sft = 32; sft >= 1; sft >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sft));
-  // total weight
-  float L = 0.0f;
+  // weight of partition `lane` (the first 64 partitions), and the total weight
+  float wl = 0.0f, L = 0.0f;
   for (uint32_t j = lane; j < nparts; j += kWave) {
     const float2 v = ml[j];
-    L = fmaf(v.y, __builtin_amdgcn_exp2f(v.x - mx), L);
+    const float f = __builtin_amdgcn_exp2f(v.x - mx);
+    if (j == lane) wl = f;
+    L = fmaf(v.y, f, L);
   }
 #pragma unroll
   for (int sft = 32; sft >= 1; sft >>= 1) L += __shfl_xor(L, sft);
-  // weighted sum of the partial vectors, partitions in order
-  for (uint32_t e = lane; e < a.head_dim; e += kWave) {
+  // weighted sum of the partial vectors, partitions in order; every lane runs
+  // every iteration (the weights are read from lane j with v_readlane)
+  for (uint32_t e0 = 0; e0 < a.head_dim; e0 += kWave) {
+    const uint32_t e = e0 + lane;
+    const bool active = e < a.head_dim;
     float O = 0.0f;
-    for (uint32_t j = 0; j < nparts; ++j)
-      O = fmaf(o[uint64_t(j) * a.head_dim + e], __builtin_amdgcn_exp2f(ml[j].x - mx), O);
-    store_out<DT>(a.out, sh * a.head_dim + e, O / L);
+#pragma unroll 8
+    for (uint32_t j = 0; j < nparts; ++j) {
+      const float f = j < uint32_t(kWave)
+                          ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), int(j)))
+                          : __builtin_amdgcn_exp2f(ml[j].x - mx);
+      const float v = active ? o[uint64_t(j) * a.head_dim + e] : 0.0f;
+      O = fmaf(v, f, O);
+    }
+    if (active) store_out<DT>(a.out, sh * a.head_dim + e, O / L);
   }
 }
 

@@ -14,21 +14,33 @@ namespace {
 constexpr int kSlotThreads = 256;
 constexpr int kStoreThreads = 256;
 
+// cu_new entries a slot-mapping workgroup stages in LDS for its search.
+constexpr uint32_t kSlotLdsSeqs = 4096;
+
 // One thread per new token. The owning sequence is found by binary search over
 // cu_new (the largest s with cu_new[s] <= i), which keeps the launch balanced
-// whatever the mix of chunk lengths.
+// whatever the mix of chunk lengths. Batches of up to kSlotLdsSeqs sequences
+// search a copy of cu_new staged in LDS by the workgroup (one coalesced read
+// instead of a chain of dependent global reads).
 template <typename Idx>
 __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
     const Idx* __restrict__ block_table, uint64_t block_table_len, const Idx* __restrict__ seq_ptr,
     uint32_t num_seqs, uint32_t page_size, const int32_t* __restrict__ start_pos,
     const int64_t* __restrict__ cu_new, uint64_t num_new, int64_t* __restrict__ slots) {
+  __shared__ int64_t s_cu[kSlotLdsSeqs + 1];
+  const bool staged = num_seqs <= kSlotLdsSeqs;
+  if (staged) {
+    for (uint32_t k = threadIdx.x; k <= num_seqs; k += kSlotThreads) s_cu[k] = cu_new[k];
+    __syncthreads();
+  }
+  const int64_t* cu = staged ? s_cu : cu_new;
   const uint64_t i = uint64_t(blockIdx.x) * kSlotThreads + threadIdx.x;
   if (i >= num_new) return;
-  // upper bound of i in cu_new[1 .. num_seqs]
+  // upper bound of i in cu[1 .. num_seqs]
   uint32_t lo = 1, hi = num_seqs + 1;
   while (lo < hi) {
     const uint32_t mid = (lo + hi) / 2;
-    if (cu_new[mid] <= int64_t(i)) {
+    if (cu[mid] <= int64_t(i)) {
       lo = mid + 1;
     } else {
       hi = mid;
@@ -36,8 +48,8 @@ __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
   }
   const uint32_t s = lo - 1;
   int64_t slot = -1;
-  if (s < num_seqs && cu_new[s] <= int64_t(i)) {
-    const int64_t p = int64_t(start_pos[s]) + (int64_t(i) - cu_new[s]);
+  if (s < num_seqs && cu[s] <= int64_t(i)) {
+    const int64_t p = int64_t(start_pos[s]) + (int64_t(i) - cu[s]);
     const uint64_t first = seq_ptr[s];
     const uint64_t last = seq_ptr[s + 1];
     if (p >= 0 && first <= last && last <= block_table_len) {
@@ -52,8 +64,9 @@ __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
 }
 
 // One workgroup per new-token row (grid-strided); each thread copies
-// `Chunk`-sized pieces of the row for K and V. Rows whose slot is -1, negative
-// or past the pool are skipped.
+// `Chunk`-sized pieces of the row for K and V. The row is read while its slot
+// is still in flight (the source address does not depend on it); rows whose
+// slot is -1, negative or past the pool are skipped.
 template <typename Chunk>
 __global__ __launch_bounds__(kStoreThreads) void store_kernel(
     const Chunk* __restrict__ key, const Chunk* __restrict__ value, Chunk* __restrict__ k_cache,
@@ -61,16 +74,15 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(
     uint64_t row_chunks, int64_t num_slots) {
   for (uint64_t row = blockIdx.x; row < num_tokens; row += gridDim.x) {
     const int64_t slot = slots[row];
-    if (slot < 0 || slot >= num_slots) continue;
     const Chunk* ksrc = key + row * row_chunks;
     const Chunk* vsrc = value + row * row_chunks;
-    Chunk* kdst = k_cache + uint64_t(slot) * row_chunks;
-    Chunk* vdst = v_cache + uint64_t(slot) * row_chunks;
     for (uint64_t c = threadIdx.x; c < row_chunks; c += kStoreThreads) {
       const Chunk kv = ksrc[c];
       const Chunk vv = vsrc[c];
-      kdst[c] = kv;
-      vdst[c] = vv;
+      if (slot >= 0 && slot < num_slots) {
+        k_cache[uint64_t(slot) * row_chunks + c] = kv;
+        v_cache[uint64_t(slot) * row_chunks + c] = vv;
+      }
     }
   }
 }
