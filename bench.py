@@ -119,7 +119,7 @@ def algorithmic_decode_bytes(w):
     return int(w.kv_bytes_logical() + pages.sum() * idx + per_seq * w.num_seqs)
 
 
-def recorded_traffic():
+def recorded_traffic(w):
     """HBM bytes per partition launch from committed counter runs, if still current."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -129,8 +129,8 @@ def recorded_traffic():
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256") != src_hash:
-        return None
-    return rec
+        return None  # the kernel changed since the counters were taken
+    return rec.get("workloads", {}).get(f"{w.name}/{w.dtype}/{w.index}")
 
 
 def cpu_baseline(w, t, out_gpu):
@@ -211,7 +211,7 @@ def main():
 
     kv = w.kv_bytes_logical()
     value = kv / (ms_per_step * 1e-3) / 1e9
-    rec = recorded_traffic()
+    rec = recorded_traffic(w)
     b = torch.tensor([], dtype=w.torch_dtype).element_size()
     line = {
         "metric": METRIC,
