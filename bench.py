@@ -3,6 +3,9 @@
 A step is one pass of the whole path over one synthetic batch (one layer):
 slot mapping of the new tokens, store of their K/V rows into the page pools,
 then paged decode attention of every sequence (partition + reduce kernels).
+A plain decode step (one new token per sequence, stored at ctx-1) runs as the
+fused hpkv_paged_attention_decode_step, which stores the row inside the decode
+launch; --unfused times the three separate calls instead.
 Default workload: the Llama-2-7B-shaped layer (Hq = Hkv = 32, d = 128,
 16-token pages, 64 sequences with ctx ~ U{512..4096}, bf16, u32 tables), one
 new token per sequence stored at position ctx-1 before decoding.
@@ -61,6 +64,8 @@ def parse():
     p.add_argument("--index", default=None, choices=["u32", "u64"])
     p.add_argument("--roofline-launches", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--unfused", action="store_true",
+                   help="run slot mapping, store and decode as separate calls")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -75,12 +80,28 @@ def make_workload(args):
     return w
 
 
-class Step:
-    """Pre-allocated device state for repeated steps of one workload."""
+def is_decode_step(w):
+    """One new token per sequence at position ctx-1 and no dropped slots."""
+    if len(w.chunks) != 1 or w.drop_mask is not None:
+        return False
+    start, cu = w.chunks[0]
+    return bool(np.all(w.context_lens > 0) and np.array_equal(cu, np.arange(w.num_seqs + 1))
+                and np.array_equal(start, w.context_lens - 1))
 
-    def __init__(self, w, t):
+
+class Step:
+    """Pre-allocated device state for repeated steps of one workload.
+
+    A decode step (one new token per sequence at ctx-1) runs as the fused
+    hpkv_paged_attention_decode_step; any other step (chunked prefill, dropped
+    slots) or --unfused runs hpkv_slot_mapping, hpkv_store_kvcache and
+    hpkv_paged_attention_decode.
+    """
+
+    def __init__(self, w, t, fused):
         import paged_kv_cache_hpkv_amd as hpkv
         self.hpkv, self.w, self.t = hpkv, w, t
+        self.fused = fused
         dev = t.q.device
         self.bt = torch.from_numpy(w.block_table).to(dev)
         self.sp = torch.from_numpy(w.seq_ptr).to(dev)
@@ -94,6 +115,12 @@ class Step:
 
     def __call__(self):
         h, w, t = self.hpkv, self.w, self.t
+        if self.fused:
+            h.hpkv_paged_attention_decode_step(
+                t.q, t.new_keys[0], t.new_values[0], t.k_cache, t.v_cache, self.bt, self.sp,
+                self.ctx, w.scale, w.max_context_len, self.ws, self.out,
+                slots_out=self.chunks[0][2])
+            return
         for c, (start, cu, slots) in enumerate(self.chunks):
             h.hpkv_slot_mapping(self.bt, self.sp, w.page_size, start, cu, slots)
             if self.drop is not None and c == 0:
@@ -169,7 +196,7 @@ def main():
     torch.cuda.set_device(dev)
     w = make_workload(args)
     t = workloads.make_tensors(w, dev)
-    step = Step(w, t)
+    step = Step(w, t, fused=is_decode_step(w) and not args.unfused)
     stream = torch.cuda.current_stream(dev)
 
     if args.copy_calibration:
@@ -238,6 +265,8 @@ def main():
             "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
             "sequences_per_s_per_layer": round(w.num_seqs / (ms_per_step * 1e-3), 1),
             "wall_s_timed_region": round(t_wall, 4),
+            "step": ("fused decode step (store of the ctx-1 row inside the decode launch)"
+                     if step.fused else "slot mapping + store + decode (separate launches)"),
         },
         "roofline": {
             "kernel": "decode_partition_kernel",

@@ -238,6 +238,37 @@ int hpkv_paged_attention_decode_reduce(int dtype, const int32_t* context_lens, u
                                        void* workspace, size_t workspace_bytes, void* out,
                                        void* stream);
 
+/* ---------------------------------------------------------------------------
+ * hpkv_paged_attention_decode_step  (device)
+ *
+ * One fused decode step: for every sequence s with n = context_lens[s] >= 1
+ * the freshly computed K and V rows of its newest token (position n-1, the
+ * decode slot of "Paged KV Cache · AI infra interview lesson", sections
+ * "Walk the Shapes First" and "Common Pitfalls") are written into the pools
+ * at slot block_table[seq_ptr[s] + (n-1)/page_size]*page_size + (n-1)%page_size,
+ * and decode attention then runs over all n tokens, exactly as
+ * hpkv_slot_mapping (start_pos = n-1, one token per sequence) +
+ * hpkv_store_kvcache + hpkv_paged_attention_decode, in the decode's own
+ * launches (the row is stored by the workgroup that reads it).
+ *   new_key, new_value  device [num_seqs, num_kv_heads, head_dim] of dtype,
+ *                       16-byte aligned
+ *   slots_out           device int64 [num_seqs] or NULL: the slot each row went
+ *                       to, -1 for n == 0 and for malformed sequences
+ * Every other argument, requirement and error is that of
+ * hpkv_paged_attention_decode (k_cache and v_cache are written). A sequence
+ * the decode reports as malformed (NaN output) gets no row written.
+ * ------------------------------------------------------------------------- */
+int hpkv_paged_attention_decode_step(int dtype, int index_type, const void* q,
+                                     const void* new_key, const void* new_value, void* k_cache,
+                                     void* v_cache, const void* block_table,
+                                     uint64_t block_table_len, const void* seq_ptr,
+                                     const int32_t* context_lens, uint32_t num_seqs,
+                                     uint32_t num_q_heads, uint32_t num_kv_heads,
+                                     uint32_t head_dim, uint32_t page_size, uint64_t num_pages,
+                                     float scale, uint32_t max_context_len, int64_t* slots_out,
+                                     void* workspace, size_t workspace_bytes, void* out,
+                                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,7 @@ EXPORTED = [
     "hpkv_validate_shape", "hpkv_slot_mapping", "hpkv_store_kvcache",
     "hpkv_paged_attention_decode_workspace_size", "hpkv_paged_attention_decode_partition_tokens",
     "hpkv_paged_attention_decode", "hpkv_paged_attention_decode_partitions",
-    "hpkv_paged_attention_decode_reduce",
+    "hpkv_paged_attention_decode_reduce", "hpkv_paged_attention_decode_step",
 ]
 
 
@@ -72,6 +72,9 @@ def _load():
                                                     vp, vp], i32),
         "hpkv_paged_attention_decode_reduce": ([i32, vp, u32, u32, u32, u32, u32, vp, sz, vp, vp],
                                                i32),
+        "hpkv_paged_attention_decode_step": ([i32, i32, vp, vp, vp, vp, vp, vp, u64, vp, vp, u32,
+                                              u32, u32, u32, u32, u64, f32, u32, vp, vp, sz, vp,
+                                              vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -234,6 +237,22 @@ def hpkv_paged_attention_decode_reduce(context_lens, page_size, max_context_len,
     _check("hpkv_paged_attention_decode_reduce", lib.hpkv_paged_attention_decode_reduce(
         _DTYPE_CODE[out.dtype], _ptr(context_lens), B, hq, d, page_size, int(max_context_len),
         _ptr(workspace), ws_bytes, _ptr(out), _stream(stream, out)))
+
+
+def hpkv_paged_attention_decode_step(q, new_key, new_value, k_cache, v_cache, block_table,
+                                     seq_ptr, context_lens, scale, max_context_len, workspace,
+                                     out, slots_out=None, stream=None):
+    """Fused decode step: store each sequence's newest K/V row (position ctx-1), then decode."""
+    _contig(new_key, new_value, slots_out)
+    assert new_key.dtype == new_value.dtype == q.dtype
+    assert slots_out is None or slots_out.dtype == torch.int64
+    (dt, it, qp, kp, vp_, btp, bt_len, spp, ctxp, B, hq, hkv, d, bs, num_pages, sc, mcl, wsp,
+     ws_bytes, outp) = _decode_args(q, k_cache, v_cache, block_table, seq_ptr, context_lens,
+                                    scale, max_context_len, workspace, out)
+    assert tuple(new_key.shape) == (B, hkv, d) and new_value.shape == new_key.shape
+    _check("hpkv_paged_attention_decode_step", lib.hpkv_paged_attention_decode_step(
+        dt, it, qp, _ptr(new_key), _ptr(new_value), kp, vp_, btp, bt_len, spp, ctxp, B, hq, hkv,
+        d, bs, num_pages, sc, mcl, _ptr(slots_out), wsp, ws_bytes, outp, _stream(stream, q)))
 
 
 def alloc_workspace(q, k_cache, max_context_len):

@@ -118,6 +118,9 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
   a->page_div = hpkv::make_fastdiv(page_size);
   a->scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   a->idx64 = index_type == HPKV_INDEX_U64;
+  a->new_k = nullptr;
+  a->new_v = nullptr;
+  a->slots_out = nullptr;
   *num_workgroups = nwg;
   return 1;  // ready to launch
 }
@@ -322,6 +325,36 @@ int hpkv_paged_attention_decode(int dtype, int index_type, const void* q, const 
                                 num_kv_heads, head_dim, page_size, num_pages, scale,
                                 max_context_len, workspace, workspace_bytes, out, &a, &nwg);
   if (st <= 0) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hpkv::launch_decode_partitions(dtype, head_dim, a, nwg, s);
+  if (e != hipSuccess) return HPKV_ERR_HIP;
+  if (a.max_parts > 1) e = hpkv::launch_decode_reduce(dtype, reduce_args(a, head_dim), s);
+  return hip_status(e);
+}
+
+int hpkv_paged_attention_decode_step(int dtype, int index_type, const void* q,
+                                     const void* new_key, const void* new_value, void* k_cache,
+                                     void* v_cache, const void* block_table,
+                                     uint64_t block_table_len, const void* seq_ptr,
+                                     const int32_t* context_lens, uint32_t num_seqs,
+                                     uint32_t num_q_heads, uint32_t num_kv_heads,
+                                     uint32_t head_dim, uint32_t page_size, uint64_t num_pages,
+                                     float scale, uint32_t max_context_len, int64_t* slots_out,
+                                     void* workspace, size_t workspace_bytes, void* out,
+                                     void* stream) {
+  DecodeKernelArgs a;
+  uint64_t nwg = 0;
+  const int st = prepare_decode(dtype, index_type, q, k_cache, v_cache, block_table,
+                                block_table_len, seq_ptr, context_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, page_size, num_pages, scale,
+                                max_context_len, workspace, workspace_bytes, out, &a, &nwg);
+  if (st <= 0) return st;
+  if (!new_key || !new_value) return HPKV_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(new_key) | reinterpret_cast<uintptr_t>(new_value)) % 16 != 0)
+    return HPKV_ERR_INVALID_ARG;
+  a.new_k = new_key;
+  a.new_v = new_value;
+  a.slots_out = slots_out;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hpkv::launch_decode_partitions(dtype, head_dim, a, nwg, s);
   if (e != hipSuccess) return HPKV_ERR_HIP;

@@ -251,9 +251,12 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
   if (w.part >= w.nparts) return false;
 
   w.out_row0 = uint64_t(w.s) * a.num_q_heads + h0;
+  const bool slot_writer = a.slots_out != nullptr && tid == 0 && h0 == 0;  // once per sequence
   if (length_is_bad(n, a.max_context_len)) {
-    if (w.part == 0)
+    if (w.part == 0) {
       for (uint32_t i = tid; i < NH * D; i += NTH) store_out<DT>(a.out, w.out_row0 * D + i, NAN);
+      if (slot_writer) a.slots_out[w.s] = -1;
+    }
     return false;
   }
 
@@ -277,6 +280,7 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
   }
   bad = __syncthreads_or(bad_page) != 0 || bad;
 
+  const bool last_part = w.part + 1 == w.nparts;
   if (bad) {  // malformed index buffers: NaN result for this partition
     if (w.nparts == 1) {
       for (uint32_t i = tid; i < NH * D; i += NTH)
@@ -288,7 +292,35 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
         if (i % D == 0) a.ws_ml[r] = make_float2(NAN, NAN);
       }
     }
+    if (slot_writer && last_part) a.slots_out[w.s] = -1;
     return false;
+  }
+
+  // Fused decode step ("Paged KV Cache · AI infra interview lesson", Step 1
+  // store at the decode slot p = ctx-1, then Step 2): the workgroup whose
+  // partition ends the context first writes the new token's K and V rows of
+  // head g to that token's pool row (its offset is already in s_row), and the
+  // barrier makes them visible to the workgroup's own loads below.
+  if (a.new_k != nullptr && last_part) {
+    if (w.cnt > 0) {
+      constexpr int EB = Elem<DT>::bytes;
+      constexpr int CH = D * EB / 16;  // 16-byte chunks per head row
+      const uint64_t dst = s_row[w.cnt - 1] * EB;
+      const uint64_t src = (uint64_t(w.s) * a.num_kv_heads + w.g) * D * EB;
+      if (tid < uint32_t(CH)) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.new_k) + src + tid * 16);
+        const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.new_v) + src + tid * 16);
+        *reinterpret_cast<u32x4*>(const_cast<char*>(static_cast<const char*>(a.k_cache)) + dst + tid * 16) = kv;
+        *reinterpret_cast<u32x4*>(const_cast<char*>(static_cast<const char*>(a.v_cache)) + dst + tid * 16) = vv;
+      }
+      if (slot_writer) {
+        const uint64_t row = s_row[w.cnt - 1] / D;  // (slot * Hkv + g)
+        a.slots_out[w.s] = int64_t((row - w.g) / a.num_kv_heads);
+      }
+      __syncthreads();
+    } else if (slot_writer) {
+      a.slots_out[w.s] = -1;  // empty context: nothing appended
+    }
   }
   return true;
 }

@@ -57,6 +57,11 @@ struct DecodeKernelArgs {
   FastDiv page_div;
   float scale_log2;     // scale * log2(e): scores are kept in base-2 units
   int idx64;            // block_table / seq_ptr hold u64 (else u32)
+  // Fused decode step (all null for a plain decode): the row of each
+  // sequence's last context token is written into the pools before it is read.
+  const void* new_k;    // [B, Hkv, d] K rows of the appended tokens
+  const void* new_v;    // [B, Hkv, d] V rows
+  int64_t* slots_out;   // [B] pool slot each row went to (-1: none), may be null
 };
 
 struct ReduceKernelArgs {

@@ -30,7 +30,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared()
-    assert len(declared) == 11
+    assert len(declared) == 12
     out = subprocess.run(["nm", "-D", "--defined-only", hpkv.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(hpkv_\w+)", out))
@@ -129,6 +129,15 @@ def test_decode_argument_errors():
         == hpkv.ERR_WORKSPACE
     # an empty batch is a no-op that succeeds without touching any pointer
     assert _decode_call(B=0, q=None, k=None, v=None, out=None, ctx=None) == hpkv.OK
+    # the fused step needs the new rows, 16-byte aligned
+    step = hpkv.lib.hpkv_paged_attention_decode_step
+    args = [hpkv.BF16, hpkv.INDEX_U32, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 4, 2,
+            128, 16, 8, 0.1, 4096, None, FAKE, 1 << 30, FAKE, None]
+    assert step(*args) == hpkv.ERR_NULL
+    args[3] = ctypes.c_void_p(0x1008)
+    assert step(*args) == hpkv.ERR_INVALID_ARG
+    args[1] = 7
+    assert step(*args) == hpkv.ERR_INVALID_ARG
 
 
 def test_workspace_size_accounting():

@@ -249,3 +249,44 @@ def test_empty_batch_is_a_no_op():
                                      torch.zeros(0, dtype=torch.int32, device=dev), 0.1, 0, None,
                                      out)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("make", [lambda: workloads.llama7b(batch=12),
+                                  lambda: workloads.gqa(batch=40, dtype="f16"),
+                                  lambda: workloads.tiny(bs=16, dtype="f32"),
+                                  lambda: workloads.prefix(groups=2, group_size=4)])
+def test_fused_decode_step_equals_separate_calls(make):
+    """hpkv_paged_attention_decode_step == slot mapping + store + decode, bit for bit."""
+    w = make()
+    w.chunks = workloads._decode_step_chunks(w.context_lens)
+    w.context_lens = w.context_lens.copy()
+    w.context_lens[1] = 0          # an empty sequence: nothing appended, zeros out
+    w.chunks = workloads._decode_step_chunks(w.context_lens)
+    w.drop_mask = None
+    t1 = workloads.make_tensors(w, "cuda")
+    poison_unused(w, t1)
+    t2 = workloads.Tensors(t1.q.clone(), t1.k_cache.clone(), t1.v_cache.clone(),
+                           [x.clone() for x in t1.new_keys], [x.clone() for x in t1.new_values])
+    slots_sep, out_sep = gpu_step(w, t1)
+    dev = t2.q.device
+    # one new row per sequence, rows of empty sequences unused
+    B = w.num_seqs
+    nk = torch.zeros(B, w.num_kv_heads, w.head_dim, dtype=t2.q.dtype, device=dev)
+    nv = torch.zeros_like(nk)
+    has = torch.from_numpy(w.context_lens > 0).to(dev)
+    nk[has] = t2.new_keys[0]
+    nv[has] = t2.new_values[0]
+    out = torch.empty_like(t2.q)
+    slots = torch.full((B,), 7, dtype=torch.int64, device=dev)
+    ws = hpkv.alloc_workspace(t2.q, t2.k_cache, w.max_context_len)
+    hpkv.hpkv_paged_attention_decode_step(
+        t2.q, nk, nv, t2.k_cache, t2.v_cache, torch.from_numpy(w.block_table).to(dev),
+        torch.from_numpy(w.seq_ptr).to(dev), torch.from_numpy(w.context_lens).to(dev), w.scale,
+        w.max_context_len, ws, out, slots_out=slots)
+    torch.cuda.synchronize()
+    assert host_bits(out).tobytes() == host_bits(out_sep).tobytes()
+    assert host_bits(t2.k_cache).tobytes() == host_bits(t1.k_cache).tobytes()
+    assert host_bits(t2.v_cache).tobytes() == host_bits(t1.v_cache).tobytes()
+    want = np.full(B, -1, dtype=np.int64)
+    want[w.context_lens > 0] = slots_sep[0]
+    np.testing.assert_array_equal(slots.cpu().numpy(), want)
