@@ -61,6 +61,9 @@ def _load():
     lib.orc_paged_attention_decode.restype = i32
     lib.orc_dense_attention.argtypes = [i32, vp, vp, vp, u64, u64, u64, u64, ctypes.c_double, vp]
     lib.orc_dense_attention.restype = i32
+    lib.orc_paged_attention_prefill.argtypes = [i32, i32, vp, vp, vp, vp, u64, vp, vp, vp, u64,
+                                                u64, u64, u64, u64, u64, ctypes.c_double, vp, vp]
+    lib.orc_paged_attention_prefill.restype = i32
     lib.orc_round_to_dtype.argtypes = [i32, vp, u64, vp]
     lib.orc_round_to_dtype.restype = None
     lib.orc_widen_dtype.argtypes = [i32, vp, u64, vp]
@@ -171,6 +174,31 @@ def paged_attention_decode(dtype, q, k_cache, v_cache, block_table, seq_ptr, con
                                             int(num_threads))
     if st != OK:
         raise ValueError(f"paged_attention_decode: oracle status {st}")
+    return out, out64
+
+
+def paged_attention_prefill(dtype, q, k_cache, v_cache, block_table, seq_ptr, q_start, cu_q,
+                            scale):
+    """Causal chunked-prefill attention: (out in storage dtype, out as float64), q [Nq, Hq, d]."""
+    q = _storage(q, dtype)
+    k_cache = _storage(k_cache, dtype)
+    v_cache = _storage(v_cache, dtype)
+    seq_ptr = np.ascontiguousarray(seq_ptr)
+    block_table = np.ascontiguousarray(block_table, dtype=seq_ptr.dtype)
+    q_start = np.ascontiguousarray(q_start, dtype=np.int32)
+    cu_q = np.ascontiguousarray(cu_q, dtype=np.int64)
+    Nq, Hq, d = q.shape
+    num_pages, bs, Hkv, _ = k_cache.shape
+    assert int(cu_q[-1]) == Nq and len(cu_q) == len(seq_ptr)
+    out = np.empty_like(q)
+    out64 = np.empty((Nq, Hq, d), dtype=np.float64)
+    st = _load().orc_paged_attention_prefill(_DTYPE_CODE[dtype], _index_bytes(seq_ptr), _ptr(q),
+                                             _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                             len(block_table), _ptr(seq_ptr), _ptr(q_start),
+                                             _ptr(cu_q), len(seq_ptr) - 1, Hq, Hkv, d, bs,
+                                             num_pages, float(scale), _ptr(out), _ptr(out64))
+    if st != OK:
+        raise ValueError(f"paged_attention_prefill: oracle status {st}")
     return out, out64
 
 

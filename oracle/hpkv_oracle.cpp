@@ -31,6 +31,10 @@
 //     repeated slots resolve last-writer-wins in token order.
 //   * GQA: query head h reads KV head h / (Hq/Hkv) ([INT] Step 2).
 //   * scale multiplies the q.k dot product ([INT] Step 2).
+//   * Chunked prefill: the query at position p of a chunk attends to tokens
+//     0..p of its own sequence (causal softmax attention), all read from the
+//     pool, so the chunk's own K/V rows are stored before attention ([INT]
+//     Step 1 chunked prefill / prefix hit, then the gather of Step 2).
 
 #include <algorithm>
 #include <cmath>
@@ -454,6 +458,73 @@ int orc_dense_attention(int dtype, const void* q, const void* K, const void* V, 
       for (uint64_t t = 0; t < L; ++t)
         acc += weights[t] * load_elem(dtype, V, (t * num_kv_heads + g) * head_dim + e);
       out[h * head_dim + e] = L == 0 ? 0.0 : acc / total;
+    }
+  }
+  return ORC_OK;
+}
+
+// Chunked prefill over the paged cache. [INT] "Step 1" describes a prefill
+// chunk that may start part-way into a page (a prefix hit, or the second half
+// of a chunked prefill); its queries attend causally: the query at position p
+// of sequence s sees that sequence's tokens 0..p, read through the block
+// table ([INT] "Step 2" gather, [LLM] "What the KV cache actually stores").
+// Query rows of sequence s are cu_q[s] .. cu_q[s+1]-1 at positions
+// q_start[s] + (i - cu_q[s]). q and out are [Nq, Hq, d]. Each query row is the
+// single-query attention of "Step 2" over its first p+1 tokens, computed in
+// double and rounded once. Returns ORC_CTX_RANGE if a position is negative or
+// beyond the sequence's slice.
+int orc_paged_attention_prefill(int dtype, int index_bytes, const void* q, const void* k_cache,
+                                const void* v_cache, const void* block_table,
+                                uint64_t block_table_len, const void* seq_ptr,
+                                const int32_t* q_start, const int64_t* cu_q, uint64_t num_seqs,
+                                uint64_t num_q_heads, uint64_t num_kv_heads, uint64_t head_dim,
+                                uint64_t page_size, uint64_t num_pages, double scale, void* out,
+                                double* out_f64) {
+  if (dtype != ORC_F32 && dtype != ORC_F16 && dtype != ORC_BF16) return ORC_BAD_ARG;
+  if (index_bytes != 4 && index_bytes != 8) return ORC_BAD_ARG;
+  if (num_kv_heads == 0 || head_dim == 0 || page_size == 0) return ORC_BAD_ARG;
+  if (num_q_heads % num_kv_heads != 0) return ORC_BAD_ARG;
+  const uint64_t Hq = num_q_heads, Hkv = num_kv_heads, d = head_dim, group = Hq / Hkv;
+  std::vector<double> z, o(d);
+  for (uint64_t s = 0; s < num_seqs; ++s) {
+    const uint64_t first = read_index(index_bytes, seq_ptr, s);
+    const uint64_t last = read_index(index_bytes, seq_ptr, s + 1);
+    for (int64_t i = cu_q[s]; i < cu_q[s + 1]; ++i) {
+      const int64_t p = int64_t(q_start[s]) + (i - cu_q[s]);
+      if (p < 0 || last < first || uint64_t(p) + 1 > (last - first) * page_size) return ORC_CTX_RANGE;
+      const uint64_t n = uint64_t(p) + 1;
+      std::vector<uint64_t> rows(n);
+      for (uint64_t t = 0; t < n; ++t) {
+        const int st = token_row(index_bytes, s, t, page_size, num_pages, Hkv, d, block_table,
+                                 block_table_len, seq_ptr, num_seqs, &rows[t]);
+        if (st != ORC_OK) return st;
+      }
+      z.assign(n, 0.0);
+      for (uint64_t h = 0; h < Hq; ++h) {
+        const uint64_t g = h / group;
+        const uint64_t q_base = (uint64_t(i) * Hq + h) * d;
+        double zmax = -INFINITY;
+        for (uint64_t t = 0; t < n; ++t) {
+          double dot = 0.0;
+          for (uint64_t e = 0; e < d; ++e)
+            dot += load_elem(dtype, q, q_base + e) *
+                   load_elem(dtype, k_cache, (rows[t] * Hkv + g) * d + e);
+          z[t] = dot * scale;
+          zmax = std::max(zmax, z[t]);
+        }
+        double denom = 0.0;
+        std::fill(o.begin(), o.end(), 0.0);
+        for (uint64_t t = 0; t < n; ++t) {
+          const double wgt = std::exp(z[t] - zmax);
+          denom += wgt;
+          for (uint64_t e = 0; e < d; ++e)
+            o[e] += wgt * load_elem(dtype, v_cache, (rows[t] * Hkv + g) * d + e);
+        }
+        for (uint64_t e = 0; e < d; ++e) {
+          if (out) store_elem(dtype, out, q_base + e, o[e] / denom);
+          if (out_f64) out_f64[q_base + e] = o[e] / denom;
+        }
+      }
     }
   }
   return ORC_OK;
