@@ -269,6 +269,51 @@ int hpkv_paged_attention_decode_step(int dtype, int index_type, const void* q,
                                      void* workspace, size_t workspace_bytes, void* out,
                                      void* stream);
 
+/* ---------------------------------------------------------------------------
+ * hpkv_paged_attention_prefill  (device)
+ *
+ * Causal attention of a prefill chunk over the paged cache. A chunk may start
+ * part-way into a page, after a prefix hit or an earlier chunk ("Paged KV
+ * Cache · AI infra interview lesson", section "Step 1: slot_mapping and
+ * store_kvcache"); its queries read K/V through the block table as in
+ * section "Step 2: paged_attention_decode", including pages aliased across
+ * sequences ("Block-Paged KV Cache", section "Element lookup through the
+ * block table"). Sequence s owns query rows i = cu_q[s] .. cu_q[s+1]-1 at
+ * positions p = q_start[s] + (i - cu_q[s]); for query head h and KV head
+ * g = h / (num_q_heads / num_kv_heads)
+ *   out[i,h,:] = sum_{t <= p} softmax_t(scale * q[i,h,:] . K[t,g,:]) V[t,g,:].
+ * The chunk's own K/V rows must already be in the pools (hpkv_slot_mapping +
+ * hpkv_store_kvcache first).
+ *   q, out        device [num_q_tokens, num_q_heads, head_dim] of dtype,
+ *                 16-byte aligned; out is written for every query row of
+ *                 every sequence (caller-owned, not aliasing q or the pools)
+ *   k_cache, v_cache, block_table, seq_ptr, page_size, num_pages: as for
+ *                 hpkv_paged_attention_decode (read only)
+ *   q_start       device int32 [num_seqs]
+ *   cu_q          device int64 [num_seqs + 1], non-decreasing, cu_q[0] = 0,
+ *                 cu_q[num_seqs] = num_q_tokens
+ *   max_q_len     >= every chunk length cu_q[s+1] - cu_q[s] (sizes the grid);
+ *                 must be >= 1 when num_q_tokens > 0
+ *   stream        hipStream_t or NULL; the call only enqueues (asynchronous)
+ * Supported: dtype bf16 or f16, head_dim in {32, 64, 128, 256}, and
+ * num_q_heads / num_kv_heads at most 256 (128 at head_dim 256); otherwise
+ * HPKV_ERR_UNSUPPORTED. Argument errors (NULL pointers, zero sizes, heads not
+ * divisible, NaN scale, misaligned buffers) return before any GPU work.
+ * Malformed contents (caller error): a sequence whose chunk is longer than
+ * max_q_len, has negative q_start or bad cu_q entries, or runs past its slice
+ * gets NaN in all its rows; rows whose keys include a page id >= num_pages
+ * get NaN. Nothing is read or written out of bounds.
+ * One kernel is enqueued; no workspace is needed.
+ * ------------------------------------------------------------------------- */
+int hpkv_paged_attention_prefill(int dtype, int index_type, const void* q, const void* k_cache,
+                                 const void* v_cache, const void* block_table,
+                                 uint64_t block_table_len, const void* seq_ptr,
+                                 const int32_t* q_start, const int64_t* cu_q, uint32_t num_seqs,
+                                 uint64_t num_q_tokens, uint32_t num_q_heads,
+                                 uint32_t num_kv_heads, uint32_t head_dim, uint32_t page_size,
+                                 uint64_t num_pages, float scale, uint32_t max_q_len, void* out,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

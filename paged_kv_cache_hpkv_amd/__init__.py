@@ -38,6 +38,7 @@ EXPORTED = [
     "hpkv_paged_attention_decode_workspace_size", "hpkv_paged_attention_decode_partition_tokens",
     "hpkv_paged_attention_decode", "hpkv_paged_attention_decode_partitions",
     "hpkv_paged_attention_decode_reduce", "hpkv_paged_attention_decode_step",
+    "hpkv_paged_attention_prefill",
 ]
 
 
@@ -75,6 +76,8 @@ def _load():
         "hpkv_paged_attention_decode_step": ([i32, i32, vp, vp, vp, vp, vp, vp, u64, vp, vp, u32,
                                               u32, u32, u32, u32, u64, f32, u32, vp, vp, sz, vp,
                                               vp], i32),
+        "hpkv_paged_attention_prefill": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, vp, u32, u64,
+                                          u32, u32, u32, u32, u64, f32, u32, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -253,6 +256,25 @@ def hpkv_paged_attention_decode_step(q, new_key, new_value, k_cache, v_cache, bl
     _check("hpkv_paged_attention_decode_step", lib.hpkv_paged_attention_decode_step(
         dt, it, qp, _ptr(new_key), _ptr(new_value), kp, vp_, btp, bt_len, spp, ctxp, B, hq, hkv,
         d, bs, num_pages, sc, mcl, _ptr(slots_out), wsp, ws_bytes, outp, _stream(stream, q)))
+
+
+def hpkv_paged_attention_prefill(q, k_cache, v_cache, block_table, seq_ptr, q_start, cu_q, scale,
+                                 max_q_len, out, stream=None):
+    """Causal chunked-prefill attention: q/out [num_q_tokens, Hq, d]; sequence s owns rows
+    cu_q[s] .. cu_q[s+1]-1 at positions q_start[s] + (i - cu_q[s])."""
+    _contig(q, k_cache, v_cache, block_table, seq_ptr, q_start, cu_q, out)
+    assert q.dtype == k_cache.dtype == v_cache.dtype == out.dtype
+    assert q_start.dtype == torch.int32 and cu_q.dtype == torch.int64
+    assert block_table.element_size() == seq_ptr.element_size()
+    assert out.shape == q.shape
+    nq, hq, d = q.shape
+    num_pages, bs, hkv, d2 = k_cache.shape
+    B = q_start.numel()
+    assert cu_q.numel() == B + 1 and seq_ptr.numel() == B + 1
+    _check("hpkv_paged_attention_prefill", lib.hpkv_paged_attention_prefill(
+        _DTYPE_CODE[q.dtype], _index_type(seq_ptr), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_table), block_table.numel(), _ptr(seq_ptr), _ptr(q_start), _ptr(cu_q), B, nq,
+        hq, hkv, d, bs, num_pages, float(scale), int(max_q_len), _ptr(out), _stream(stream, q)))
 
 
 def alloc_workspace(q, k_cache, max_context_len):

@@ -362,4 +362,66 @@ int hpkv_paged_attention_decode_step(int dtype, int index_type, const void* q,
   return hip_status(e);
 }
 
+int hpkv_paged_attention_prefill(int dtype, int index_type, const void* q, const void* k_cache,
+                                 const void* v_cache, const void* block_table,
+                                 uint64_t block_table_len, const void* seq_ptr,
+                                 const int32_t* q_start, const int64_t* cu_q, uint32_t num_seqs,
+                                 uint64_t num_q_tokens, uint32_t num_q_heads,
+                                 uint32_t num_kv_heads, uint32_t head_dim, uint32_t page_size,
+                                 uint64_t num_pages, float scale, uint32_t max_q_len, void* out,
+                                 void* stream) {
+  if (!valid_dtype(dtype) || !valid_index(index_type)) return HPKV_ERR_INVALID_ARG;
+  if (num_seqs == 0 || num_q_tokens == 0) return HPKV_OK;
+  if (!q || !k_cache || !v_cache || !seq_ptr || !q_start || !cu_q || !out) return HPKV_ERR_NULL;
+  if (block_table_len > 0 && !block_table) return HPKV_ERR_NULL;
+  if (num_q_heads == 0 || num_kv_heads == 0 || head_dim == 0 || page_size == 0 ||
+      num_pages == 0 || max_q_len == 0)
+    return HPKV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return HPKV_ERR_INVALID_ARG;
+  if (page_size > 0x7fffffffu || max_q_len > 0x7fffffffu) return HPKV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return HPKV_ERR_INVALID_ARG;  // NaN scale
+  if (!hpkv::prefill_head_dim_supported(dtype, head_dim)) return HPKV_ERR_UNSUPPORTED;
+  const uint32_t group = num_q_heads / num_kv_heads;
+  const uint32_t rows = hpkv::prefill_rows_per_workgroup(dtype, head_dim);
+  if (group > rows) return HPKV_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out)) % 16 != 0)
+    return HPKV_ERR_INVALID_ARG;
+
+  // no chunk can hold more rows than the call has
+  const uint64_t qmax = max_q_len < num_q_tokens ? max_q_len : num_q_tokens;
+  const uint32_t block_positions = rows / group;
+  const uint64_t pos_blocks = (qmax + block_positions - 1) / block_positions;
+  const uint64_t work = pos_blocks * num_kv_heads * num_seqs;
+  const uint64_t nwg = (work + 7) / 8 * 8;  // a multiple of the 8 XCDs
+  if (nwg > 0x7fffffffull) return HPKV_ERR_UNSUPPORTED;
+
+  hpkv::PrefillKernelArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.out = out;
+  a.block_table = block_table;
+  a.seq_ptr = seq_ptr;
+  a.q_start = q_start;
+  a.cu_q = cu_q;
+  a.block_table_len = block_table_len;
+  a.num_pages = num_pages;
+  a.num_q_tokens = num_q_tokens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.page_size = page_size;
+  a.group = group;
+  a.block_positions = block_positions;
+  a.pos_blocks = uint32_t(pos_blocks);
+  a.max_q_len = max_q_len;
+  a.num_work = uint32_t(work);
+  a.page_div = hpkv::make_fastdiv(page_size);
+  a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  a.idx64 = index_type == HPKV_INDEX_U64;
+  return hip_status(hpkv::launch_prefill(dtype, head_dim, a, uint32_t(nwg),
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

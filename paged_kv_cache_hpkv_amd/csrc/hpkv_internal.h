@@ -77,6 +77,39 @@ struct ReduceKernelArgs {
   uint32_t max_context_len;
 };
 
+struct PrefillKernelArgs {
+  const void* q;             // [num_q_tokens, Hq, d]
+  const void* k_cache;
+  const void* v_cache;
+  void* out;                 // [num_q_tokens, Hq, d]
+  const void* block_table;
+  const void* seq_ptr;
+  const int32_t* q_start;    // [B] position of each chunk's first query
+  const int64_t* cu_q;       // [B+1] query rows of sequence s: cu_q[s] .. cu_q[s+1]-1
+  uint64_t block_table_len;
+  uint64_t num_pages;
+  uint64_t num_q_tokens;
+  uint32_t num_seqs;
+  uint32_t num_q_heads;
+  uint32_t num_kv_heads;
+  uint32_t page_size;
+  uint32_t group;            // num_q_heads / num_kv_heads
+  uint32_t block_positions;  // chunk positions one workgroup covers
+  uint32_t pos_blocks;       // workgroups per (sequence, KV head)
+  uint32_t max_q_len;
+  uint32_t num_work;         // num_seqs * num_kv_heads * pos_blocks
+  FastDiv page_div;
+  float scale_log2;
+  int idx64;
+};
+
+// Rows (query position x query head pairs) one prefill workgroup covers.
+uint32_t prefill_rows_per_workgroup(int dtype, uint32_t head_dim);
+bool prefill_head_dim_supported(int dtype, uint32_t head_dim);
+
+hipError_t launch_prefill(int dtype, uint32_t head_dim, const PrefillKernelArgs& a,
+                          uint32_t num_workgroups, hipStream_t stream);
+
 // Query heads served by one decode workgroup for a GQA group of `group` heads
 // (the matrix-core path takes up to 16 heads of a group at once).
 uint32_t heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group);

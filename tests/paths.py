@@ -124,3 +124,83 @@ def check_step(w: workloads.Workload, device="cuda", seed_poison=True, verbose=T
     assert worst_ratio <= 1.0, f"decode error {max_err} above tolerance"
     return dict(max_err=max_err, worst_ratio=worst_ratio, out=g_out, oracle_out=o_out,
                 oracle_out64=o_out64, tensors=t)
+
+
+# ------------------------------------------------------------ chunked prefill
+
+def max_chunk_len(cu) -> int:
+    cu = np.asarray(cu, dtype=np.int64)
+    return int(np.diff(cu).max()) if len(cu) > 1 else 0
+
+
+def gpu_prefill(w: workloads.Workload, t: workloads.Tensors, queries, max_q_len=None):
+    """Per chunk through libhpkv: slot mapping + store of the chunk's K/V rows, then
+    causal prefill attention of the chunk's queries. Returns the outputs per chunk."""
+    dev = t.k_cache.device
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sp = torch.from_numpy(w.seq_ptr).to(dev)
+    outs = []
+    for c, (start, cu) in enumerate(w.chunks):
+        start_t = torch.from_numpy(start).to(dev)
+        cu_t = torch.from_numpy(cu).to(dev)
+        slots = torch.empty(int(cu[-1]), dtype=torch.int64, device=dev)
+        hpkv.hpkv_slot_mapping(bt, sp, w.page_size, start_t, cu_t, slots)
+        hpkv.hpkv_store_kvcache(t.new_keys[c], t.new_values[c], t.k_cache, t.v_cache, slots)
+        out = torch.empty_like(queries[c])
+        mq = max_chunk_len(cu) if max_q_len is None else max_q_len
+        hpkv.hpkv_paged_attention_prefill(queries[c], t.k_cache, t.v_cache, bt, sp, start_t, cu_t,
+                                          w.scale, max(mq, 1), out)
+        outs.append(out)
+    torch.cuda.synchronize(dev)
+    return outs
+
+
+def oracle_prefill_rows(w: workloads.Workload, h: dict, q_bits, start, cu, rows):
+    """Oracle prefill outputs (float64 [len(rows), Hq, d]) of the given query rows of a chunk,
+    computed one sequence position at a time (pools in `h` already hold the chunk)."""
+    start = np.asarray(start, dtype=np.int32)
+    cu = np.asarray(cu, dtype=np.int64)
+    B = len(start)
+    seq_of = np.searchsorted(cu, rows, side="right") - 1
+    out = np.empty((len(rows), w.num_q_heads, w.head_dim), dtype=np.float64)
+    pending = list(range(len(rows)))
+    while pending:  # one oracle call per round, each sequence at most once per round
+        taken, rest = {}, []
+        for k in pending:
+            if seq_of[k] in taken:
+                rest.append(k)
+            else:
+                taken[seq_of[k]] = k
+        order = sorted(taken.items())
+        q_start = np.zeros(B, dtype=np.int32)
+        counts = np.zeros(B, dtype=np.int64)
+        for s, k in order:
+            q_start[s] = start[s] + (rows[k] - cu[s])
+            counts[s] = 1
+        cu_s = np.zeros(B + 1, dtype=np.int64)
+        cu_s[1:] = np.cumsum(counts)
+        q_sel = np.ascontiguousarray(q_bits[[rows[k] for _, k in order]])
+        _, o64 = oracle.paged_attention_prefill(w.dtype, q_sel, h["k_cache"], h["v_cache"],
+                                                w.block_table, w.seq_ptr, q_start, cu_s, w.scale)
+        for j, (_, k) in enumerate(order):
+            out[k] = o64[j]
+        pending = rest
+    return out
+
+
+def oracle_prefill(w: workloads.Workload, h: dict, q_bits_list, sample_rows=None):
+    """The prefill step on the oracle, in place on the host pools of `h`: per chunk, slot
+    mapping + store, then prefill of all its rows (or of sample_rows[c])."""
+    outs = []
+    for c, (start, cu) in enumerate(w.chunks):
+        slots = oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, start, cu)
+        oracle.store_kvcache(h["new_keys"][c], h["new_values"][c], h["k_cache"], h["v_cache"],
+                             slots)
+        if sample_rows is None:
+            _, o64 = oracle.paged_attention_prefill(w.dtype, q_bits_list[c], h["k_cache"],
+                                                    h["v_cache"], w.block_table, w.seq_ptr,
+                                                    start, cu, w.scale)
+        else:
+            o64 = oracle_prefill_rows(w, h, q_bits_list[c], start, cu, sample_rows[c])
+        outs.append(o64)
+    return outs

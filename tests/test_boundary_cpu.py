@@ -30,7 +30,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared()
-    assert len(declared) == 12
+    assert len(declared) == 13
     out = subprocess.run(["nm", "-D", "--defined-only", hpkv.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(hpkv_\w+)", out))
@@ -138,6 +138,38 @@ def test_decode_argument_errors():
     assert step(*args) == hpkv.ERR_INVALID_ARG
     args[1] = 7
     assert step(*args) == hpkv.ERR_INVALID_ARG
+
+
+def _prefill_call(**over):
+    args = dict(dtype=hpkv.BF16, index=hpkv.INDEX_U32, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, bt_len=4,
+                sp=FAKE, q_start=FAKE, cu_q=FAKE, B=2, nq=10, hq=8, hkv=2, d=128, bs=16,
+                num_pages=8, scale=0.1, max_q=6, out=FAKE, stream=None)
+    args.update(over)
+    return hpkv.lib.hpkv_paged_attention_prefill(*args.values())
+
+
+def test_prefill_argument_errors():
+    assert _prefill_call(dtype=7) == hpkv.ERR_INVALID_ARG
+    assert _prefill_call(index=3) == hpkv.ERR_INVALID_ARG
+    for name in ("q", "k", "v", "sp", "q_start", "cu_q", "out"):
+        assert _prefill_call(**{name: None}) == hpkv.ERR_NULL, name
+    assert _prefill_call(bt=None) == hpkv.ERR_NULL
+    assert _prefill_call(hq=6, hkv=4) == hpkv.ERR_INVALID_ARG
+    assert _prefill_call(hkv=0) == hpkv.ERR_INVALID_ARG
+    assert _prefill_call(bs=0) == hpkv.ERR_INVALID_ARG
+    assert _prefill_call(num_pages=0) == hpkv.ERR_INVALID_ARG
+    assert _prefill_call(max_q=0) == hpkv.ERR_INVALID_ARG
+    assert _prefill_call(scale=float("nan")) == hpkv.ERR_INVALID_ARG
+    assert _prefill_call(out=ctypes.c_void_p(0x1008)) == hpkv.ERR_INVALID_ARG
+    assert _prefill_call(k=ctypes.c_void_p(0x1004)) == hpkv.ERR_INVALID_ARG
+    assert _prefill_call(d=96) == hpkv.ERR_UNSUPPORTED
+    assert _prefill_call(d=16) == hpkv.ERR_UNSUPPORTED
+    assert _prefill_call(dtype=hpkv.F32) == hpkv.ERR_UNSUPPORTED
+    assert _prefill_call(hq=512, hkv=1) == hpkv.ERR_UNSUPPORTED    # group wider than a workgroup
+    assert _prefill_call(hq=256, hkv=1, d=256) == hpkv.ERR_UNSUPPORTED
+    # nothing to do: no sequences or no query rows
+    assert _prefill_call(B=0, q=None, k=None, v=None, out=None) == hpkv.OK
+    assert _prefill_call(nq=0, q=None, k=None, v=None, out=None, max_q=0) == hpkv.OK
 
 
 def test_workspace_size_accounting():

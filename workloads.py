@@ -187,15 +187,22 @@ def qwen3(dtype: str = "bf16", index: str = "u32", seed: int = 4, batch: int = 1
                     128 ** -0.5, chunks=chunks, drop_mask=drop, seed=seed)
 
 
-def prefix(dtype: str = "bf16", index: str = "u64", seed: int = 5, groups: int = 32,
-           group_size: int = 16, prefix_tokens: int = 2048, n_chunks: int = 3) -> Workload:
+def chunked_prefill(name: str = "prefix", dtype: str = "bf16", index: str = "u64", seed: int = 5,
+                    groups: int = 32, group_size: int = 16, prefix_tokens: int = 2048,
+                    n_chunks: int = 3, num_q_heads: int = 32, num_kv_heads: int = 8,
+                    head_dim: int = 128, bs: int = 16, tail_lo: int = 64,
+                    tail_hi: int = 1024) -> Workload:
+    """Groups of sequences aliasing a common prefix of prefix_tokens (whole pages,
+    the same page ids in every table of the group), each followed by a private
+    tail of U{tail_lo..tail_hi} tokens written in n_chunks chunks cut at seeded
+    points (some chunk starts mid-page)."""
+    assert prefix_tokens % bs == 0, "an aliased prefix covers whole pages"
     rng = np.random.default_rng(seed)
-    bs = 16
     B = groups * group_size
-    tails = rng.integers(64, 1024, size=B, endpoint=True)
+    tails = rng.integers(tail_lo, tail_hi, size=B, endpoint=True)
     prefix_pages = _pages_needed(prefix_tokens, bs)
     need = groups * prefix_pages + int(sum(_pages_needed(t, bs) for t in tails))
-    num_pages = int(np.ceil(need * 1.10))
+    num_pages = max(1, int(np.ceil(need * 1.10)))
     perm = rng.permutation(num_pages).tolist()
     tables = []
     k = 0
@@ -214,7 +221,7 @@ def prefix(dtype: str = "bf16", index: str = "u64", seed: int = 5, groups: int =
     for s in range(B):
         inner = np.sort(rng.choice(np.arange(1, tails[s]), size=n_chunks - 1, replace=False))
         cuts[s] = np.concatenate([[0], inner, [tails[s]]]) + prefix_tokens
-    if np.all(cuts[:, 1:-1] % bs == 0):  # make sure some chunk starts mid-page
+    if n_chunks > 1 and np.all(cuts[:, 1:-1] % bs == 0):  # make sure some chunk starts mid-page
         cuts[0, 1] += 1
     chunks = []
     for c in range(n_chunks):
@@ -223,8 +230,14 @@ def prefix(dtype: str = "bf16", index: str = "u64", seed: int = 5, groups: int =
         cu = np.zeros(B + 1, dtype=np.int64)
         cu[1:] = np.cumsum(n)
         chunks.append((start, cu))
-    return Workload("prefix", dtype, index, 32, 8, 128, bs, num_pages, ctx, seq_ptr, bt,
-                    128 ** -0.5, chunks=chunks, seed=seed)
+    return Workload(name, dtype, index, num_q_heads, num_kv_heads, head_dim, bs, num_pages, ctx,
+                    seq_ptr, bt, head_dim ** -0.5, chunks=chunks, seed=seed)
+
+
+def prefix(dtype: str = "bf16", index: str = "u64", seed: int = 5, groups: int = 32,
+           group_size: int = 16, prefix_tokens: int = 2048, n_chunks: int = 3) -> Workload:
+    return chunked_prefill("prefix", dtype, index, seed, groups, group_size, prefix_tokens,
+                           n_chunks)
 
 
 WORKLOADS = {"tiny": tiny, "llama7b": llama7b, "gqa": gqa, "qwen3": qwen3, "prefix": prefix}
@@ -259,3 +272,10 @@ def make_tensors(w: Workload, device="cpu") -> Tensors:
         nk.append(_randn((n, w.num_kv_heads, w.head_dim), dt, device, base + 10 + 2 * c))
         nv.append(_randn((n, w.num_kv_heads, w.head_dim), dt, device, base + 11 + 2 * c))
     return Tensors(q, k_cache, v_cache, nk, nv)
+
+
+def make_prefill_queries(w: Workload, device="cpu") -> List[torch.Tensor]:
+    """N(0,1) queries of every chunk: [N_c, Hq, d] per chunk."""
+    base = 1000 * w.seed
+    return [_randn((int(cu[-1]), w.num_q_heads, w.head_dim), w.torch_dtype, device,
+                   base + 50 + c) for c, (_, cu) in enumerate(w.chunks)]
