@@ -21,6 +21,14 @@ Printed: ONE JSON line with
                step on host copies of the same inputs, timed on the host.
 Inputs are resident in HBM before timing starts; nothing is skipped inside the
 timed region.
+
+--path prefill times causal chunked-prefill attention instead (default
+workload: the prefix-sharing batch, 512 sequences whose tails are written in
+three chunks): a step is, per chunk, slot mapping + store of the chunk's K/V
+rows + hpkv_paged_attention_prefill of its queries. value is the causal
+attention flops of the step (4 * d * Hq * (p + 1) per query position p) over
+the step time in TFLOP/s; roofline is the prefill kernel alone against the
+dense 16-bit matrix-core peak; cpu_baseline runs the oracle on sampled rows.
 """
 import argparse
 import hashlib
@@ -38,6 +46,8 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA16_PEAK_TFLOPS = 2500.0  # dense bf16 / f16 matrix-core peak
+PREFILL_METRIC = "paged chunked-prefill attention: achieved TFLOP/s (causal flops)"
 METRIC = "paged decode: achieved KV HBM GB/s (% of peak) + sequences/s per layer"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_hpkv_amd", "csrc", "hpkv_decode.hip")
@@ -59,7 +69,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="llama7b", choices=sorted(workloads.WORKLOADS))
+    p.add_argument("--path", default="decode", choices=["decode", "prefill"])
+    p.add_argument("--workload", default=None, choices=sorted(workloads.WORKLOADS))
     p.add_argument("--dtype", default=None, choices=["bf16", "f16", "f32"])
     p.add_argument("--index", default=None, choices=["u32", "u64"])
     p.add_argument("--roofline-launches", type=int, default=50)
@@ -72,7 +83,8 @@ def parse():
 
 
 def make_workload(args):
-    w = workloads.WORKLOADS[args.workload]()
+    name = args.workload or ("prefix" if args.path == "prefill" else "llama7b")
+    w = workloads.WORKLOADS[name]()
     if args.dtype:
         w = w.with_dtype(args.dtype)
     if args.index:
@@ -183,6 +195,151 @@ def cpu_baseline(w, t, out_gpu):
                                             and finite)
 
 
+def prefill_flops(w, chunk):
+    """Causal attention flops of one chunk: 4 * d * Hq * (p + 1) summed over its positions."""
+    start, cu = chunk
+    n = np.diff(cu).astype(np.int64)
+    st = start.astype(np.int64)
+    keys = n * st + n * (n + 1) // 2  # sum over p in [start, start+n) of (p + 1)
+    return 4 * w.head_dim * w.num_q_heads * int(keys.sum())
+
+
+class PrefillStep:
+    """Per chunk: slot mapping + store of its K/V rows, then causal prefill attention."""
+
+    def __init__(self, w, t, queries):
+        import paged_kv_cache_hpkv_amd as hpkv
+        self.hpkv, self.w, self.t, self.q = hpkv, w, t, queries
+        dev = t.k_cache.device
+        self.bt = torch.from_numpy(w.block_table).to(dev)
+        self.sp = torch.from_numpy(w.seq_ptr).to(dev)
+        self.chunks = [(torch.from_numpy(s).to(dev), torch.from_numpy(c).to(dev),
+                        torch.empty(int(c[-1]), dtype=torch.int64, device=dev),
+                        max(1, int(np.diff(c).max())))
+                       for s, c in w.chunks]
+        self.out = [torch.empty_like(q) for q in queries]
+
+    def attention(self, c):
+        w, t = self.w, self.t
+        start, cu, _, mq = self.chunks[c]
+        self.hpkv.hpkv_paged_attention_prefill(self.q[c], t.k_cache, t.v_cache, self.bt, self.sp,
+                                               start, cu, w.scale, mq, self.out[c])
+
+    def __call__(self):
+        h, w, t = self.hpkv, self.w, self.t
+        for c, (start, cu, slots, _) in enumerate(self.chunks):
+            h.hpkv_slot_mapping(self.bt, self.sp, w.page_size, start, cu, slots)
+            h.hpkv_store_kvcache(t.new_keys[c], t.new_values[c], t.k_cache, t.v_cache, slots)
+            self.attention(c)
+
+
+def prefill_cpu_baseline(w, t, step, rows_per_chunk=8):
+    """The oracle's prefill on sampled query rows of every chunk, on host copies of the
+    pools after the step (a row at position p only reads keys 0..p, which hold the same
+    bits at any point after their chunk was stored)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from paths import decode_errors, host_bits, oracle_prefill_rows  # noqa: E402
+    h = dict(k_cache=host_bits(t.k_cache), v_cache=host_bits(t.v_cache))
+    rng = np.random.default_rng(0)
+    flops, secs, worst, ok = 0, 0.0, 0.0, True
+    for c, (start, cu) in enumerate(w.chunks):
+        rows = np.sort(rng.choice(int(cu[-1]), rows_per_chunk, replace=False))
+        q_bits = host_bits(step.q[c])
+        seq_of = np.searchsorted(cu, rows, side="right") - 1
+        pos = start[seq_of].astype(np.int64) + rows - cu[seq_of]
+        t0 = time.perf_counter()
+        ref = oracle_prefill_rows(w, h, q_bits, start, cu, rows)
+        secs += time.perf_counter() - t0
+        flops += 4 * w.head_dim * w.num_q_heads * int((pos + 1).sum())
+        err, ratio, finite = decode_errors(w.dtype, host_bits(step.out[c])[rows], ref)
+        worst = max(worst, err)
+        ok = ok and finite and ratio <= 1.0
+    return dict(value=round(flops / secs / 1e12, 6), unit="TFLOP/s", cores=1, kind="oracle",
+                sample=f"{rows_per_chunk} random query rows (all heads) of each of the "
+                       f"{len(w.chunks)} chunks, double precision, 1 host thread, "
+                       f"{secs:.2f} s"), \
+        dict(max_abs_err=worst, within_tolerance=ok)
+
+
+def main_prefill(args, dev):
+    w = make_workload(args)
+    t = workloads.make_tensors(w, dev)
+    queries = workloads.make_prefill_queries(w, dev)
+    step = PrefillStep(w, t, queries)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # the prefill kernel alone: per-launch HIP events on the launch stream
+    nl = max(1, args.roofline_launches // len(w.chunks))
+    durs = [[] for _ in w.chunks]
+    for _ in range(nl):
+        for c in range(len(w.chunks)):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step.attention(c)
+            b.record(stream)
+            durs[c].append((a, b))
+    torch.cuda.synchronize()
+    mean_ms = [float(np.mean([a.elapsed_time(b) for a, b in d])) for d in durs]
+    flops = [prefill_flops(w, ch) for ch in w.chunks]
+    achieved = sum(flops) / (sum(mean_ms) * 1e-3) / 1e12
+    value = sum(flops) / (ms_per_step * 1e-3) / 1e12
+    line = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_TEXT.get(w.name, w.name) + " (prefill attention of each chunk)",
+            "global_batch": w.num_seqs,
+            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "page_size": w.page_size, "index": w.index,
+            "query_rows_per_chunk": [int(cu[-1]) for _, cu in w.chunks],
+            "flops_per_step": sum(flops),
+            "wall_s_timed_region": round(t_wall, 4),
+            "step": "per chunk: slot mapping + store + prefill attention (separate launches)",
+        },
+        "roofline": {
+            "kernel": "prefill_mfma_kernel",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "mean_launch_ms": [round(x, 5) for x in mean_ms],
+            "launches": nl * len(w.chunks),
+        },
+    }
+    if not args.no_cpu_baseline:
+        cb, parity = prefill_cpu_baseline(w, t, step)
+        line["cpu_baseline"] = cb
+        line["parity_vs_oracle"] = parity
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -194,6 +351,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.path == "prefill":
+        main_prefill(args, dev)
+        return
     w = make_workload(args)
     t = workloads.make_tensors(w, dev)
     step = Step(w, t, fused=is_decode_step(w) and not args.unfused)

@@ -381,6 +381,8 @@ int hpkv_paged_attention_prefill(int dtype, int index_type, const void* q, const
   if (page_size > 0x7fffffffu || max_q_len > 0x7fffffffu) return HPKV_ERR_INVALID_ARG;
   if (!(scale == scale)) return HPKV_ERR_INVALID_ARG;  // NaN scale
   if (!hpkv::prefill_head_dim_supported(dtype, head_dim)) return HPKV_ERR_UNSUPPORTED;
+  // the kernel keeps pool rows (page * page_size + offset) in 32 bits
+  if (num_pages > 0xffffffffull / page_size) return HPKV_ERR_UNSUPPORTED;
   const uint32_t group = num_q_heads / num_kv_heads;
   const uint32_t rows = hpkv::prefill_rows_per_workgroup(dtype, head_dim);
   if (group > rows) return HPKV_ERR_UNSUPPORTED;

@@ -48,7 +48,10 @@
 //    (bad cu_q / q_start / seq_ptr entries, a chunk longer than max_q_len or
 //    past its slice) gets NaN rows; a block that meets a page id >= num_pages
 //    writes NaN rows. Nothing is read or written out of bounds.
+#include <float.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "hpkv_device.h"
 
@@ -57,6 +60,7 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kKeyTile = 32;  // keys per tile (one 16x16x32 contraction of P.V)
+constexpr uint32_t kSegKeys = 4096;  // keys whose pool rows a workgroup resolves at once
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -72,13 +76,38 @@ __device__ inline uint2 lds_read_tr16(const char* p) {
   return r;
 }
 
+// Max over the four lanes l, l^16, l^32, l^48 that hold one row of a score tile
+// (v_permlane32_swap / v_permlane16_swap exchange whole 32- and 16-lane halves).
+__device__ inline float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Two fp32 weights rounded to nearest even in the 16-bit input type, packed low-first.
+template <int DT>
+__device__ inline uint32_t pack16(float x, float y) {
+  uint32_t r;
+  if constexpr (DT == kBF16) {
+    const bf16x2 v = bf16x2{(__bf16)x, (__bf16)y};
+    __builtin_memcpy(&r, &v, 4);
+  } else {
+    const f16x2 v = f16x2{(_Float16)x, (_Float16)y};
+    __builtin_memcpy(&r, &v, 4);
+  }
+  return r;
+}
+
 template <int DT>
 __device__ inline uint32_t nan_bits16() {
   return DT == kBF16 ? 0x7fc0u : 0x7e00u;
 }
 
-template <int DT, int D, int JT, int NW>
-__global__ __launch_bounds__(NW * kWave, 1) void prefill_mfma_kernel(const PrefillKernelArgs a) {
+template <int DT, int D, int JT, int NW, int MINB, typename Idx>
+__global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const PrefillKernelArgs a) {
   static_assert(DT != kF32 && D % 32 == 0 && D <= 256, "unsupported shape");
   constexpr int NTH = NW * kWave;
   constexpr int CPR = D * 2 / 16;                       // 16-byte chunks per K/V row
@@ -94,6 +123,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void prefill_mfma_kernel(const Prefi
 
   __shared__ __attribute__((aligned(16))) char s_k[2][kKeyTile * KROW];
   __shared__ __attribute__((aligned(16))) char s_v[2][kKeyTile * VROW];
+  __shared__ uint32_t s_rows[kSegKeys];  // pool row of each key of the current segment
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid % kWave;
@@ -115,8 +145,10 @@ __global__ __launch_bounds__(NW * kWave, 1) void prefill_mfma_kernel(const Prefi
   const int64_t c0 = a.cu_q[s];
   const int64_t c1 = a.cu_q[s + 1];
   const int32_t pstart = a.q_start[s];
-  const uint64_t first = read_idx(a.seq_ptr, s, a.idx64);
-  const uint64_t last = read_idx(a.seq_ptr, s + 1, a.idx64);
+  const Idx* seq_ptr = static_cast<const Idx*>(a.seq_ptr);
+  const Idx* block_table = static_cast<const Idx*>(a.block_table);
+  const uint64_t first = seq_ptr[s];
+  const uint64_t last = seq_ptr[s + 1];
   const int64_t n = c1 - c0;
   bool bad = c0 < 0 || n < 0 || uint64_t(c1) > a.num_q_tokens || n > int64_t(a.max_q_len) ||
              pstart < 0 || last < first || last > a.block_table_len;
@@ -146,63 +178,66 @@ __global__ __launch_bounds__(NW * kWave, 1) void prefill_mfma_kernel(const Prefi
   const uint32_t kend = uint32_t(pstart) + p_hi;  // keys 0 .. kend-1 are visible to the block
   const uint32_t ntiles = (kend + kKeyTile - 1) / kKeyTile;
 
+  // Scores are scaled by c = |scale| * log2(e) >= 0; a negative scale is folded into q
+  // as a sign flip (exact), so the row max of the raw products is the max of the scores.
+  const float c = fmaxf(fabsf(a.scale_log2), FLT_MIN);  // > 0 (a zero scale acts as FLT_MIN)
+  const uint32_t qflip = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
+  // lazy rescaling: the subtracted max is only raised when the row max grows by more
+  // than 8 (log2 units), so weights stay below 2^8 and most tiles skip the rescale
+  const float thr = c > 0.0f ? 8.0f / c : INFINITY;
+
   // rows of this lane: position (or -1 if inactive) and the query row in q/out
   int32_t pos[JT];
   uint64_t qrow[JT];
   u32x4 qop[JT][KS];
+  int32_t min_pos = 0x7fffffff;  // smallest active position of this lane
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) {
     const uint32_t r = wave * 16 * JT + jt * 16 + col;
     const uint32_t pl = p_lo + r / G;
     const bool active = r < QP * G && pl < p_hi;
     pos[jt] = active ? int32_t(uint32_t(pstart) + pl) : -1;
+    if (active) min_pos = min(min_pos, pos[jt]);
     qrow[jt] = active ? (uint64_t(c0 + pl) * a.num_q_heads + uint64_t(g) * G + r % G) : 0;
     const char* qp = static_cast<const char*>(a.q) + (qrow[jt] * D_ + 8 * q4) * 2;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qop[jt][ks] = active ? *reinterpret_cast<const u32x4*>(qp + 64 * ks) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = active ? *reinterpret_cast<const u32x4*>(qp + 64 * ks) : u32x4{0, 0, 0, 0};
+      qop[jt][ks] = v ^ qflip;
+    }
   }
+  // tiles wholly at or below the wave's smallest active position need no causal mask
+#pragma unroll
+  for (int o = 32; o >= 1; o /= 2) min_pos = min(min_pos, __shfl_xor(min_pos, o));
+  const bool wave_active = min_pos != 0x7fffffff;
 
   f32x4 acc[JT][NB];
-  float m[JT], l[JT];
+  f32x4 accl[JT];         // row sums of the weights (the matrix cores add them up)
+  float mthr[JT], mc[JT]; // rescale threshold (raw units) and the subtracted max * c
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) {
-    m[jt] = -INFINITY;
-    l[jt] = 0.0f;
+    mthr[jt] = -INFINITY;
+    mc[jt] = 0.0f;
+    accl[jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[jt][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
+  const uint32_t one2 = DT == kBF16 ? 0x3f803f80u : 0x3c003c00u;  // two 16-bit 1.0s
+  const u32x4 ones = u32x4{one2, one2, one2, one2};
 
   // loader role: tile row lr (+ RPP per pass), 16-byte chunk lc
   const bool loader = tid < uint32_t(LOADERS);
   const uint32_t lr = tid / CPR, lc = tid % CPR;
-  const char* kbase = static_cast<const char*>(a.k_cache) + lc * 16;
-  const char* vbase = static_cast<const char*>(a.v_cache) + lc * 16;
   const uint64_t row_stride = uint64_t(a.num_kv_heads) * D_ * 2;
-  const uint64_t head_off = uint64_t(g) * D_ * 2;
-  uint64_t phys[NP];
-  uint32_t poff[NP];
+  const uint64_t head_off = uint64_t(g) * D_ * 2 + lc * 16;
+  const char* kbase = static_cast<const char*>(a.k_cache) + head_off;
+  const char* vbase = static_cast<const char*>(a.v_cache) + head_off;
   bool bad_page = false;
-  auto fetch_pages = [&](uint32_t tb) {
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      uint32_t key = tb + p * RPP + lr;
-      key = key < kend ? key : kend - 1;
-      const uint32_t pg = fastdiv(key, a.page_div);
-      poff[p] = key - pg * a.page_size;
-      phys[p] = read_idx(a.block_table, first + pg, a.idx64);
-    }
-  };
   u32x4 kr[NP], vr[NP];
-  auto load_kv = [&]() {
+  auto load_kv = [&](uint32_t tl) {  // tl: first key of the tile, relative to the segment
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      uint64_t ph = phys[p];
-      if (ph >= a.num_pages) {
-        bad_page = true;
-        ph = 0;
-      }
-      const uint64_t off = (ph * a.page_size + poff[p]) * row_stride + head_off;
+      const uint64_t off = uint64_t(s_rows[tl + p * RPP + lr]) * row_stride;
       kr[p] = load16<false>(kbase + off);
       vr[p] = load16<false>(vbase + off);
     }
@@ -216,23 +251,10 @@ __global__ __launch_bounds__(NW * kWave, 1) void prefill_mfma_kernel(const Prefi
     }
   };
 
-  if (loader) {
-    fetch_pages(0);
-    load_kv();
-    if (ntiles > 1) fetch_pages(kKeyTile);
-    store_lds(0);
-  }
-  __syncthreads();
-
-  for (uint32_t it = 0; it < ntiles; ++it) {
-    const uint32_t tb = it * kKeyTile;
-    const int b = it & 1;
-    const bool has_next = it + 1 < ntiles;
-    if (loader && has_next) {
-      load_kv();
-      if (it + 2 < ntiles) fetch_pages(tb + 2 * kKeyTile);
-    }
-
+  // One 32-key tile: scores, online softmax, P.V. MASK: some key of the tile lies past
+  // the position of some row of this wave (the diagonal tiles); the others skip the mask.
+  auto tile = [&](auto mask_tag, int b, uint32_t tb) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     // scores: keys tb + 16u + 4*q4 + r of row `col` of each column block
     f32x4 sacc[2][JT];
 #pragma unroll
@@ -241,47 +263,45 @@ __global__ __launch_bounds__(NW * kWave, 1) void prefill_mfma_kernel(const Prefi
       for (int jt = 0; jt < JT; ++jt) sacc[u][jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kop =
-            *reinterpret_cast<const u32x4*>(&s_k[b][(16 * u + col) * KROW + (32 * ks + 8 * q4) * 2]);
+        const u32x4 kop = *reinterpret_cast<const u32x4*>(
+            &s_k[b][(16 * u + col) * KROW + (32 * ks + 8 * q4) * 2]);
 #pragma unroll
-        for (int jt = 0; jt < JT; ++jt) sacc[u][jt] = mfma_16x16x32<DT>(kop, qop[jt][ks], sacc[u][jt]);
+        for (int jt = 0; jt < JT; ++jt)
+          sacc[u][jt] = mfma_16x16x32<DT>(kop, qop[jt][ks], sacc[u][jt]);
       }
     }
-
     u32x4 pop[JT];
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) {
-      float z[8];
+      float sv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int32_t t = int32_t(tb + 16 * (e / 4) + 4 * q4 + (e % 4));
-        z[e] = t <= pos[jt] ? sacc[e / 4][jt][e % 4] * a.scale_log2 : -INFINITY;
+        sv[e] = sacc[e / 4][jt][e % 4];
+        if constexpr (MASK) {
+          if (int32_t(tb + 16 * (e / 4) + 4 * q4 + (e % 4)) > pos[jt]) sv[e] = -INFINITY;
+        }
       }
-      float mt = z[0];
+      float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mt = row_max4(mt);
+      const bool need = mt > mthr[jt];
+      if (__any(need)) {
+        const float mcn = need ? mt * c : mc[jt];
+        // no earlier weights on first use (mthr still -inf): the accumulators are zero
+        const float corr = mthr[jt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mc[jt] - mcn);
+        if (need) mthr[jt] = mt + thr;
+        mc[jt] = mcn;
+        accl[jt] *= corr;
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, z[e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m[jt], mt);
-      const float mu = mn == -INFINITY ? 0.0f : mn;
-      const float corr = __builtin_amdgcn_exp2f(m[jt] - mu);
-      m[jt] = mn;
-      l[jt] *= corr;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[jt][nb] *= corr;
-      uint32_t pw[4];
-      float psum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const uint32_t b0 = round16<DT>(__builtin_amdgcn_exp2f(z[e] - mu));
-        const uint32_t b1 = round16<DT>(__builtin_amdgcn_exp2f(z[e + 1] - mu));
-        psum += widen_bits16<DT>(b0) + widen_bits16<DT>(b1);
-        pw[e / 2] = b0 | (b1 << 16);
+        for (int nb = 0; nb < NB; ++nb) acc[jt][nb] *= corr;
       }
-      l[jt] += psum;
-      pop[jt] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+      // masked scores are -inf and c > 0, so their weight is exactly 0
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], c, -mc[jt]));
+      pop[jt] = u32x4{pack16<DT>(pv[0], pv[1]), pack16<DT>(pv[2], pv[3]),
+                      pack16<DT>(pv[4], pv[5]), pack16<DT>(pv[6], pv[7])};
     }
-
     // O^T += V^T P^T; lane (q4, col) fetches row 4*q4 + col/4 (and 16 + that) of the
     // tile, columns 16*nb + 4*(col%4) .. +3, and receives column 16*nb + col.
     const char* vrow0 = &s_v[b][(4 * q4 + col / 4) * VROW + 8 * (col % 4)];
@@ -293,20 +313,54 @@ __global__ __launch_bounds__(NW * kWave, 1) void prefill_mfma_kernel(const Prefi
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) acc[jt][nb] = mfma_16x16x32<DT>(vop, pop[jt], acc[jt][nb]);
     }
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) accl[jt] = mfma_16x16x32<DT>(ones, pop[jt], accl[jt]);
+  };
 
-    if (loader && has_next) store_lds(b ^ 1);
+  // Keys are processed in segments of kSegKeys: the workgroup first resolves every key
+  // of the segment to its pool row through the block table (keys past the block's last
+  // position reuse the last visible key), then streams the segment's tiles.
+  for (uint32_t seg0 = 0; seg0 < kend; seg0 += kSegKeys) {
+    const uint32_t seg_len = kend - seg0 < kSegKeys ? kend - seg0 : kSegKeys;
+    const uint32_t seg_tiles = (seg_len + kKeyTile - 1) / kKeyTile;
+    for (uint32_t k = tid; k < seg_tiles * kKeyTile; k += NTH) {
+      const uint32_t key = seg0 + k < kend ? seg0 + k : kend - 1;
+      const uint32_t pg = fastdiv(key, a.page_div);
+      uint64_t ph = uint64_t(block_table[first + pg]);
+      if (ph >= a.num_pages) {
+        bad_page = true;
+        ph = 0;
+      }
+      s_rows[k] = uint32_t(ph * a.page_size + (key - pg * a.page_size));
+    }
     __syncthreads();
+    if (loader) {
+      load_kv(0);
+      store_lds(0);
+    }
+    __syncthreads();
+    for (uint32_t it = 0; it < seg_tiles; ++it) {
+      const uint32_t tb = seg0 + it * kKeyTile;
+      const int b = it & 1;
+      const bool has_next = it + 1 < seg_tiles;
+      if (loader && has_next) load_kv((it + 1) * kKeyTile);
+      if (wave_active) {
+        if (int32_t(tb + kKeyTile - 1) <= min_pos) {
+          tile(std::false_type{}, b, tb);
+        } else {
+          tile(std::true_type{}, b, tb);
+        }
+      }
+      if (loader && has_next) store_lds(b ^ 1);
+      __syncthreads();
+    }
   }
 
   const bool any_bad = __syncthreads_or(bad_page);
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) {
-    // the four lane quarters hold disjoint keys of each row: add their sums
-    float lt = l[jt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
     if (pos[jt] < 0) continue;
-    const float inv = any_bad ? __builtin_nanf("") : 1.0f / lt;
+    const float inv = any_bad ? __builtin_nanf("") : 1.0f / accl[jt][0];
     char* orow = static_cast<char*>(a.out) + (qrow[jt] * D_ + 4 * q4) * 2;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -318,18 +372,29 @@ __global__ __launch_bounds__(NW * kWave, 1) void prefill_mfma_kernel(const Prefi
   }
 }
 
+#ifndef HPKV_PREFILL_JT
+#define HPKV_PREFILL_JT 1
+#define HPKV_PREFILL_MINB 2
+#define HPKV_PREFILL_NW 8
+#endif
 template <int DT, int D>
 struct PrefillShape {
-  static constexpr int JT = D >= 256 ? 2 : 4;  // 16-row column blocks per wave
-  static constexpr int NW = 4;
+  static constexpr int JT = HPKV_PREFILL_JT;  // 16-row column blocks per wave
+  static constexpr int NW = HPKV_PREFILL_NW;
+  static constexpr int MINB = D >= 256 ? 1 : HPKV_PREFILL_MINB;  // workgroups per CU
   static constexpr int ROWS = NW * 16 * JT;
 };
 
 template <int DT, int D>
 hipError_t launch_prefill_shape(const PrefillKernelArgs& a, uint32_t nwg, hipStream_t stream) {
   using S = PrefillShape<DT, D>;
-  hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, S::JT, S::NW>), dim3(nwg), dim3(S::NW * kWave),
-                     0, stream, a);
+  if (a.idx64) {
+    hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, S::JT, S::NW, S::MINB, uint64_t>), dim3(nwg),
+                       dim3(S::NW * kWave), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, S::JT, S::NW, S::MINB, uint32_t>), dim3(nwg),
+                       dim3(S::NW * kWave), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -354,7 +419,11 @@ bool prefill_head_dim_supported(int dtype, uint32_t head_dim) {
 
 uint32_t prefill_rows_per_workgroup(int dtype, uint32_t head_dim) {
   (void)dtype;
-  return head_dim >= 256 ? PrefillShape<kBF16, 256>::ROWS : PrefillShape<kBF16, 128>::ROWS;
+  static_assert(PrefillShape<kBF16, 256>::ROWS == PrefillShape<kBF16, 128>::ROWS &&
+                PrefillShape<kBF16, 32>::ROWS == PrefillShape<kBF16, 128>::ROWS,
+                "one row count for every head size");
+  (void)head_dim;
+  return PrefillShape<kBF16, 128>::ROWS;
 }
 
 hipError_t launch_prefill(int dtype, uint32_t head_dim, const PrefillKernelArgs& a,
