@@ -372,16 +372,18 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
   }
 }
 
-#ifndef HPKV_PREFILL_JT
-#define HPKV_PREFILL_JT 1
-#define HPKV_PREFILL_MINB 2
-#define HPKV_PREFILL_NW 8
-#endif
+// Launch shape per head size: 16-row column blocks per wave (JT), waves per
+// workgroup (NW) and workgroups per CU (MINB). Every operand byte read from LDS
+// feeds JT matrix-core products, and the LDS read rate (not the matrix cores)
+// bounds a one-block wave, so two blocks per wave at two waves per SIMD is the
+// best balance where the registers allow it; at head_dim 256 the accumulators
+// of two blocks do not fit two waves per SIMD, so it keeps one block per wave
+// and eight waves per workgroup. Every shape covers 128 rows per workgroup.
 template <int DT, int D>
 struct PrefillShape {
-  static constexpr int JT = HPKV_PREFILL_JT;  // 16-row column blocks per wave
-  static constexpr int NW = HPKV_PREFILL_NW;
-  static constexpr int MINB = D >= 256 ? 1 : HPKV_PREFILL_MINB;  // workgroups per CU
+  static constexpr int JT = D >= 256 ? 1 : 2;
+  static constexpr int NW = D >= 256 ? 8 : 4;
+  static constexpr int MINB = D >= 256 ? 1 : 2;
   static constexpr int ROWS = NW * 16 * JT;
 };
 
