@@ -51,6 +51,8 @@ PREFILL_METRIC = "paged chunked-prefill attention: achieved TFLOP/s (causal flop
 METRIC = "paged decode: achieved KV HBM GB/s (% of peak) + sequences/s per layer"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_hpkv_amd", "csrc", "hpkv_decode.hip")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_hpkv_amd", "csrc", "hpkv_prefill.hip")
 
 WORKLOAD_TEXT = {
     "llama7b": "Llama-2-7B-shaped layer decode step: Hq=Hkv=32, d=128, bs=16, 64 seqs, "
@@ -158,12 +160,13 @@ def algorithmic_decode_bytes(w):
     return int(w.kv_bytes_logical() + pages.sum() * idx + per_seq * w.num_seqs)
 
 
-def recorded_traffic(w):
-    """HBM bytes per partition launch from committed counter runs, if still current."""
+def recorded_traffic(w, traffic_file=TRAFFIC_FILE, src=DECODE_SRC):
+    """HBM bytes per launch of the dominant kernel from committed counter runs, if the
+    kernel source has not changed since they were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file) as f:
             rec = json.load(f)
-        with open(DECODE_SRC, "rb") as f:
+        with open(src, "rb") as f:
             src_hash = hashlib.sha256(f.read()).hexdigest()
     except (OSError, ValueError):
         return None
@@ -193,6 +196,16 @@ def cpu_baseline(w, t, out_gpu):
                        f"sequences) once, double precision, {threads} host threads, "
                        f"{dt:.2f} s"), dict(max_abs_err=max_err, within_tolerance=ratio <= 1.0
                                             and finite)
+
+
+def calibration_copy(dev):
+    """A plain 1 GiB device copy, whose counter readings scale the kernels' HBM bytes."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def prefill_flops(w, chunk):
@@ -297,6 +310,7 @@ def main_prefill(args, dev):
     flops = [prefill_flops(w, ch) for ch in w.chunks]
     achieved = sum(flops) / (sum(mean_ms) * 1e-3) / 1e12
     value = sum(flops) / (ms_per_step * 1e-3) / 1e12
+    prec = recorded_traffic(w, PREFILL_TRAFFIC_FILE, PREFILL_SRC)
     line = {
         "metric": PREFILL_METRIC,
         "value": round(value, 2),
@@ -327,12 +341,17 @@ def main_prefill(args, dev):
             "peak": MFMA16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": None if prec is None else prec.get("hbm_bytes_per_launch"),
             "algorithmic_flops_per_launch": flops,
             "mean_launch_ms": [round(x, 5) for x in mean_ms],
             "launches": nl * len(w.chunks),
         },
     }
+    if prec is not None:
+        line["roofline"]["traffic_unit"] = ("HBM bytes per launch, one entry per chunk "
+                                            "(rocprofv3 FETCH_SIZE + WRITE_SIZE)")
+    if args.copy_calibration:
+        calibration_copy(dev)
     if not args.no_cpu_baseline:
         cb, parity = prefill_cpu_baseline(w, t, step)
         line["cpu_baseline"] = cb
@@ -360,12 +379,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(dev)
 
     for _ in range(args.warmup):
         step()
