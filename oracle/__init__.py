@@ -22,6 +22,7 @@ from . import build as _build
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+KV_CODE = {"i8": 3, "fp8": 4}  # quantized pool element types (1 byte each)
 _ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 
 # status codes of the oracle library
@@ -64,6 +65,17 @@ def _load():
     lib.orc_paged_attention_prefill.argtypes = [i32, i32, vp, vp, vp, vp, u64, vp, vp, vp, u64,
                                                 u64, u64, u64, u64, u64, ctypes.c_double, vp, vp]
     lib.orc_paged_attention_prefill.restype = i32
+    lib.orc_paged_attention_decode_quant.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                                     vp, u64, vp, vp, u64, u64, u64, u64, u64,
+                                                     u64, ctypes.c_double, vp, vp, i32]
+    lib.orc_paged_attention_decode_quant.restype = i32
+    lib.orc_store_kvcache_quant.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64,
+                                            u64, u64, u64, u64]
+    lib.orc_store_kvcache_quant.restype = i64
+    lib.orc_fp8_e4m3_decode.argtypes = [vp, u64, vp]
+    lib.orc_fp8_e4m3_decode.restype = None
+    lib.orc_quantize.argtypes = [i32, vp, u64, vp]
+    lib.orc_quantize.restype = None
     lib.orc_round_to_dtype.argtypes = [i32, vp, u64, vp]
     lib.orc_round_to_dtype.restype = None
     lib.orc_widen_dtype.argtypes = [i32, vp, u64, vp]
@@ -199,6 +211,68 @@ def paged_attention_prefill(dtype, q, k_cache, v_cache, block_table, seq_ptr, q_
                                              num_pages, float(scale), _ptr(out), _ptr(out64))
     if st != OK:
         raise ValueError(f"paged_attention_prefill: oracle status {st}")
+    return out, out64
+
+
+def fp8_e4m3_decode(codes):
+    """float64 values of OCP E4M3 ("e4m3fn") codes (uint8 array)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().orc_fp8_e4m3_decode(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def quantize(kv_type, t):
+    """Codes (uint8) of fp32 values t: nearest, ties to even, saturating."""
+    t = np.ascontiguousarray(t, dtype=np.float32)
+    out = np.empty(t.shape, dtype=np.uint8)
+    _load().orc_quantize(KV_CODE[kv_type], _ptr(t), t.size, _ptr(out))
+    return out
+
+
+def store_kvcache_quant(dtype, kv_type, key, value, k_cache, v_cache, k_scale, k_zero, v_scale,
+                        v_zero, slots):
+    """In-place quantized store into uint8 pools [num_pages, bs, Hkv, d]; returns #skipped."""
+    if not (k_cache.flags.c_contiguous and v_cache.flags.c_contiguous):
+        raise ValueError("caches must be C-contiguous")
+    assert k_cache.dtype == np.uint8 and v_cache.dtype == np.uint8
+    key = _storage(key, dtype)
+    value = _storage(value, dtype)
+    sc = [np.ascontiguousarray(x, dtype=np.float32) for x in (k_scale, k_zero, v_scale, v_zero)]
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    num_pages, bs, H, d = k_cache.shape
+    r = _load().orc_store_kvcache_quant(_DTYPE_CODE[dtype], KV_CODE[kv_type], _ptr(key),
+                                        _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                        *[_ptr(x) for x in sc], _ptr(slots), len(slots), bs,
+                                        num_pages, H, d)
+    if r < 0:
+        raise ValueError("store_kvcache_quant: bad arguments")
+    return r
+
+
+def paged_attention_decode_quant(dtype, kv_type, q, k_cache, v_cache, k_scale, k_zero, v_scale,
+                                 v_zero, block_table, seq_ptr, context_lens, scale,
+                                 num_threads=1):
+    """Decode over quantized pools; returns (out in dtype, out as float64)."""
+    q = _storage(q, dtype)
+    k_cache = np.ascontiguousarray(k_cache, dtype=np.uint8)
+    v_cache = np.ascontiguousarray(v_cache, dtype=np.uint8)
+    sc = [np.ascontiguousarray(x, dtype=np.float32) for x in (k_scale, k_zero, v_scale, v_zero)]
+    seq_ptr = np.ascontiguousarray(seq_ptr)
+    block_table = np.ascontiguousarray(block_table, dtype=seq_ptr.dtype)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B, Hq, d = q.shape
+    num_pages, bs, Hkv, _ = k_cache.shape
+    assert all(x.size == num_pages * Hkv for x in sc)
+    out = np.empty_like(q)
+    out64 = np.empty((B, Hq, d), dtype=np.float64)
+    st = _load().orc_paged_attention_decode_quant(
+        _DTYPE_CODE[dtype], KV_CODE[kv_type], _index_bytes(seq_ptr), _ptr(q), _ptr(k_cache),
+        _ptr(v_cache), *[_ptr(x) for x in sc], _ptr(block_table), len(block_table),
+        _ptr(seq_ptr), _ptr(ctx), B, Hq, Hkv, d, bs, num_pages, float(scale), _ptr(out),
+        _ptr(out64), int(num_threads))
+    if st != OK:
+        raise ValueError(f"paged_attention_decode_quant: oracle status {st}")
     return out, out64
 
 

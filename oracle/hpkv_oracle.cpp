@@ -31,6 +31,14 @@
 //     repeated slots resolve last-writer-wins in token order.
 //   * GQA: query head h reads KV head h / (Hq/Hkv) ([INT] Step 2).
 //   * scale multiplies the q.k dot product ([INT] Step 2).
+//   * Quantized pools ([HUR] "Quantization compatibility": per-block-affine
+//     along the paged axis with block_size == page_size, so every physical
+//     page slot carries its own scales): elements are int8 or OCP fp8 E4M3
+//     ("e4m3fn"); each page holds, per KV head, an fp32 scale and zero point
+//     for K and for V, and an element with code q stands for
+//     scale * (value(q) - zero). The store quantizes t = x / scale + zero
+//     (both steps in fp32) to the nearest code, ties to even, saturating at
+//     the type's range (int8: [-128, 127]; e4m3fn: +-448).
 //   * Chunked prefill: the query at position p of a chunk attends to tokens
 //     0..p of its own sequence (causal softmax attention), all read from the
 //     pool, so the chunk's own K/V rows are stored before attention ([INT]
@@ -57,8 +65,9 @@ enum : int {
   ORC_OUT_OF_RANGE = 7,       // an element lookup coordinate is out of range
 };
 
-// Element storage types understood by the oracle.
-enum : int { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+// Element storage types understood by the oracle (the last two only for the
+// K/V pools).
+enum : int { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_I8 = 3, ORC_FP8 = 4 };
 
 uint64_t read_index(int index_bytes, const void* p, uint64_t i) {
   if (index_bytes == 4) return static_cast<const uint32_t*>(p)[i];
@@ -96,6 +105,57 @@ double load_elem(int dtype, const void* base, uint64_t idx) {
   if (dtype == ORC_F32) return widen_f32(static_cast<const uint32_t*>(base)[idx]);
   const uint16_t b = static_cast<const uint16_t*>(base)[idx];
   return dtype == ORC_BF16 ? widen_bf16(b) : widen_f16(b);
+}
+
+// OCP 8-bit float E4M3 in its "fn" variant: 1 sign bit, 4 exponent bits with
+// bias 7, 3 fraction bits. Exponent 0 holds subnormals (frac/8 * 2^-6); the
+// pattern with every exponent and fraction bit set is NaN; there is no
+// infinity, so the largest finite magnitude is 1.75 * 2^8 = 448.
+double widen_fp8_e4m3(uint8_t bits) {
+  const int sign = bits >> 7;
+  const int expo = (bits >> 3) & 0xf;
+  const int frac = bits & 0x7;
+  double mag;
+  if (expo == 0xf && frac == 0x7) {
+    mag = NAN;
+  } else if (expo == 0) {
+    mag = std::ldexp(double(frac), -9);  // frac/8 * 2^-6
+  } else {
+    mag = std::ldexp(double(8 + frac), expo - 10);  // (1 + frac/8) * 2^(expo-7)
+  }
+  return sign ? -mag : mag;
+}
+
+// The value a quantized code stands for before the affine map.
+double code_value(int kv_type, uint8_t code) {
+  return kv_type == ORC_I8 ? double(int8_t(code)) : widen_fp8_e4m3(code);
+}
+
+// Quantizes fp32 t to a code of kv_type: the nearest representable value,
+// ties to even, saturating at the largest finite magnitude; NaN gives the NaN
+// code for fp8 and 0 for int8. For fp8 the search runs over every finite
+// code, so no rounding shortcut is involved.
+uint8_t quantize_code(int kv_type, float t) {
+  if (kv_type == ORC_I8) {
+    if (std::isnan(t)) return 0;
+    double r = std::nearbyint(double(t));  // default rounding mode: ties to even
+    if (r < -128.0) r = -128.0;
+    if (r > 127.0) r = 127.0;
+    return uint8_t(int8_t(int(r)));
+  }
+  if (std::isnan(t)) return 0x7f;
+  const double a = std::fabs(double(t));
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7e; ++c) {  // every finite non-negative code, in increasing value
+    const double err = std::fabs(widen_fp8_e4m3(uint8_t(c)) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  if (a >= 448.0) best = 0x7e;  // saturate
+  return uint8_t(best | (std::signbit(t) ? 0x80 : 0));
 }
 
 // ---- rounding double -> storage type, to nearest, ties to even -------------
@@ -209,7 +269,25 @@ struct DecodeArgs {
   double scale;
   void* out;        // [B, Hq, d] in dtype
   double* out_f64;  // [B, Hq, d] unrounded, may be null
+  // Pool element type (ORC_F32/F16/BF16: the same as dtype; ORC_I8/ORC_FP8:
+  // quantized, with per (page, KV head) scales and zero points for K and V).
+  int kv_type;
+  const float* k_scale;
+  const float* k_zero;
+  const float* v_scale;
+  const float* v_zero;
 };
+
+// Element e of KV head g in pool row `row` (= page * page_size + offset), as the
+// real number it stands for.
+double kv_elem(const DecodeArgs& a, const void* pool, const float* sc, const float* zr,
+               uint64_t row, uint64_t g, uint64_t e) {
+  const uint64_t idx = (row * a.num_kv_heads + g) * a.head_dim + e;
+  if (a.kv_type != ORC_I8 && a.kv_type != ORC_FP8) return load_elem(a.dtype, pool, idx);
+  const uint64_t p = (row / a.page_size) * a.num_kv_heads + g;
+  const double v = code_value(a.kv_type, static_cast<const uint8_t*>(pool)[idx]);
+  return double(sc[p]) * (v - double(zr[p]));
+}
 
 // One sequence of [INT] "Step 2: paged_attention_decode": gather the first
 // ctx tokens of K and V through the block table, then for every query head
@@ -237,10 +315,10 @@ int decode_one_sequence(const DecodeArgs& a, uint64_t s) {
     const uint64_t q_base = (s * Hq + h) * d;
     double zmax = -INFINITY;
     for (uint64_t t = 0; t < n; ++t) {
-      const uint64_t k_base = (rows[t] * Hkv + g) * d;
       double dot = 0.0;
       for (uint64_t e = 0; e < d; ++e)
-        dot += load_elem(a.dtype, a.q, q_base + e) * load_elem(a.dtype, a.k_cache, k_base + e);
+        dot += load_elem(a.dtype, a.q, q_base + e) *
+               kv_elem(a, a.k_cache, a.k_scale, a.k_zero, rows[t], g, e);
       z[t] = dot * a.scale;
       zmax = std::max(zmax, z[t]);
     }
@@ -249,8 +327,8 @@ int decode_one_sequence(const DecodeArgs& a, uint64_t s) {
     for (uint64_t t = 0; t < n; ++t) {
       const double w = std::exp(z[t] - zmax);
       denom += w;
-      const uint64_t v_base = (rows[t] * Hkv + g) * d;
-      for (uint64_t e = 0; e < d; ++e) o[e] += w * load_elem(a.dtype, a.v_cache, v_base + e);
+      for (uint64_t e = 0; e < d; ++e)
+        o[e] += w * kv_elem(a, a.v_cache, a.v_scale, a.v_zero, rows[t], g, e);
     }
     for (uint64_t e = 0; e < d; ++e) {
       const double val = n == 0 ? 0.0 : o[e] / denom;
@@ -260,6 +338,8 @@ int decode_one_sequence(const DecodeArgs& a, uint64_t s) {
   }
   return ORC_OK;
 }
+
+int run_decode(const DecodeArgs& a, int num_threads);
 
 }  // namespace
 
@@ -406,7 +486,94 @@ int orc_paged_attention_decode(int dtype, int index_bytes, const void* q, const 
   DecodeArgs a{dtype,       index_bytes,  q,           k_cache,      v_cache,
                block_table, block_table_len, seq_ptr, context_lens, num_seqs,
                num_q_heads, num_kv_heads, head_dim,    page_size,    num_pages,
-               scale,       out,          out_f64};
+               scale,       out,          out_f64,     dtype,        nullptr,
+               nullptr,     nullptr,      nullptr};
+  return run_decode(a, num_threads);
+}
+
+// Decode over quantized pools (kv_type ORC_I8 or ORC_FP8, 1 byte per element,
+// [num_pages, page_size, Hkv, d]); scales and zero points are fp32
+// [num_pages, Hkv]. Every K/V element is taken at its exact real value
+// scale * (value(code) - zero) in double; the rest is the decode above.
+int orc_paged_attention_decode_quant(int dtype, int kv_type, int index_bytes, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const float* k_scale, const float* k_zero,
+                                     const float* v_scale, const float* v_zero,
+                                     const void* block_table, uint64_t block_table_len,
+                                     const void* seq_ptr, const int32_t* context_lens,
+                                     uint64_t num_seqs, uint64_t num_q_heads,
+                                     uint64_t num_kv_heads, uint64_t head_dim, uint64_t page_size,
+                                     uint64_t num_pages, double scale, void* out, double* out_f64,
+                                     int num_threads) {
+  if (dtype != ORC_F32 && dtype != ORC_F16 && dtype != ORC_BF16) return ORC_BAD_ARG;
+  if (kv_type != ORC_I8 && kv_type != ORC_FP8) return ORC_BAD_ARG;
+  if (index_bytes != 4 && index_bytes != 8) return ORC_BAD_ARG;
+  if (num_kv_heads == 0 || head_dim == 0 || page_size == 0) return ORC_BAD_ARG;
+  if (num_q_heads % num_kv_heads != 0) return ORC_BAD_ARG;
+  if (!k_scale || !k_zero || !v_scale || !v_zero) return ORC_BAD_ARG;
+  DecodeArgs a{dtype,       index_bytes,  q,           k_cache,      v_cache,
+               block_table, block_table_len, seq_ptr, context_lens, num_seqs,
+               num_q_heads, num_kv_heads, head_dim,    page_size,    num_pages,
+               scale,       out,          out_f64,     kv_type,      k_scale,
+               k_zero,      v_scale,      v_zero};
+  return run_decode(a, num_threads);
+}
+
+// Quantized store: every new row with a slot in [0, num_pages*page_size) is
+// quantized element by element with the scale and zero point of its page and
+// KV head (t = x / scale + zero in fp32, then quantize_code) and written to
+// that pool row; rows with any other slot are skipped (last writer wins for
+// repeated slots). key/value are [n, Hkv, d] of dtype. Returns the number of
+// skipped rows, or -1 on a bad argument.
+int64_t orc_store_kvcache_quant(int dtype, int kv_type, const void* key, const void* value,
+                                void* k_cache, void* v_cache, const float* k_scale,
+                                const float* k_zero, const float* v_scale, const float* v_zero,
+                                const int64_t* slots, uint64_t n, uint64_t page_size,
+                                uint64_t num_pages, uint64_t num_kv_heads, uint64_t head_dim) {
+  if (dtype != ORC_F32 && dtype != ORC_F16 && dtype != ORC_BF16) return -1;
+  if (kv_type != ORC_I8 && kv_type != ORC_FP8) return -1;
+  if (page_size == 0 || num_kv_heads == 0 || head_dim == 0) return -1;
+  const uint64_t num_slots = num_pages * page_size;
+  int64_t skipped = 0;
+  for (uint64_t i = 0; i < n; ++i) {
+    if (slots[i] < 0 || uint64_t(slots[i]) >= num_slots) {
+      ++skipped;
+      continue;
+    }
+    const uint64_t slot = uint64_t(slots[i]);
+    const uint64_t page = slot / page_size;
+    for (uint64_t g = 0; g < num_kv_heads; ++g) {
+      const uint64_t p = page * num_kv_heads + g;
+      for (uint64_t e = 0; e < head_dim; ++e) {
+        const uint64_t src = (i * num_kv_heads + g) * head_dim + e;
+        const uint64_t dst = (slot * num_kv_heads + g) * head_dim + e;
+        const float xk = float(load_elem(dtype, key, src));
+        const float xv = float(load_elem(dtype, value, src));
+        const float tk = xk / k_scale[p] + k_zero[p];
+        const float tv = xv / v_scale[p] + v_zero[p];
+        static_cast<uint8_t*>(k_cache)[dst] = quantize_code(kv_type, tk);
+        static_cast<uint8_t*>(v_cache)[dst] = quantize_code(kv_type, tv);
+      }
+    }
+  }
+  return skipped;
+}
+
+// Exposes the fp8 decoding and the quantizer for the pins.
+void orc_fp8_e4m3_decode(const uint8_t* codes, uint64_t n, double* out) {
+  for (uint64_t i = 0; i < n; ++i) out[i] = widen_fp8_e4m3(codes[i]);
+}
+
+void orc_quantize(int kv_type, const float* t, uint64_t n, uint8_t* out) {
+  for (uint64_t i = 0; i < n; ++i) out[i] = quantize_code(kv_type, t[i]);
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_decode(const DecodeArgs& a, int num_threads) {
+  const uint64_t num_seqs = a.num_seqs;
   if (num_threads < 1) num_threads = 1;
   std::vector<int> status(num_threads, ORC_OK);
   auto work = [&](int k) {
@@ -426,6 +593,10 @@ int orc_paged_attention_decode(int dtype, int index_bytes, const void* q, const 
     if (st != ORC_OK) return st;
   return ORC_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 // Textbook softmax attention for one query over K/V held contiguously
 // ([L, Hkv, d], token-major, never read through a page pool): the dense
