@@ -63,6 +63,11 @@ typedef enum { HPKV_INDEX_U32 = 0, HPKV_INDEX_U64 = 1 } hpkv_index_type;
 /* Element type of q, out, new K/V rows and the page pools. */
 typedef enum { HPKV_F32 = 0, HPKV_F16 = 1, HPKV_BF16 = 2 } hpkv_dtype;
 
+/* Element type of quantized page pools, one byte per element: two's-complement
+ * int8, or OCP 8-bit float E4M3 in its "fn" variant (bias 7, largest finite
+ * magnitude 448, no infinity, NaN = 0x7f / 0xff). */
+typedef enum { HPKV_KV_I8 = 3, HPKV_KV_FP8_E4M3 = 4 } hpkv_kv_type;
+
 /* Static description of a status code (never NULL). */
 const char* hpkv_status_string(int status);
 
@@ -313,6 +318,71 @@ int hpkv_paged_attention_prefill(int dtype, int index_type, const void* q, const
                                  uint32_t num_kv_heads, uint32_t head_dim, uint32_t page_size,
                                  uint64_t num_pages, float scale, uint32_t max_q_len, void* out,
                                  void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Quantized page pools.
+ *
+ * "Block-Paged KV Cache", section "Quantization compatibility": KV caches are
+ * often int8/fp8, and per-block-affine quantization is allowed only along the
+ * paged axis with block_size == page_size, so the scales belong to a physical
+ * page slot and a page shared by several sequences carries its own. The
+ * dequantization formula is not given there; this library takes the affine
+ * reading: each page slot holds, per KV head, an fp32 scale and zero point
+ * for K and another pair for V, and a code c stands for
+ *   scale * (value(c) - zero)
+ * with value(c) the int8 integer or the E4M3 number.
+ *   k_scale, k_zero, v_scale, v_zero   device fp32 [num_pages, num_kv_heads]
+ *   k_cache, v_cache                   device [num_pages, page_size,
+ *                                      num_kv_heads, head_dim] of kv_type
+ * Scales must be finite and non-zero; zero points finite.
+ * ------------------------------------------------------------------------- */
+
+/* ---------------------------------------------------------------------------
+ * hpkv_store_kvcache_quant  (device)
+ *
+ * hpkv_store_kvcache into quantized pools: for every i < num_tokens whose slot
+ * is in [0, num_pages*page_size), element x of K row i (KV head g) is written
+ * as the code nearest to t = x / k_scale[page, g] + k_zero[page, g] (page =
+ * slot / page_size; the division rounded to nearest fp32, then the add), ties
+ * to even, saturating at the type's range (int8 [-128, 127], E4M3 +-448); NaN
+ * gives 0 (int8) or 0x7f (E4M3). Likewise V with v_scale / v_zero. Other
+ * slots are skipped; repeated slots race.
+ *   key, value   device [num_tokens, num_kv_heads, head_dim] of dtype,
+ *                16-byte aligned
+ *   head_dim     a multiple of 8 (else HPKV_ERR_UNSUPPORTED)
+ * ------------------------------------------------------------------------- */
+int hpkv_store_kvcache_quant(int dtype, int kv_type, const void* key, const void* value,
+                             void* k_cache, void* v_cache, const float* k_scale,
+                             const float* k_zero, const float* v_scale, const float* v_zero,
+                             const int64_t* slots, uint64_t num_tokens, uint32_t page_size,
+                             uint64_t num_pages, uint32_t num_kv_heads, uint32_t head_dim,
+                             void* stream);
+
+/* ---------------------------------------------------------------------------
+ * hpkv_paged_attention_decode_quant  (device)
+ *
+ * hpkv_paged_attention_decode over quantized pools: every K/V element is
+ * taken as scale * (value(code) - zero) of its page slot and KV head. q and
+ * out keep dtype (f32, f16 or bf16); arithmetic is fp32 throughout (the page
+ * scale multiplies each score, the V scale each weight, and the zero points
+ * enter as one correction per row). The workspace, its size function
+ * (hpkv_paged_attention_decode_workspace_size with the same dtype), the
+ * tail masking, the malformed-input NaN results and the argument errors are
+ * those of hpkv_paged_attention_decode. Requirements: head_dim in
+ * {16, 32, 64, 128, 256}; q, k_cache, v_cache and workspace 16-byte aligned;
+ * num_pages * num_kv_heads < 2^32.
+ * ------------------------------------------------------------------------- */
+int hpkv_paged_attention_decode_quant(int dtype, int kv_type, int index_type, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const float* k_scale, const float* k_zero,
+                                      const float* v_scale, const float* v_zero,
+                                      const void* block_table, uint64_t block_table_len,
+                                      const void* seq_ptr, const int32_t* context_lens,
+                                      uint32_t num_seqs, uint32_t num_q_heads,
+                                      uint32_t num_kv_heads, uint32_t head_dim,
+                                      uint32_t page_size, uint64_t num_pages, float scale,
+                                      uint32_t max_context_len, void* workspace,
+                                      size_t workspace_bytes, void* out, void* stream);
 
 #ifdef __cplusplus
 }

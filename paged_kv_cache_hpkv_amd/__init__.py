@@ -28,6 +28,8 @@ ERR_HIP = -5
 ERR_WORKSPACE = -6
 
 F32, F16, BF16 = 0, 1, 2
+KV_I8, KV_FP8_E4M3 = 3, 4
+KV_TYPES = {"i8": KV_I8, "fp8": KV_FP8_E4M3}
 INDEX_U32, INDEX_U64 = 0, 1
 
 _DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
@@ -38,7 +40,8 @@ EXPORTED = [
     "hpkv_paged_attention_decode_workspace_size", "hpkv_paged_attention_decode_partition_tokens",
     "hpkv_paged_attention_decode", "hpkv_paged_attention_decode_partitions",
     "hpkv_paged_attention_decode_reduce", "hpkv_paged_attention_decode_step",
-    "hpkv_paged_attention_prefill",
+    "hpkv_paged_attention_prefill", "hpkv_store_kvcache_quant",
+    "hpkv_paged_attention_decode_quant",
 ]
 
 
@@ -76,6 +79,11 @@ def _load():
         "hpkv_paged_attention_decode_step": ([i32, i32, vp, vp, vp, vp, vp, vp, u64, vp, vp, u32,
                                               u32, u32, u32, u32, u64, f32, u32, vp, vp, sz, vp,
                                               vp], i32),
+        "hpkv_store_kvcache_quant": ([i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64, u32,
+                                      u64, u32, u32, vp], i32),
+        "hpkv_paged_attention_decode_quant": ([i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, u64,
+                                               vp, vp, u32, u32, u32, u32, u32, u64, f32, u32,
+                                               vp, sz, vp, vp], i32),
         "hpkv_paged_attention_prefill": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, vp, u32, u64,
                                           u32, u32, u32, u32, u64, f32, u32, vp, vp], i32),
     }
@@ -275,6 +283,39 @@ def hpkv_paged_attention_prefill(q, k_cache, v_cache, block_table, seq_ptr, q_st
         _DTYPE_CODE[q.dtype], _index_type(seq_ptr), _ptr(q), _ptr(k_cache), _ptr(v_cache),
         _ptr(block_table), block_table.numel(), _ptr(seq_ptr), _ptr(q_start), _ptr(cu_q), B, nq,
         hq, hkv, d, bs, num_pages, float(scale), int(max_q_len), _ptr(out), _stream(stream, q)))
+
+
+def hpkv_store_kvcache_quant(kv_type, key, value, k_cache, v_cache, k_scale, k_zero, v_scale,
+                             v_zero, slots, stream=None):
+    """Quantizing store into uint8 pools [num_pages, bs, Hkv, d]; scales fp32 [num_pages, Hkv]."""
+    _contig(key, value, k_cache, v_cache, k_scale, k_zero, v_scale, v_zero, slots)
+    assert k_cache.dtype == v_cache.dtype == torch.uint8 and slots.dtype == torch.int64
+    assert all(x.dtype == torch.float32 for x in (k_scale, k_zero, v_scale, v_zero))
+    num_pages, bs, hkv, d = k_cache.shape
+    _check("hpkv_store_kvcache_quant", lib.hpkv_store_kvcache_quant(
+        _DTYPE_CODE[key.dtype], KV_TYPES[kv_type], _ptr(key), _ptr(value), _ptr(k_cache),
+        _ptr(v_cache), _ptr(k_scale), _ptr(k_zero), _ptr(v_scale), _ptr(v_zero), _ptr(slots),
+        slots.numel(), bs, num_pages, hkv, d, _stream(stream, k_cache)))
+
+
+def hpkv_paged_attention_decode_quant(kv_type, q, k_cache, v_cache, k_scale, k_zero, v_scale,
+                                      v_zero, block_table, seq_ptr, context_lens, scale,
+                                      max_context_len, workspace, out, stream=None):
+    """Decode over quantized uint8 pools; q/out keep their float type."""
+    _contig(q, k_cache, v_cache, k_scale, k_zero, v_scale, v_zero, block_table, seq_ptr,
+            context_lens, workspace, out)
+    assert k_cache.dtype == v_cache.dtype == torch.uint8 and q.dtype == out.dtype
+    assert context_lens.dtype == torch.int32
+    assert all(x.dtype == torch.float32 for x in (k_scale, k_zero, v_scale, v_zero))
+    B, hq, d = q.shape
+    num_pages, bs, hkv, d2 = k_cache.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hpkv_paged_attention_decode_quant", lib.hpkv_paged_attention_decode_quant(
+        _DTYPE_CODE[q.dtype], KV_TYPES[kv_type], _index_type(seq_ptr), _ptr(q), _ptr(k_cache),
+        _ptr(v_cache), _ptr(k_scale), _ptr(k_zero), _ptr(v_scale), _ptr(v_zero),
+        _ptr(block_table), block_table.numel(), _ptr(seq_ptr), _ptr(context_lens), B, hq, hkv,
+        d, bs, num_pages, float(scale), int(max_context_len), _ptr(workspace), ws_bytes,
+        _ptr(out), _stream(stream, q)))
 
 
 def alloc_workspace(q, k_cache, max_context_len):

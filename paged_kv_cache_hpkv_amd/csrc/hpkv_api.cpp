@@ -37,6 +37,13 @@ bool decode_head_dim_supported(int dtype, uint32_t head_dim) {
   return lanes >= 1 && lanes <= 64 && (lanes & (lanes - 1)) == 0;
 }
 
+// Quantized pools: 16 one-byte codes per lane chunk, a power-of-two number of
+// lanes per row.
+bool quant_head_dim_supported(uint32_t head_dim) {
+  return head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128 ||
+         head_dim == 256;
+}
+
 uint32_t max_parts_for(uint32_t max_context_len) {
   return max_context_len == 0 ? 1u : (max_context_len + kPartTokens - 1) / kPartTokens;
 }
@@ -65,8 +72,10 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
                    uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
                    uint32_t page_size, uint64_t num_pages, float scale, uint32_t max_context_len,
                    void* workspace, size_t workspace_bytes, void* out, DecodeKernelArgs* a,
-                   uint64_t* num_workgroups) {
+                   uint64_t* num_workgroups, int kv_type = -1) {
   if (!valid_dtype(dtype) || !valid_index(index_type)) return HPKV_ERR_INVALID_ARG;
+  const bool quant = kv_type >= 0;
+  if (quant && kv_type != HPKV_KV_I8 && kv_type != HPKV_KV_FP8_E4M3) return HPKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return HPKV_OK;
   if (!q || !k_cache || !v_cache || !seq_ptr || !context_lens || !out) return HPKV_ERR_NULL;
   if (block_table_len > 0 && !block_table) return HPKV_ERR_NULL;
@@ -76,7 +85,9 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
   if (num_q_heads % num_kv_heads != 0) return HPKV_ERR_INVALID_ARG;
   if (page_size > 0x7fffffffu || max_context_len > 0x7fffffffu) return HPKV_ERR_INVALID_ARG;
   if (!(scale == scale)) return HPKV_ERR_INVALID_ARG;  // NaN scale
-  if (!decode_head_dim_supported(dtype, head_dim)) return HPKV_ERR_UNSUPPORTED;
+  if (quant ? !quant_head_dim_supported(head_dim) : !decode_head_dim_supported(dtype, head_dim))
+    return HPKV_ERR_UNSUPPORTED;
+  if (quant && num_pages > 0xffffffffull / num_kv_heads) return HPKV_ERR_UNSUPPORTED;
   // q, K and V are read with 16-byte vector loads
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
        reinterpret_cast<uintptr_t>(v_cache)) % 16 != 0)
@@ -87,7 +98,8 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
     return HPKV_ERR_INVALID_ARG;
 
   const uint32_t group = num_q_heads / num_kv_heads;
-  const uint32_t gt = hpkv::heads_per_workgroup(dtype, head_dim, group);
+  const uint32_t gt = quant ? hpkv::heads_per_workgroup_quant(group)
+                            : hpkv::heads_per_workgroup(dtype, head_dim, group);
   const uint32_t max_parts = max_parts_for(max_context_len);
   const uint64_t head_tiles = uint64_t(num_kv_heads) * (group / gt);
   const uint64_t nwg = head_tiles * max_parts * num_seqs;
@@ -121,6 +133,8 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
   a->new_k = nullptr;
   a->new_v = nullptr;
   a->slots_out = nullptr;
+  a->kv_type = quant ? kv_type : dtype;
+  a->k_scale = a->k_zero = a->v_scale = a->v_zero = nullptr;
   *num_workgroups = nwg;
   return 1;  // ready to launch
 }
@@ -424,6 +438,63 @@ int hpkv_paged_attention_prefill(int dtype, int index_type, const void* q, const
   a.idx64 = index_type == HPKV_INDEX_U64;
   return hip_status(hpkv::launch_prefill(dtype, head_dim, a, uint32_t(nwg),
                                          static_cast<hipStream_t>(stream)));
+}
+
+int hpkv_store_kvcache_quant(int dtype, int kv_type, const void* key, const void* value,
+                             void* k_cache, void* v_cache, const float* k_scale,
+                             const float* k_zero, const float* v_scale, const float* v_zero,
+                             const int64_t* slots, uint64_t num_tokens, uint32_t page_size,
+                             uint64_t num_pages, uint32_t num_kv_heads, uint32_t head_dim,
+                             void* stream) {
+  if (!valid_dtype(dtype)) return HPKV_ERR_INVALID_ARG;
+  if (kv_type != HPKV_KV_I8 && kv_type != HPKV_KV_FP8_E4M3) return HPKV_ERR_INVALID_ARG;
+  if (page_size == 0 || num_pages == 0 || num_kv_heads == 0 || head_dim == 0)
+    return HPKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return HPKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !slots || !k_scale || !k_zero || !v_scale ||
+      !v_zero)
+    return HPKV_ERR_NULL;
+  if (head_dim % 8 != 0) return HPKV_ERR_UNSUPPORTED;
+  const uint64_t row_elems = uint64_t(num_kv_heads) * head_dim;
+  if (num_pages * page_size > uint64_t(INT64_MAX) / row_elems) return HPKV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value)) % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) % 8 != 0)
+    return HPKV_ERR_INVALID_ARG;
+  return hip_status(hpkv::launch_store_quant(dtype, kv_type, key, value, k_cache, v_cache,
+                                             k_scale, k_zero, v_scale, v_zero, slots, num_tokens,
+                                             page_size, num_pages, num_kv_heads, head_dim,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int hpkv_paged_attention_decode_quant(int dtype, int kv_type, int index_type, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const float* k_scale, const float* k_zero,
+                                      const float* v_scale, const float* v_zero,
+                                      const void* block_table, uint64_t block_table_len,
+                                      const void* seq_ptr, const int32_t* context_lens,
+                                      uint32_t num_seqs, uint32_t num_q_heads,
+                                      uint32_t num_kv_heads, uint32_t head_dim,
+                                      uint32_t page_size, uint64_t num_pages, float scale,
+                                      uint32_t max_context_len, void* workspace,
+                                      size_t workspace_bytes, void* out, void* stream) {
+  DecodeKernelArgs a;
+  uint64_t nwg = 0;
+  const int st = prepare_decode(dtype, index_type, q, k_cache, v_cache, block_table,
+                                block_table_len, seq_ptr, context_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, page_size, num_pages, scale,
+                                max_context_len, workspace, workspace_bytes, out, &a, &nwg,
+                                kv_type);
+  if (st <= 0) return st;
+  if (!k_scale || !k_zero || !v_scale || !v_zero) return HPKV_ERR_NULL;
+  a.k_scale = k_scale;
+  a.k_zero = k_zero;
+  a.v_scale = v_scale;
+  a.v_zero = v_zero;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hpkv::launch_decode_partitions_quant(dtype, kv_type, head_dim, a, nwg, s);
+  if (e != hipSuccess) return HPKV_ERR_HIP;
+  if (a.max_parts > 1) e = hpkv::launch_decode_reduce(dtype, reduce_args(a, head_dim), s);
+  return hip_status(e);
 }
 
 }  // extern "C"

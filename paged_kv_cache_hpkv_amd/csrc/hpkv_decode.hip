@@ -82,29 +82,6 @@ __device__ inline float dot16(const u32x4 k, const u32x4 q) {
   return a;
 }
 
-// Widens one 16-byte chunk to 16/bytes floats.
-template <int DT>
-__device__ inline void widen16(const u32x4 v, float* f) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  if constexpr (DT == kBF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(w[i] << 16);
-      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  } else if constexpr (DT == kF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f16x2 h = as_pair<f16x2>(w[i]);
-      f[2 * i] = float(h.x);
-      f[2 * i + 1] = float(h.y);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
-  }
-}
-
 template <int CTRL>
 __device__ inline float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
@@ -173,9 +150,14 @@ __device__ inline WorkItem grid_item(const DecodeKernelArgs& a) {
 // Returns false when the workgroup has nothing (more) to do; for a malformed
 // sequence it has then already written the NaN result of its NH query heads
 // h0 .. h0+NH-1.
-template <int DT, int D, int NH, int NTH>
+// No per-token work beyond the row table.
+struct NoTokenHook {
+  __device__ void operator()(uint32_t, uint64_t) const {}
+};
+
+template <int DT, int D, int NH, int NTH, class Hook = NoTokenHook>
 __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem& it,
-                                       uint64_t* s_row, Partition& w) {
+                                       uint64_t* s_row, Partition& w, Hook on_token = Hook{}) {
   const uint32_t tid = threadIdx.x;
   w.s = it.s;
   w.part = it.part;
@@ -216,6 +198,7 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
       phys = 0;
     }
     s_row[i] = ((phys * a.page_size + off) * a.num_kv_heads + w.g) * uint64_t(D);
+    on_token(i, phys);
   }
   bad = __syncthreads_or(bad_page) != 0 || bad;
 
@@ -451,6 +434,215 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
   finish_partition<DT, D, GT, NW>(a, w, s_m, s_l, s_acc);
 }
 
+
+// ---------------------------------------------------------------------------
+// Quantized pools (int8 or OCP fp8 E4M3, one byte per element). Per-block-
+// affine quantization with one block per page ("Block-Paged KV Cache",
+// section "Quantization compatibility"): the page slot of token t carries, per
+// KV head, scale and zero point for K and V, and a code c stands for
+// scale * (value(c) - zero). With the page factors of token t,
+//   q . k_t = ks_t * (q . value(kc_t) - kz_t * sum(q)),
+//   sum_t p_t v_t = sum_t (p_t vs_t) value(vc_t) - sum_t (p_t vs_t) vz_t,
+// so the inner loops work on the raw code values: one conversion and one FMA
+// per element, the scales enter once per token. int8 codes are read as
+// unsigned bytes of code + 128 (sign bit flipped), the 128 folded into the
+// zero point. Lane layout, softmax and merges are those of the kernel above
+// with 16 one-byte elements per lane chunk.
+// ---------------------------------------------------------------------------
+
+// The 16 code values of one 16-byte chunk as floats (int8: value + 128).
+template <int QT>
+__device__ inline void codes16(const u32x4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (QT == kFP8) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[i]), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[i]), true);
+      f[4 * i] = lo[0];
+      f[4 * i + 1] = lo[1];
+      f[4 * i + 2] = hi[0];
+      f[4 * i + 3] = hi[1];
+    } else {
+      const uint32_t u = w[i] ^ 0x80808080u;
+      f[4 * i] = float(u & 0xffu);
+      f[4 * i + 1] = float((u >> 8) & 0xffu);
+      f[4 * i + 2] = float((u >> 16) & 0xffu);
+      f[4 * i + 3] = float(u >> 24);
+    }
+  }
+}
+
+template <int DT, int QT, int D, int GT, class TU>
+__global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_kernel(
+    const DecodeKernelArgs a) {
+  constexpr int NW = TU::NW;
+  constexpr int NTH = NW * kWave;
+  constexpr int NLOAD = TU::NLOAD;
+  constexpr int EQ = Elem<DT>::bytes;  // bytes of a q / out element
+  constexpr int EPL = 16;              // codes per 16-byte chunk
+  constexpr int LPR = D / EPL;         // lanes per token row
+  constexpr int RPL = kWave / LPR;     // token rows per wave load
+  constexpr int TT = RPL * NLOAD;      // tokens per wave tile
+  static_assert(D % EPL == 0 && LPR <= kWave && (LPR & (LPR - 1)) == 0, "unsupported head_dim");
+  constexpr float kBias = QT == kI8 ? 128.0f : 0.0f;
+
+  __shared__ uint64_t s_row[kMaxPartTokens];
+  __shared__ float4 s_fac[kMaxPartTokens];  // (ks, kz + bias, vs, vz + bias) of each token
+  __shared__ float s_m[NW][GT];
+  __shared__ float s_l[NW][GT];
+  __shared__ float s_acc[NW][GT][D];
+
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t wave = threadIdx.x / kWave;
+  const WorkItem item = grid_item<GT>(a);
+  const uint64_t kvh = item.g;
+  auto stage_factors = [&](uint32_t i, uint64_t phys) {
+    const uint64_t f = phys * a.num_kv_heads + kvh;
+    s_fac[i] = make_float4(a.k_scale[f], a.k_zero[f] + kBias, a.v_scale[f], a.v_zero[f] + kBias);
+  };
+  Partition w;
+  if (!setup_partition<DT, D, GT, NTH>(a, item, s_row, w, stage_factors)) return;
+  const uint32_t cnt = w.cnt;
+  const uint64_t out_row0 = w.out_row0;
+
+  const uint32_t row = lane / LPR;
+  const uint32_t c = lane % LPR;
+
+  // q of the lane's 16 elements of each head, and sum(q) over the head
+  float qf[GT][EPL], qsum[GT];
+#pragma unroll
+  for (int hh = 0; hh < GT; ++hh) {
+    const char* qp = static_cast<const char*>(a.q) + ((out_row0 + hh) * D + c * EPL) * EQ;
+#pragma unroll
+    for (int h2 = 0; h2 < EPL * EQ / 16; ++h2) {
+      float t[16 / EQ];
+      widen16<DT>(*reinterpret_cast<const u32x4*>(qp + 16 * h2), t);
+#pragma unroll
+      for (int e = 0; e < 16 / EQ; ++e) qf[hh][h2 * (16 / EQ) + e] = t[e];
+    }
+    float sq = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sq += qf[hh][e];
+    qsum[hh] = row_sum<LPR>(sq);
+  }
+
+  float m[GT], l[GT], accz[GT], acc[GT][EPL];
+#pragma unroll
+  for (int hh = 0; hh < GT; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+    accz[hh] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.0f;
+  }
+
+  const char* kbase = static_cast<const char*>(a.k_cache) + c * 16;
+  const char* vbase = static_cast<const char*>(a.v_cache) + c * 16;
+
+  for (uint32_t tb = wave * TT; tb < cnt; tb += NW * TT) {
+    u32x4 kr[NLOAD], vr[NLOAD];
+    float4 fac[NLOAD];
+#pragma unroll
+    for (int k = 0; k < NLOAD; ++k) {
+      const uint32_t li = tb + k * RPL + row;
+      const uint32_t ti = li < cnt ? li : cnt - 1;
+      const uint64_t off = s_row[ti];
+      kr[k] = load16<TU::NT>(kbase + off);
+      vr[k] = load16<TU::NT>(vbase + off);
+      fac[k] = s_fac[ti];
+    }
+
+    float sc[GT][NLOAD];
+#pragma unroll
+    for (int k = 0; k < NLOAD; ++k) {
+      const bool valid = tb + k * RPL + row < cnt;
+      float kf[EPL];
+      codes16<QT>(kr[k], kf);
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh) {
+        float d0 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) d0 = fmaf(qf[hh][e], kf[e], d0);
+        const float dot = row_sum<LPR>(d0);
+        const float z = fac[k].x * fmaf(-fac[k].y, qsum[hh], dot) * a.scale_log2;
+        sc[hh][k] = valid ? z : -INFINITY;
+      }
+    }
+
+    float mu[GT];
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh) {
+      float mt = sc[hh][0];
+#pragma unroll
+      for (int k = 1; k < NLOAD; ++k) mt = fmaxf(mt, sc[hh][k]);
+      const float mn = fmaxf(m[hh], mt);
+      mu[hh] = mn == -INFINITY ? 0.0f : mn;
+      const float corr = __builtin_amdgcn_exp2f(m[hh] - mu[hh]);
+      l[hh] *= corr;
+      accz[hh] *= corr;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[hh][e] *= corr;
+      m[hh] = mn;
+    }
+#pragma unroll
+    for (int k = 0; k < NLOAD; ++k) {
+      float vf[EPL];
+      codes16<QT>(vr[k], vf);
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh) {
+        const float p = __builtin_amdgcn_exp2f(sc[hh][k] - mu[hh]);
+        l[hh] += p;
+        const float pv = p * fac[k].z;  // weight times the token's V scale
+        accz[hh] = fmaf(pv, fac[k].w, accz[hh]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pv, vf[e], acc[hh][e]);
+      }
+    }
+  }
+
+  // the zero-point term is common to every element of the head
+#pragma unroll
+  for (int hh = 0; hh < GT; ++hh) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[hh][e] -= accz[hh];
+  }
+
+  // Merge the RPL row groups of the wave (log-sum-exp rule).
+#pragma unroll
+  for (int sh = LPR; sh < kWave; sh <<= 1) {
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh) {
+      const float mo = __shfl_xor(m[hh], sh);
+      const float lo = __shfl_xor(l[hh], sh);
+      const float mn = fmaxf(m[hh], mo);
+      const float mref = mn == -INFINITY ? 0.0f : mn;
+      const float fa = __builtin_amdgcn_exp2f(m[hh] - mref);
+      const float fb = __builtin_amdgcn_exp2f(mo - mref);
+      l[hh] = l[hh] * fa + lo * fb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float ao = __shfl_xor(acc[hh][e], sh);
+        acc[hh][e] = acc[hh][e] * fa + ao * fb;
+      }
+      m[hh] = mn;
+    }
+  }
+  if (row == 0) {
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wave][hh][c * EPL + e] = acc[hh][e];
+      if (c == 0) {
+        s_m[wave][hh] = m[hh];
+        s_l[wave][hh] = l[hh];
+      }
+    }
+  }
+  __syncthreads();
+
+  finish_partition<DT, D, GT, NW>(a, w, s_m, s_l, s_acc);
+}
 
 // ---------------------------------------------------------------------------
 // One query head per KV head (MHA), head-parallel: the 16-lane row groups of a
@@ -856,7 +1048,65 @@ hipError_t launch_dt(uint32_t head_dim, const DecodeKernelArgs& a, uint64_t nwg,
   }
 }
 
+template <int DT, int QT, int D, int GT>
+hipError_t launch_quant(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
+  using TU = Tune<GT == 1 ? 8 : 4, GT >= 4 ? 4 : 8, true, 2>;
+  hipLaunchKernelGGL((decode_partition_quant_kernel<DT, QT, D, GT, TU>), dim3(uint32_t(nwg)),
+                     dim3(TU::NW * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DT, int QT, int D>
+hipError_t launch_quant_d(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
+  switch (heads_per_workgroup_quant(a.group)) {
+    case 1: return launch_quant<DT, QT, D, 1>(a, nwg, stream);
+    case 2: return launch_quant<DT, QT, D, 2>(a, nwg, stream);
+    case 4: return launch_quant<DT, QT, D, 4>(a, nwg, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT, int QT>
+hipError_t launch_quant_dt(uint32_t head_dim, const DecodeKernelArgs& a, uint64_t nwg,
+                           hipStream_t stream) {
+  switch (head_dim) {
+    case 16: return launch_quant_d<DT, QT, 16>(a, nwg, stream);
+    case 32: return launch_quant_d<DT, QT, 32>(a, nwg, stream);
+    case 64: return launch_quant_d<DT, QT, 64>(a, nwg, stream);
+    case 128: return launch_quant_d<DT, QT, 128>(a, nwg, stream);
+    case 256: return launch_quant_d<DT, QT, 256>(a, nwg, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+hipError_t launch_quant_kv(int kv_type, uint32_t head_dim, const DecodeKernelArgs& a,
+                           uint64_t nwg, hipStream_t stream) {
+  switch (kv_type) {
+    case kI8: return launch_quant_dt<DT, kI8>(head_dim, a, nwg, stream);
+    case kFP8: return launch_quant_dt<DT, kFP8>(head_dim, a, nwg, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+uint32_t heads_per_workgroup_quant(uint32_t group) {
+  if (group % 4 == 0) return 4;
+  if (group % 2 == 0) return 2;
+  return 1;
+}
+
+hipError_t launch_decode_partitions_quant(int dtype, int kv_type, uint32_t head_dim,
+                                          const DecodeKernelArgs& a, uint64_t num_workgroups,
+                                          hipStream_t stream) {
+  switch (dtype) {
+    case kF32: return launch_quant_kv<kF32>(kv_type, head_dim, a, num_workgroups, stream);
+    case kF16: return launch_quant_kv<kF16>(kv_type, head_dim, a, num_workgroups, stream);
+    case kBF16: return launch_quant_kv<kBF16>(kv_type, head_dim, a, num_workgroups, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 uint32_t heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group) {
   if (mfma_eligible(dtype, head_dim, group)) return group % 16 == 0 ? 16 : group % 8 == 0 ? 8 : 4;

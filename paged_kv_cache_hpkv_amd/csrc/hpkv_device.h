@@ -71,6 +71,29 @@ __device__ inline float widen_bits16(uint32_t b) {
   }
 }
 
+// Widens one 16-byte chunk to 16/bytes floats.
+template <int DT>
+__device__ inline void widen16(const u32x4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else if constexpr (DT == kF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2 h = as_pair<f16x2>(w[i]);
+      f[2 * i] = float(h.x);
+      f[2 * i + 1] = float(h.y);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  }
+}
+
 // Bits of fp32 x rounded to nearest even in the 16-bit storage type DT
 // (NaN stays NaN).
 template <int DT>

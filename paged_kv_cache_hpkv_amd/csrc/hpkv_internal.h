@@ -9,6 +9,8 @@ namespace hpkv {
 
 // Element storage types, same numbering as hpkv_dtype.
 enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+// Quantized pool element types, same numbering as hpkv_kv_type.
+enum : int { kI8 = 3, kFP8 = 4 };
 
 inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : 2; }
 
@@ -62,6 +64,14 @@ struct DecodeKernelArgs {
   const void* new_k;    // [B, Hkv, d] K rows of the appended tokens
   const void* new_v;    // [B, Hkv, d] V rows
   int64_t* slots_out;   // [B] pool slot each row went to (-1: none), may be null
+  // Quantized pools (kv_type kI8 / kFP8, 1-byte elements; dtype is then the
+  // type of q and out): fp32 [num_pages, Hkv] scale and zero point of each page
+  // slot and KV head, for K and for V. Null for 16/32-bit pools.
+  int kv_type;
+  const float* k_scale;
+  const float* k_zero;
+  const float* v_scale;
+  const float* v_zero;
 };
 
 struct ReduceKernelArgs {
@@ -113,6 +123,19 @@ hipError_t launch_prefill(int dtype, uint32_t head_dim, const PrefillKernelArgs&
 // Query heads served by one decode workgroup for a GQA group of `group` heads
 // (the matrix-core path takes up to 16 heads of a group at once).
 uint32_t heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group);
+// The same for quantized pools.
+uint32_t heads_per_workgroup_quant(uint32_t group);
+
+hipError_t launch_decode_partitions_quant(int dtype, int kv_type, uint32_t head_dim,
+                                          const DecodeKernelArgs& a, uint64_t num_workgroups,
+                                          hipStream_t stream);
+
+hipError_t launch_store_quant(int dtype, int kv_type, const void* key, const void* value,
+                              void* k_cache, void* v_cache, const float* k_scale,
+                              const float* k_zero, const float* v_scale, const float* v_zero,
+                              const int64_t* slots, uint64_t num_tokens, uint32_t page_size,
+                              uint64_t num_pages, uint32_t num_kv_heads, uint32_t head_dim,
+                              hipStream_t stream);
 
 hipError_t launch_slot_mapping(bool idx64, const void* block_table, uint64_t block_table_len,
                                const void* seq_ptr, uint32_t num_seqs, uint32_t page_size,

@@ -6,7 +6,7 @@
 //   slot(s, p) = block_table[seq_ptr[s] + p / page_size] * page_size + p % page_size
 // Store: every new-token row with a slot other than -1 is copied bit for bit
 // into that pool row of K and of V.
-#include "hpkv_internal.h"
+#include "hpkv_device.h"
 
 namespace hpkv {
 namespace {
@@ -87,7 +87,93 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(
   }
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// ---------------------------------------------------------------------------
+// Quantized store ("Block-Paged KV Cache", section "Quantization
+// compatibility": per-block-affine with one block per page, so each page slot
+// carries its own scale and zero point per KV head). Element x of a new row is
+// written as the code nearest to t = x / scale + zero (fp32 division rounded
+// to nearest, then the add), ties to even, saturating: int8 in [-128, 127];
+// OCP fp8 E4M3 ("e4m3fn": bias 7, largest finite 448, no infinity) at +-448.
+// NaN gives 0 (int8) or the NaN code 0x7f (fp8).
+// ---------------------------------------------------------------------------
+
+__device__ inline uint32_t quant_i8(float t) {
+  if (t != t) return 0u;
+  const float r = fminf(fmaxf(rintf(t), -128.0f), 127.0f);  // rintf: ties to even
+  return uint32_t(int32_t(r)) & 0xffu;
+}
+
+__device__ inline uint32_t quant_fp8_e4m3(float t) {
+  if (t != t) return 0x7fu;
+  const uint32_t sign = (__float_as_uint(t) >> 24) & 0x80u;
+  const float a = fabsf(t);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7eu;  // saturate
+  } else if (a < 0.015625f) {
+    code = uint32_t(rintf(a * 512.0f));  // subnormal quantum 2^-9 (8 -> 2^-6, code 0x08)
+  } else {
+    const int e = int((__float_as_uint(a) >> 23) & 0xffu) - 127;  // a in [2^e, 2^(e+1))
+    const float m = __uint_as_float(__float_as_uint(a) & 0x807fffffu | 0x3f800000u);  // [1, 2)
+    const uint32_t f = uint32_t(rintf((m - 1.0f) * 8.0f));  // 0..8, exact product, ties to even
+    code = (uint32_t(e + 7) << 3) + f;  // f == 8 carries into the exponent
+  }
+  return sign | code;
+}
+
+template <int DT, int QT>
+__device__ inline uint32_t quant_code(float t) {
+  if constexpr (QT == kI8) {
+    return quant_i8(t);
+  } else {
+    return quant_fp8_e4m3(t);
+  }
+}
+
+// One workgroup per new row; each thread turns 8 elements of one KV head of the
+// row (K and V) into 8 codes.
+template <int DT, int QT>
+__global__ __launch_bounds__(kStoreThreads) void store_quant_kernel(
+    const void* __restrict__ key, const void* __restrict__ value, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
+    const float* __restrict__ k_zero, const float* __restrict__ v_scale,
+    const float* __restrict__ v_zero, const int64_t* __restrict__ slots, uint64_t num_tokens,
+    uint32_t page_size, int64_t num_slots, uint32_t num_kv_heads, uint32_t head_dim) {
+  constexpr int EB = Elem<DT>::bytes;
+  const uint32_t groups = num_kv_heads * head_dim / 8;  // 8-element groups per row
+  for (uint64_t rowi = blockIdx.x; rowi < num_tokens; rowi += gridDim.x) {
+    const int64_t slot = slots[rowi];
+    if (slot < 0 || slot >= num_slots) continue;
+    const uint64_t page = uint64_t(slot) / page_size;
+    for (uint32_t gi = threadIdx.x; gi < groups; gi += kStoreThreads) {
+      const uint32_t g = gi * 8 / head_dim;
+      const uint64_t f = page * num_kv_heads + g;
+      const uint64_t src = (rowi * num_kv_heads * head_dim + uint64_t(gi) * 8) * EB;
+      float xk[8], xv[8];
+#pragma unroll
+      for (int h = 0; h < 8 * EB / 16; ++h) {
+        float tk[16 / EB], tv[16 / EB];
+        widen16<DT>(*reinterpret_cast<const u32x4*>(static_cast<const char*>(key) + src + 16 * h), tk);
+        widen16<DT>(*reinterpret_cast<const u32x4*>(static_cast<const char*>(value) + src + 16 * h), tv);
+#pragma unroll
+        for (int e = 0; e < 16 / EB; ++e) {
+          xk[h * (16 / EB) + e] = tk[e];
+          xv[h * (16 / EB) + e] = tv[e];
+        }
+      }
+      const float ks = k_scale[f], kz = k_zero[f], vs = v_scale[f], vz = v_zero[f];
+      uint32_t ck[2] = {0u, 0u}, cv[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ck[e / 4] |= quant_code<DT, QT>(__fdiv_rn(xk[e], ks) + kz) << (8 * (e % 4));
+        cv[e / 4] |= quant_code<DT, QT>(__fdiv_rn(xv[e], vs) + vz) << (8 * (e % 4));
+      }
+      const uint64_t dst = uint64_t(slot) * num_kv_heads * head_dim + uint64_t(gi) * 8;
+      *reinterpret_cast<uint2*>(k_cache + dst) = make_uint2(ck[0], ck[1]);
+      *reinterpret_cast<uint2*>(v_cache + dst) = make_uint2(cv[0], cv[1]);
+    }
+  }
+}
 
 }  // namespace
 
@@ -138,6 +224,54 @@ hipError_t launch_store(int chunk_bytes, const void* key, const void* value, voi
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_store_quant_dt(int kv_type, const void* key, const void* value, void* k_cache,
+                                 void* v_cache, const float* ks, const float* kz,
+                                 const float* vs, const float* vz, const int64_t* slots,
+                                 uint64_t num_tokens, uint32_t page_size, int64_t num_slots,
+                                 uint32_t num_kv_heads, uint32_t head_dim, hipStream_t stream) {
+  const uint32_t blocks = uint32_t(num_tokens < (1u << 20) ? num_tokens : (1u << 20));
+  uint8_t* kc = static_cast<uint8_t*>(k_cache);
+  uint8_t* vc = static_cast<uint8_t*>(v_cache);
+  if (kv_type == kI8) {
+    hipLaunchKernelGGL((store_quant_kernel<DT, kI8>), dim3(blocks), dim3(kStoreThreads), 0,
+                       stream, key, value, kc, vc, ks, kz, vs, vz, slots, num_tokens, page_size,
+                       num_slots, num_kv_heads, head_dim);
+  } else if (kv_type == kFP8) {
+    hipLaunchKernelGGL((store_quant_kernel<DT, kFP8>), dim3(blocks), dim3(kStoreThreads), 0,
+                       stream, key, value, kc, vc, ks, kz, vs, vz, slots, num_tokens, page_size,
+                       num_slots, num_kv_heads, head_dim);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_store_quant(int dtype, int kv_type, const void* key, const void* value,
+                              void* k_cache, void* v_cache, const float* k_scale,
+                              const float* k_zero, const float* v_scale, const float* v_zero,
+                              const int64_t* slots, uint64_t num_tokens, uint32_t page_size,
+                              uint64_t num_pages, uint32_t num_kv_heads, uint32_t head_dim,
+                              hipStream_t stream) {
+  const int64_t num_slots = int64_t(num_pages * page_size);
+  switch (dtype) {
+    case kF32:
+      return launch_store_quant_dt<kF32>(kv_type, key, value, k_cache, v_cache, k_scale, k_zero,
+                                         v_scale, v_zero, slots, num_tokens, page_size, num_slots,
+                                         num_kv_heads, head_dim, stream);
+    case kF16:
+      return launch_store_quant_dt<kF16>(kv_type, key, value, k_cache, v_cache, k_scale, k_zero,
+                                         v_scale, v_zero, slots, num_tokens, page_size, num_slots,
+                                         num_kv_heads, head_dim, stream);
+    case kBF16:
+      return launch_store_quant_dt<kBF16>(kv_type, key, value, k_cache, v_cache, k_scale, k_zero,
+                                          v_scale, v_zero, slots, num_tokens, page_size,
+                                          num_slots, num_kv_heads, head_dim, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace hpkv

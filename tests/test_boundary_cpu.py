@@ -30,7 +30,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared()
-    assert len(declared) == 13
+    assert len(declared) == 15
     out = subprocess.run(["nm", "-D", "--defined-only", hpkv.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(hpkv_\w+)", out))
@@ -170,6 +170,37 @@ def test_prefill_argument_errors():
     # nothing to do: no sequences or no query rows
     assert _prefill_call(B=0, q=None, k=None, v=None, out=None) == hpkv.OK
     assert _prefill_call(nq=0, q=None, k=None, v=None, out=None, max_q=0) == hpkv.OK
+
+
+def test_quant_argument_errors():
+    st = hpkv.lib.hpkv_store_kvcache_quant
+    good = [hpkv.BF16, hpkv.KV_FP8_E4M3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4,
+            16, 8, 2, 128, None]
+
+    def call(i, v, fn=st, base=good):
+        a = list(base)
+        a[i] = v
+        return fn(*a)
+    assert call(0, 9) == hpkv.ERR_INVALID_ARG
+    assert call(1, hpkv.BF16) == hpkv.ERR_INVALID_ARG           # not a quantized type
+    for i in range(2, 11):
+        assert call(i, None) == hpkv.ERR_NULL, i
+    assert call(12, 0) == hpkv.ERR_INVALID_ARG                  # page_size
+    assert call(15, 12) == hpkv.ERR_UNSUPPORTED                 # head_dim not a multiple of 8
+    assert call(2, ctypes.c_void_p(0x1008)) == hpkv.ERR_INVALID_ARG
+    assert call(11, 0) == hpkv.OK                               # nothing to store
+    dq = hpkv.lib.hpkv_paged_attention_decode_quant
+    base = [hpkv.BF16, hpkv.KV_I8, hpkv.INDEX_U32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, 4, FAKE, FAKE, 2, 4, 2, 128, 16, 8, 0.1, 256, None, 0, FAKE, None]
+    assert call(1, 2, dq, base) == hpkv.ERR_INVALID_ARG
+    assert call(1, 7, dq, base) == hpkv.ERR_INVALID_ARG
+    for i in (6, 7, 8, 9):
+        assert call(i, None, dq, base) == hpkv.ERR_NULL, i
+    assert call(17, 8, dq, base) == hpkv.ERR_UNSUPPORTED         # head_dim 8: half a lane chunk
+    assert call(17, 96, dq, base) == hpkv.ERR_UNSUPPORTED
+    assert call(21, 4096, dq, base) == hpkv.ERR_WORKSPACE        # several partitions need partials
+    assert call(19, 1 << 31, dq, base) == hpkv.ERR_UNSUPPORTED   # pages * heads >= 2^32
+    assert call(14, 0, dq, base) == hpkv.OK                      # empty batch
 
 
 def test_workspace_size_accounting():

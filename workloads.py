@@ -279,3 +279,41 @@ def make_prefill_queries(w: Workload, device="cpu") -> List[torch.Tensor]:
     base = 1000 * w.seed
     return [_randn((int(cu[-1]), w.num_q_heads, w.head_dim), w.torch_dtype, device,
                    base + 50 + c) for c, (_, cu) in enumerate(w.chunks)]
+
+
+@dataclass
+class QuantTensors:
+    k_codes: torch.Tensor    # uint8 [num_pages, bs, Hkv, d]
+    v_codes: torch.Tensor
+    k_scale: torch.Tensor    # fp32 [num_pages, Hkv]
+    k_zero: torch.Tensor
+    v_scale: torch.Tensor
+    v_zero: torch.Tensor
+
+
+def make_quant_tensors(w: Workload, kv_type: str, device="cpu") -> QuantTensors:
+    """Random codes for quantized pools (fp8: exponent field at most 7, i.e. magnitudes
+    below 2 and no NaN code) and per (page, KV head)
+    scales and zero points: int8 scales U(0.01, 0.04) with integer zero points in
+    [-8, 8] (N(0,1) data then spans most of the int8 range), fp8 scales U(0.25, 2)
+    with zero points U(-0.5, 0.5)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(1000 * w.seed + 77)
+    shape = (w.num_pages, w.page_size, w.num_kv_heads, w.head_dim)
+    k = torch.randint(0, 256, shape, generator=g, dtype=torch.int32).to(torch.uint8)
+    v = torch.randint(0, 256, shape, generator=g, dtype=torch.int32).to(torch.uint8)
+    if kv_type == "fp8":  # exponent field <= 7: magnitudes below 2, never a NaN code
+        k &= 0xBF
+        v &= 0xBF
+    ps = (w.num_pages, w.num_kv_heads)
+    if kv_type == "i8":
+        ks = 0.01 + 0.03 * torch.rand(ps, generator=g)
+        vs = 0.01 + 0.03 * torch.rand(ps, generator=g)
+        kz = torch.randint(-8, 9, ps, generator=g).float()
+        vz = torch.randint(-8, 9, ps, generator=g).float()
+    else:
+        ks = 0.25 + 1.75 * torch.rand(ps, generator=g)
+        vs = 0.25 + 1.75 * torch.rand(ps, generator=g)
+        kz = torch.rand(ps, generator=g) - 0.5
+        vz = torch.rand(ps, generator=g) - 0.5
+    return QuantTensors(*[x.contiguous().to(device) for x in (k, v, ks, kz, vs, vz)])
