@@ -79,6 +79,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--unfused", action="store_true",
                    help="run slot mapping, store and decode as separate calls")
+    p.add_argument("--kv", default=None, choices=["i8", "fp8"],
+                   help="decode over quantized pools (per page-slot, per KV head scales)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -196,6 +198,130 @@ def cpu_baseline(w, t, out_gpu):
                        f"sequences) once, double precision, {threads} host threads, "
                        f"{dt:.2f} s"), dict(max_abs_err=max_err, within_tolerance=ratio <= 1.0
                                             and finite)
+
+
+class QuantStep:
+    """A decode step over quantized pools: slot mapping, the quantizing store of the new
+    rows, then decode (partition + reduce)."""
+
+    def __init__(self, w, t, qt, kv):
+        import paged_kv_cache_hpkv_amd as hpkv
+        self.hpkv, self.w, self.t, self.qt, self.kv = hpkv, w, t, qt, kv
+        dev = t.q.device
+        self.bt = torch.from_numpy(w.block_table).to(dev)
+        self.sp = torch.from_numpy(w.seq_ptr).to(dev)
+        self.ctx = torch.from_numpy(w.context_lens).to(dev)
+        self.chunks = [(torch.from_numpy(s).to(dev), torch.from_numpy(c).to(dev),
+                        torch.empty(int(c[-1]), dtype=torch.int64, device=dev))
+                       for s, c in w.chunks]
+        self.drop = None if w.drop_mask is None else torch.from_numpy(w.drop_mask).to(dev)
+        self.out = torch.empty_like(t.q)
+        self.ws = hpkv.alloc_workspace(t.q, qt.k_codes, w.max_context_len)
+
+    def decode(self):
+        w, t, q = self.w, self.t, self.qt
+        self.hpkv.hpkv_paged_attention_decode_quant(
+            self.kv, t.q, q.k_codes, q.v_codes, q.k_scale, q.k_zero, q.v_scale, q.v_zero,
+            self.bt, self.sp, self.ctx, w.scale, w.max_context_len, self.ws, self.out)
+
+    def __call__(self):
+        h, w, t, q = self.hpkv, self.w, self.t, self.qt
+        for c, (start, cu, slots) in enumerate(self.chunks):
+            h.hpkv_slot_mapping(self.bt, self.sp, w.page_size, start, cu, slots)
+            if self.drop is not None and c == 0:
+                slots.masked_fill_(self.drop, -1)
+            h.hpkv_store_kvcache_quant(self.kv, t.new_keys[c], t.new_values[c], q.k_codes,
+                                       q.v_codes, q.k_scale, q.k_zero, q.v_scale, q.v_zero,
+                                       slots)
+        self.decode()
+
+
+def quant_kv_bytes(w):
+    """K+V bytes of one-byte codes a decode pass must read: sum(ctx) * 2 * Hkv * d."""
+    return int(w.context_lens.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim
+
+
+def algorithmic_quant_bytes(w):
+    """Codes, q, out, table entries, lengths and the (scale, zero) pairs of K and V of
+    every page a sequence reads (16 B per page and KV head)."""
+    b = torch.tensor([], dtype=w.torch_dtype).element_size()
+    idx = w.block_table.dtype.itemsize
+    pages = -(-w.context_lens.astype(np.int64) // w.page_size)
+    per_seq = 2 * w.num_q_heads * w.head_dim * b + 4 + 2 * idx
+    return int(quant_kv_bytes(w) + pages.sum() * (idx + 16 * w.num_kv_heads)
+               + per_seq * w.num_seqs)
+
+
+def main_quant(args, dev):
+    w = make_workload(args)
+    t = workloads.make_tensors(w, dev)
+    qt = workloads.make_quant_tensors(w, args.kv, dev)
+    step = QuantStep(w, t, qt, args.kv)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.roofline_launches)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.roofline_launches)]
+    for i in range(args.roofline_launches):
+        starts[i].record(stream)
+        step.decode()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    alg = algorithmic_quant_bytes(w)
+    achieved = alg / (dec_ms * 1e-3) / 1e9
+    kv = quant_kv_bytes(w)
+    value = kv / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC + " (quantized pools)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype + "/" + args.kv,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_TEXT.get(w.name, w.name) + f", {args.kv} KV pools",
+            "global_batch": w.num_seqs,
+            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "page_size": w.page_size, "index": w.index,
+            "sum_ctx_tokens": int(w.context_lens.astype(np.int64).sum()),
+            "kv_bytes_per_step": kv,
+            "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "sequences_per_s_per_layer": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+            "wall_s_timed_region": round(t_wall, 4),
+            "step": "slot mapping + quantizing store + quantized decode (separate launches)",
+        },
+        "roofline": {
+            "kernel": "decode_partition_quant_kernel + decode_reduce_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": alg,
+            "mean_launch_ms": round(dec_ms, 5),
+            "launches": args.roofline_launches,
+        },
+    }
+    print(json.dumps(line), flush=True)
 
 
 def calibration_copy(dev):
@@ -372,6 +498,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.path == "prefill":
         main_prefill(args, dev)
+        return
+    if args.kv:
+        main_quant(args, dev)
         return
     w = make_workload(args)
     t = workloads.make_tensors(w, dev)
