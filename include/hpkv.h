@@ -384,6 +384,82 @@ int hpkv_paged_attention_decode_quant(int dtype, int kv_type, int index_type, co
                                       uint32_t max_context_len, void* workspace,
                                       size_t workspace_bytes, void* out, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Host block manager (host; no GPU work).
+ *
+ * Owner of the physical pages that block tables name ("Paged KV Cache · AI
+ * infra interview lesson", sections "Walk the Shapes First" and "Step 5:
+ * BlockManager: ref counts and chained-hash prefix caching"; "LLM Inference
+ * Engineering & Economics", Chapter 2, sections "PagedAttention separates
+ * logical space from physical space", "Prefix reuse is another optimization"
+ * and "Deterministic evals for this layer"):
+ *   - a pool of num_pages pages of page_size tokens and a free list;
+ *   - a sequence gets a new page exactly when its length becomes
+ *     len % page_size == 1;
+ *   - every page counts the block tables that hold it and returns to the free
+ *     list only when the last one releases it;
+ *   - a full page is registered under XXH64 of its page_size token ids (int32,
+ *     little-endian) seeded with the hash of the previous page of the same
+ *     sequence (0 for the first), so the hash covers the whole prefix; a new
+ *     sequence reuses the leading full pages whose hash and tokens match (the
+ *     partially filled last page is never shared, so no writable page has two
+ *     owners);
+ *   - free pages are reused first-freed first; a freed page stays in the
+ *     prefix cache until it is handed out for other content.
+ * Not thread-safe: one caller at a time per manager.
+ * Errors: HPKV_ERR_NULL (missing pointer), HPKV_ERR_INVALID_ARG (unknown or
+ * duplicate seq_id, bad enum), HPKV_ERR_INVALID_INDEX (out of free pages; the
+ * state is unchanged), HPKV_ERR_WORKSPACE (export capacity too small; the
+ * needed length is still reported).
+ * ------------------------------------------------------------------------- */
+typedef struct hpkv_block_manager hpkv_block_manager;
+
+/* New manager over pages 0 .. num_pages-1, all free; NULL if a size is 0 or
+ * memory runs out. */
+hpkv_block_manager* hpkv_bm_create(uint64_t num_pages, uint32_t page_size);
+void hpkv_bm_destroy(hpkv_block_manager* bm);
+
+/* Admits sequence seq_id with its first num_tokens token ids (a prompt, host
+ * int32 array): reuses cached leading full pages, takes fresh pages for the
+ * rest and registers every full page. *cached_tokens (may be NULL) receives
+ * the number of prompt tokens whose pages were reused (a multiple of
+ * page_size), i.e. whose K/V need not be computed again. */
+int hpkv_bm_admit(hpkv_block_manager* bm, uint64_t seq_id, const int32_t* token_ids,
+                  uint64_t num_tokens, uint64_t* cached_tokens);
+
+/* Appends one token; takes a fresh page when the new length is
+ * len % page_size == 1. *slot (may be NULL) receives the pool slot of the new
+ * token, position len-1 (the decode slot of "Common Pitfalls"). */
+int hpkv_bm_append(hpkv_block_manager* bm, uint64_t seq_id, int32_t token_id, int64_t* slot);
+
+/* Drops the sequence's references (its pages, last first). */
+int hpkv_bm_release(hpkv_block_manager* bm, uint64_t seq_id);
+
+/* Free and allocated page counts (free + allocated = num_pages), live
+ * sequences and pages registered in the prefix cache; any pointer may be NULL. */
+int hpkv_bm_stats(const hpkv_block_manager* bm, uint64_t* free_pages, uint64_t* allocated_pages,
+                  uint64_t* live_sequences, uint64_t* cached_pages);
+
+/* Writes the CSR tables of the listed sequences, in that order, as the
+ * device entry points take them: block_table (capacity entries of
+ * index_type), seq_ptr (num_seqs + 1 entries) and context_lens (int32
+ * [num_seqs], may be NULL), all host memory. *block_table_len receives the
+ * entries needed. */
+int hpkv_bm_export(const hpkv_block_manager* bm, const uint64_t* seq_ids, uint32_t num_seqs,
+                   int index_type, void* block_table, uint64_t capacity, void* seq_ptr,
+                   int32_t* context_lens, uint64_t* block_table_len);
+
+/* Checks the accounting invariants: every page's reference count equals the
+ * number of live tables that hold it; a page is free exactly when that count
+ * is 0 and the free list holds each free page; free + allocated = pool; a
+ * partially filled (writable) page has one owner and is not shared through the
+ * prefix cache; every prefix-cache entry names a full page with that hash.
+ * HPKV_OK or HPKV_ERR_INVALID_INDEX. */
+int hpkv_bm_check(const hpkv_block_manager* bm);
+
+/* XXH64 of len bytes with the given seed (the page hash above). */
+uint64_t hpkv_xxh64(const void* data, uint64_t len, uint64_t seed);
+
 #ifdef __cplusplus
 }
 #endif

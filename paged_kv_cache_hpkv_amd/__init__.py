@@ -41,7 +41,9 @@ EXPORTED = [
     "hpkv_paged_attention_decode", "hpkv_paged_attention_decode_partitions",
     "hpkv_paged_attention_decode_reduce", "hpkv_paged_attention_decode_step",
     "hpkv_paged_attention_prefill", "hpkv_store_kvcache_quant",
-    "hpkv_paged_attention_decode_quant",
+    "hpkv_paged_attention_decode_quant", "hpkv_bm_create", "hpkv_bm_destroy", "hpkv_bm_admit",
+    "hpkv_bm_append", "hpkv_bm_release", "hpkv_bm_stats", "hpkv_bm_export", "hpkv_bm_check",
+    "hpkv_xxh64",
 ]
 
 
@@ -84,6 +86,15 @@ def _load():
         "hpkv_paged_attention_decode_quant": ([i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, u64,
                                                vp, vp, u32, u32, u32, u32, u32, u64, f32, u32,
                                                vp, sz, vp, vp], i32),
+        "hpkv_bm_create": ([u64, u32], vp),
+        "hpkv_bm_destroy": ([vp], None),
+        "hpkv_bm_admit": ([vp, u64, vp, u64, vp], i32),
+        "hpkv_bm_append": ([vp, u64, ctypes.c_int32, vp], i32),
+        "hpkv_bm_release": ([vp, u64], i32),
+        "hpkv_bm_stats": ([vp, vp, vp, vp, vp], i32),
+        "hpkv_bm_export": ([vp, vp, u32, i32, vp, u64, vp, vp, vp], i32),
+        "hpkv_bm_check": ([vp], i32),
+        "hpkv_xxh64": ([vp, u64, u64], u64),
         "hpkv_paged_attention_prefill": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, vp, u32, u64,
                                           u32, u32, u32, u32, u64, f32, u32, vp, vp], i32),
     }
@@ -316,6 +327,80 @@ def hpkv_paged_attention_decode_quant(kv_type, q, k_cache, v_cache, k_scale, k_z
         _ptr(block_table), block_table.numel(), _ptr(seq_ptr), _ptr(context_lens), B, hq, hkv,
         d, bs, num_pages, float(scale), int(max_context_len), _ptr(workspace), ws_bytes,
         _ptr(out), _stream(stream, q)))
+
+
+# ------------------------------------------------------------ host block manager
+
+class BlockManager:
+    """Host page allocator with reference counts and chained-hash prefix reuse
+    (hpkv_bm_* in include/hpkv.h). Every method forwards to the library."""
+
+    def __init__(self, num_pages, page_size):
+        self._destroy = lib.hpkv_bm_destroy  # kept: module globals may be gone at exit
+        self._h = lib.hpkv_bm_create(int(num_pages), int(page_size))
+        if not self._h:
+            raise HpkvError("hpkv_bm_create", ERR_INVALID_ARG)
+        self.num_pages, self.page_size = int(num_pages), int(page_size)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def admit(self, seq_id, token_ids):
+        """Admits a sequence with its prompt; returns the prompt tokens served from cache."""
+        import numpy as np
+        t = np.ascontiguousarray(token_ids, dtype=np.int32)
+        cached = ctypes.c_uint64(0)
+        _check("hpkv_bm_admit", lib.hpkv_bm_admit(self._h, int(seq_id), _np_ptr(t), t.size,
+                                                  ctypes.byref(cached)))
+        return cached.value
+
+    def append(self, seq_id, token_id):
+        """Appends one token; returns its pool slot."""
+        slot = ctypes.c_int64(0)
+        _check("hpkv_bm_append", lib.hpkv_bm_append(self._h, int(seq_id), int(token_id),
+                                                    ctypes.byref(slot)))
+        return slot.value
+
+    def release(self, seq_id):
+        _check("hpkv_bm_release", lib.hpkv_bm_release(self._h, int(seq_id)))
+
+    def stats(self):
+        v = [ctypes.c_uint64(0) for _ in range(4)]
+        _check("hpkv_bm_stats", lib.hpkv_bm_stats(self._h, *[ctypes.byref(x) for x in v]))
+        return dict(zip(("free", "allocated", "sequences", "cached"), (x.value for x in v)))
+
+    def export(self, seq_ids, index="u32"):
+        """(block_table, seq_ptr, context_lens) numpy arrays for the listed sequences."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
+        it = INDEX_U32 if index == "u32" else INDEX_U64
+        dt = np.uint32 if index == "u32" else np.uint64
+        sp = np.zeros(len(ids) + 1, dtype=dt)
+        ctx = np.zeros(len(ids), dtype=np.int32)
+        need = ctypes.c_uint64(0)
+        st = lib.hpkv_bm_export(self._h, _np_ptr(ids), len(ids), it, None, 0, _np_ptr(sp),
+                                _np_ptr(ctx), ctypes.byref(need))
+        if st not in (OK, ERR_WORKSPACE):
+            raise HpkvError("hpkv_bm_export", st)
+        bt = np.zeros(max(need.value, 1), dtype=dt)
+        _check("hpkv_bm_export", lib.hpkv_bm_export(self._h, _np_ptr(ids), len(ids), it,
+                                                    _np_ptr(bt), bt.size, _np_ptr(sp),
+                                                    _np_ptr(ctx), ctypes.byref(need)))
+        return bt[:need.value], sp, ctx
+
+    def check(self):
+        """Status of the accounting-invariant check (OK or ERR_INVALID_INDEX)."""
+        return lib.hpkv_bm_check(self._h)
+
+
+def xxh64(data: bytes, seed: int = 0) -> int:
+    buf = ctypes.create_string_buffer(bytes(data), len(data))
+    return int(lib.hpkv_xxh64(buf, len(data), int(seed)))
 
 
 def alloc_workspace(q, k_cache, max_context_len):

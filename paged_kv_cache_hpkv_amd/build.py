@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhpkv.so")
-SOURCES = ["hpkv_api.cpp", "hpkv_slots_store.hip", "hpkv_decode.hip", "hpkv_prefill.hip"]
+SOURCES = ["hpkv_api.cpp", "hpkv_slots_store.hip", "hpkv_decode.hip", "hpkv_prefill.hip",
+           "hpkv_blocks.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

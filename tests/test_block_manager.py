@@ -1,0 +1,150 @@
+"""Host block manager (hpkv_bm_*): page growth, reference counts, chained-hash
+prefix reuse and the accounting invariants.
+
+"Paged KV Cache · AI infra interview lesson": a new page exactly when
+len % page_size == 1 ("Walk the Shapes First"), the decode slot at position
+len-1 ("Common Pitfalls"), ref counts and chained-hash prefix caching
+("Step 5"). "LLM Inference Engineering & Economics", Chapter 2, "Deterministic
+evals for this layer": free + allocated = pool, allocated >= pages referenced
+by live tables, no two writable logical pages alias. Slots are checked against
+the oracle's slot mapping over the exported tables; the hash against the
+xxhash package.
+"""
+import numpy as np
+import pytest
+import xxhash
+
+import oracle
+import paged_kv_cache_hpkv_amd as hpkv
+
+
+def test_xxh64_matches_xxhash_package():
+    rng = np.random.default_rng(0)
+    for n in list(range(0, 70)) + [127, 128, 1000]:
+        data = rng.integers(0, 256, n, dtype=np.uint8).tobytes()
+        for seed in (0, 1, int(rng.integers(0, 2 ** 63)), 2 ** 64 - 1):
+            assert hpkv.xxh64(data, seed) == xxhash.xxh64(data, seed=seed).intdigest()
+
+
+def _slot_by_oracle(bm, sid, pos):
+    bt, sp, _ = bm.export([sid])
+    return int(oracle.slot_mapping(bt, sp, bm.page_size, np.array([pos], np.int32),
+                                   np.array([0, 1], np.int64))[0])
+
+
+@pytest.mark.parametrize("bs", [1, 4, 16])
+def test_growth_rule_and_decode_slot(bs):
+    bm = hpkv.BlockManager(64, bs)
+    bm.admit(7, [])
+    for n in range(1, 3 * bs + 2):  # n = length after the append
+        before = bm.stats()["allocated"]
+        slot = bm.append(7, 100 + n)
+        grew = bm.stats()["allocated"] - before
+        assert grew == (1 if (bs == 1 or n % bs == 1) else 0), n
+        assert slot == _slot_by_oracle(bm, 7, n - 1)
+        _, _, ctx = bm.export([7])
+        assert ctx[0] == n
+        assert bm.check() == hpkv.OK
+    # five tokens at four per page need two pages ("Why It Matters")
+    bm2 = hpkv.BlockManager(8, 4)
+    bm2.admit(1, [1, 2, 3, 4, 5])
+    assert bm2.stats()["allocated"] == 2
+
+
+def test_prefix_sharing_refcounts_and_release():
+    bm = hpkv.BlockManager(16, 4)
+    prompt = list(range(10))                       # 2 full pages + 2 tokens
+    assert bm.admit(1, prompt) == 0
+    assert bm.admit(2, prompt) == 8                # both full pages reused
+    bt, sp, ctx = bm.export([1, 2])
+    t1, t2 = bt[sp[0]:sp[1]].tolist(), bt[sp[1]:sp[2]].tolist()
+    assert t1[:2] == t2[:2] and t1[2] != t2[2]     # the partial last page stays private
+    assert bm.stats()["allocated"] == 4 and bm.check() == hpkv.OK
+    assert bm.admit(3, prompt[:4] + [99] * 6) == 4  # diverges in the second page
+    bm.release(1)
+    assert bm.stats()["allocated"] == 3 + 2        # shared pages live on for 2 and 3
+    assert bm.check() == hpkv.OK
+    bm.release(2)
+    bm.release(3)
+    assert bm.stats() == {"free": 16, "allocated": 0, "sequences": 0,
+                          "cached": bm.stats()["cached"]}
+    assert bm.check() == hpkv.OK
+    # freed pages stay in the prefix cache: the same prompt revives them
+    assert bm.admit(4, prompt) == 8
+    assert bm.export([4])[0][:2].tolist() == t1[:2]
+    assert bm.check() == hpkv.OK
+
+
+def test_appended_pages_become_shareable_once_full():
+    bm = hpkv.BlockManager(16, 4)
+    bm.admit(1, [5, 6, 7])
+    bm.append(1, 8)                                # fills page 0
+    assert bm.admit(2, [5, 6, 7, 8, 9]) == 4
+    assert bm.check() == hpkv.OK
+
+
+def test_cached_pages_are_handed_out_when_needed():
+    bm = hpkv.BlockManager(4, 4)
+    bm.admit(1, list(range(8)))
+    bm.release(1)                                  # 2 cached free pages
+    bm.admit(2, list(range(100, 116)))             # needs all 4 pages: cache evicted
+    bm.release(2)
+    assert bm.admit(3, list(range(8))) == 0
+    assert bm.check() == hpkv.OK
+
+
+def test_exhaustion_leaves_state_unchanged():
+    bm = hpkv.BlockManager(5, 4)
+    bm.admit(1, list(range(12)))
+    snap = bm.stats()
+    with pytest.raises(hpkv.HpkvError) as e:
+        bm.admit(2, list(range(50, 62)))
+    assert e.value.status == hpkv.ERR_INVALID_INDEX
+    assert bm.stats() == snap and bm.check() == hpkv.OK
+    bm.admit(3, list(range(3)))                    # one page left
+    with pytest.raises(hpkv.HpkvError):
+        for t in range(3, 9):                      # needs a 7th page at length 5
+            bm.append(3, t)
+    assert bm.check() == hpkv.OK
+    with pytest.raises(hpkv.HpkvError):
+        bm.admit(1, [1])                           # duplicate id
+    with pytest.raises(hpkv.HpkvError):
+        bm.release(42)                             # unknown id
+
+
+def test_randomized_lifecycle_keeps_invariants():
+    rng = np.random.default_rng(3)
+    bs, num_pages = 4, 40
+    bm = hpkv.BlockManager(num_pages, bs)
+    prompts = [list(rng.integers(0, 50, int(n))) for n in rng.integers(1, 20, 6)]
+    live, next_id = {}, 0
+    for step in range(600):
+        op = rng.integers(0, 3)
+        try:
+            if op == 0 or not live:
+                p = prompts[int(rng.integers(0, len(prompts)))]
+                p = p[:int(rng.integers(1, len(p) + 1))]
+                bm.admit(next_id, p)
+                live[next_id] = len(p)
+                next_id += 1
+            elif op == 1:
+                sid = list(live)[int(rng.integers(0, len(live)))]
+                slot = bm.append(sid, int(rng.integers(0, 50)))
+                live[sid] += 1
+                assert slot == _slot_by_oracle(bm, sid, live[sid] - 1)
+            else:
+                sid = list(live)[int(rng.integers(0, len(live)))]
+                bm.release(sid)
+                del live[sid]
+        except hpkv.HpkvError as e:
+            assert e.status == hpkv.ERR_INVALID_INDEX  # out of pages: allowed, state intact
+        assert bm.check() == hpkv.OK, step
+        st = bm.stats()
+        assert st["free"] + st["allocated"] == num_pages
+        if live:
+            ids = sorted(live)
+            bt, sp, ctx = bm.export(ids)
+            assert ctx.tolist() == [live[i] for i in ids]
+            assert len(set(bt.tolist())) <= st["allocated"]  # allocated >= referenced
+            assert oracle.validate_index_buffers(sp, bt, num_pages, ctx, bs) == oracle.OK
+            assert hpkv.hpkv_validate_index_buffers(sp, bt, num_pages, ctx, bs) == hpkv.OK
