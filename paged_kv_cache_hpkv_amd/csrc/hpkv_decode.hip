@@ -1050,7 +1050,10 @@ hipError_t launch_dt(uint32_t head_dim, const DecodeKernelArgs& a, uint64_t nwg,
 
 template <int DT, int QT, int D, int GT>
 hipError_t launch_quant(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
-  using TU = Tune<GT == 1 ? 8 : 4, GT >= 4 ? 4 : 8, true, 2>;
+  // Two-wave workgroups keep the most waves resident (the loop is latency-bound:
+  // converting and FMA-ing one-byte codes leaves no loads in flight for long);
+  // 4-head tiles hold 64 q floats per lane, so they load two rows per lane.
+  using TU = Tune<2, GT >= 4 ? 2 : 8, true, 2>;
   hipLaunchKernelGGL((decode_partition_quant_kernel<DT, QT, D, GT, TU>), dim3(uint32_t(nwg)),
                      dim3(TU::NW * kWave), 0, stream, a);
   return hipGetLastError();
