@@ -98,7 +98,7 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
     return HPKV_ERR_INVALID_ARG;
 
   const uint32_t group = num_q_heads / num_kv_heads;
-  const uint32_t gt = quant ? hpkv::heads_per_workgroup_quant(group)
+  const uint32_t gt = quant ? hpkv::heads_per_workgroup_quant(dtype, head_dim, group)
                             : hpkv::heads_per_workgroup(dtype, head_dim, group);
   const uint32_t max_parts = max_parts_for(max_context_len);
   const uint64_t head_tiles = uint64_t(num_kv_heads) * (group / gt);

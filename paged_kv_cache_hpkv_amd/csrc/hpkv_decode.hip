@@ -930,6 +930,270 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_k
   finish_partition<DT, D, GT, NW>(a, w, s_m, s_l, s_acc);
 }
 
+// ---------------------------------------------------------------------------
+// Quantized pools, GQA groups of 4 or more query heads, 16-bit q: the matrix-
+// core kernel above on one-byte codes. Each lane loads 16 codes of a row
+// (half the bytes per token of a 16-bit pool) and writes them to the wave's
+// LDS tile as exact 16-bit values (int8 codes as code + 128 in 0..255, E4M3
+// values; both are exact in bf16 and in f16), so the two products are those
+// of the 16-bit kernel over raw code values. The page factors of token t enter
+// around them:
+//   score = ks_t * (q . value_t - kz_t * sum(q)),   weight' = p_t * vs_t,
+//   out   = (sum_t weight'_t value_t - sum_t weight'_t vz_t) / sum_t p_t,
+// with the bias of int8 codes folded into the zero points. V^T is read with the
+// transposing LDS read ds_read_b64_tr_b16 (lanes 4r..4r+3 of each 16-lane group
+// fetch row r of a 4x16 block; lane i receives column i), from rows padded by
+// 32 bytes so those 8-byte reads fall on distinct banks.
+// ---------------------------------------------------------------------------
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ inline uint2 lds_read_tr16(const char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((lds_char*)(const_cast<char*>(p))));
+  uint2 r;
+  __builtin_memcpy(&r, &v, sizeof(r));
+  return r;
+}
+
+// Two exact code values (fp32) as a packed 16-bit pair of the q type.
+template <int DT>
+__device__ inline uint32_t pack_exact16(float x, float y) {
+  if constexpr (DT == kBF16) {  // at most 8 significant bits: the upper halves are exact
+    return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
+  } else {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(x, y);  // exact: no rounding happens
+    uint32_t r;
+    __builtin_memcpy(&r, &h, 4);
+    return r;
+  }
+}
+
+// 16 codes (one 16-byte chunk) as 16 exact 16-bit values: `lo` holds elements
+// 0..7, `hi` elements 8..15.
+template <int DT, int QT>
+__device__ inline void codes16_to_bits16(const u32x4 c, u32x4& lo, u32x4& hi) {
+  if constexpr (QT == kFP8) {  // packed scaled conversion with scale 1: exact
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    uint32_t r[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == kBF16) {
+        const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+        const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+        __builtin_memcpy(&r[2 * i], &a, 4);
+        __builtin_memcpy(&r[2 * i + 1], &b, 4);
+      } else {
+        const auto a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
+        const auto b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
+        __builtin_memcpy(&r[2 * i], &a, 4);
+        __builtin_memcpy(&r[2 * i + 1], &b, 4);
+      }
+    }
+    lo = u32x4{r[0], r[1], r[2], r[3]};
+    hi = u32x4{r[4], r[5], r[6], r[7]};
+    return;
+  }
+  float f[16];
+  codes16<QT>(c, f);
+  lo = u32x4{pack_exact16<DT>(f[0], f[1]), pack_exact16<DT>(f[2], f[3]),
+             pack_exact16<DT>(f[4], f[5]), pack_exact16<DT>(f[6], f[7])};
+  hi = u32x4{pack_exact16<DT>(f[8], f[9]), pack_exact16<DT>(f[10], f[11]),
+             pack_exact16<DT>(f[12], f[13]), pack_exact16<DT>(f[14], f[15])};
+}
+
+template <int DT, int QT, int D, int GT, class TU>
+__global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_quant_kernel(
+    const DecodeKernelArgs a) {
+  static_assert(DT != kF32 && D % 32 == 0 && D <= 128 && GT <= 16, "unsupported shape");
+  constexpr int NW = TU::NW;
+  constexpr int NTH = NW * kWave;
+  constexpr int LPR = D / 16;       // lanes per row: 16 codes per lane
+  constexpr int RPL = kWave / LPR;  // rows per wave load
+  constexpr int TT = 32;            // tokens per tile
+  constexpr int NL = TT / RPL;      // wave loads per tile, for K and for V
+  constexpr int KROW = D * 2 + 16;  // LDS bytes per K row (16-byte lane reads)
+  constexpr int VROW = D * 2 + 32;  // LDS bytes per V row (transposing 8-byte reads)
+  constexpr int KS = D / 32;
+  constexpr int NB = D / 16;
+  constexpr float kBias = QT == kI8 ? 128.0f : 0.0f;
+
+  __shared__ uint64_t s_row[kMaxPartTokens];
+  __shared__ float4 s_fac[kMaxPartTokens];  // (ks, kz + bias, vs, vz + bias) of each token
+  __shared__ __attribute__((aligned(16))) char s_tile[NW][TT * (KROW + VROW)];
+  __shared__ float s_m[NW][GT];
+  __shared__ float s_l[NW][GT];
+  static_assert(sizeof(float) * GT * D <= TT * (KROW + VROW), "merge buffer must fit the tiles");
+
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t wave = threadIdx.x / kWave;
+  const WorkItem item = grid_item<GT>(a);
+  const uint64_t kvh = item.g;
+  auto stage_factors = [&](uint32_t i, uint64_t phys) {
+    const uint64_t f = phys * a.num_kv_heads + kvh;
+    s_fac[i] = make_float4(a.k_scale[f], a.k_zero[f] + kBias, a.v_scale[f], a.v_zero[f] + kBias);
+  };
+  Partition w;
+  if (!setup_partition<DT, D, GT, NTH>(a, item, s_row, w, stage_factors)) return;
+  const uint32_t cnt = w.cnt;
+
+  const uint32_t q4 = lane / 16;
+  const uint32_t col = lane % 16;
+
+  u32x4 qop[KS];
+  float qpart = 0.0f;  // this lane's share of sum(q) of head `col`
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qop[ks] = u32x4{0, 0, 0, 0};
+    if (col < GT) {
+      const char* qp = static_cast<const char*>(a.q) + ((w.out_row0 + col) * D + 32 * ks + 8 * q4) * 2;
+      qop[ks] = *reinterpret_cast<const u32x4*>(qp);
+      float f[8];
+      widen16<DT>(qop[ks], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qpart += f[e];
+    }
+  }
+  qpart += __shfl_xor(qpart, 16);
+  const float qsum = qpart + __shfl_xor(qpart, 32);
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY, l = 0.0f, accz = 0.0f;
+
+  const uint32_t lr = lane / LPR, lc = lane % LPR;  // row-major load: row, 16-code chunk
+  char* kt = s_tile[wave];
+  char* vt = s_tile[wave] + TT * KROW;
+  const char* kbase = static_cast<const char*>(a.k_cache) + lc * 16;
+  const char* vbase = static_cast<const char*>(a.v_cache) + lc * 16;
+
+  uint32_t tb = wave * TT;
+  if (tb < cnt) {
+    u32x4 kr[NL], vr[NL];
+    auto load_tile = [&](uint32_t t0) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const uint32_t li = t0 + i * RPL + lr;
+        const uint64_t off = s_row[li < cnt ? li : cnt - 1];  // one byte per element
+        kr[i] = load16<TU::NT>(kbase + off);
+        vr[i] = load16<TU::NT>(vbase + off);
+      }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const uint32_t r = i * RPL + lr;
+        u32x4 lo, hi;
+        codes16_to_bits16<DT, QT>(kr[i], lo, hi);
+        *reinterpret_cast<u32x4*>(kt + r * KROW + lc * 32) = lo;
+        *reinterpret_cast<u32x4*>(kt + r * KROW + lc * 32 + 16) = hi;
+        codes16_to_bits16<DT, QT>(vr[i], lo, hi);
+        *reinterpret_cast<u32x4*>(vt + r * VROW + lc * 32) = lo;
+        *reinterpret_cast<u32x4*>(vt + r * VROW + lc * 32 + 16) = hi;
+      }
+    };
+    load_tile(tb);
+    store_tile();
+    while (true) {
+      const uint32_t tn = tb + NW * TT;
+      const bool has_next = tn < cnt;
+      if (has_next) load_tile(tn);
+
+      f32x4 sacc[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        sacc[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 kop =
+              *reinterpret_cast<const u32x4*>(kt + (16 * g + col) * KROW + (32 * ks + 8 * q4) * 2);
+          sacc[g] = mfma_16x16x32<DT>(kop, qop[ks], sacc[g]);
+        }
+      }
+      float z[8];
+      float4 fac[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t t = tb + 16 * (j / 4) + 4 * q4 + (j % 4);
+        fac[j] = s_fac[t < cnt ? t : cnt - 1];
+        const float zz = fac[j].x * fmaf(-fac[j].y, qsum, sacc[j / 4][j % 4]) * a.scale_log2;
+        z[j] = t < cnt ? zz : -INFINITY;
+      }
+      float mt = z[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mt = fmaxf(mt, z[j]);
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m, mt);
+      const float mu = mn == -INFINITY ? 0.0f : mn;
+      const float corr = __builtin_amdgcn_exp2f(m - mu);
+      m = mn;
+      l *= corr;
+      accz *= corr;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) acc[n] *= corr;
+
+      uint32_t pw[4];
+      float psum = 0.0f, zsum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(z[j] - mu);
+        const float p1 = __builtin_amdgcn_exp2f(z[j + 1] - mu);
+        const uint32_t b0 = round16<DT>(p0 * fac[j].z);
+        const uint32_t b1 = round16<DT>(p1 * fac[j + 1].z);
+        psum += p0 + p1;
+        zsum = fmaf(widen_bits16<DT>(b0), fac[j].w, zsum);
+        zsum = fmaf(widen_bits16<DT>(b1), fac[j + 1].w, zsum);
+        pw[j / 2] = b0 | (b1 << 16);
+      }
+      if (col >= GT) {
+        pw[0] = pw[1] = pw[2] = pw[3] = 0u;
+        psum = zsum = 0.0f;
+      }
+      l += psum;
+      accz += zsum;
+      const u32x4 pop = u32x4{pw[0], pw[1], pw[2], pw[3]};
+
+      // V^T: lane (q4, col) fetches row 4*q4 + col/4 (and 16 + that), columns
+      // 16n + 4*(col%4) .. +3, and receives column 16n + col
+      const char* vrow0 = vt + (4 * q4 + col / 4) * VROW + 8 * (col % 4);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const uint2 lo = lds_read_tr16(vrow0 + 32 * n);
+        const uint2 hi = lds_read_tr16(vrow0 + 16 * VROW + 32 * n);
+        acc[n] = mfma_16x16x32<DT>(u32x4{lo.x, lo.y, hi.x, hi.y}, pop, acc[n]);
+      }
+      if (!has_next) break;
+      store_tile();
+      tb = tn;
+    }
+  }
+
+  // the four lane quarters hold disjoint tokens of each head: add their sums
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  accz += __shfl_xor(accz, 16);
+  accz += __shfl_xor(accz, 32);
+  __syncthreads();  // every wave is done with its tile before the tiles become merge space
+  float(*s_acc)[GT][D] = reinterpret_cast<float(*)[GT][D]>(&s_tile[0][0]);
+  if (col < GT) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_acc[wave][col][16 * n + 4 * q4 + r] = acc[n][r] - accz;
+    }
+    if (q4 == 0) {
+      s_m[wave][col] = m;
+      s_l[wave][col] = l;
+    }
+  }
+  __syncthreads();
+  finish_partition<DT, D, GT, NW>(a, w, s_m, s_l, s_acc);
+}
+
 // One wave per (sequence, query head) with more than one partition: merges the
 // partitions with the log-sum-exp rule, normalises and rounds to dtype. Lane j
 // reads partition j's (max, sum) so the partials are fetched in parallel; the
@@ -1059,9 +1323,32 @@ hipError_t launch_quant(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t str
   return hipGetLastError();
 }
 
+template <int DT, int QT, int D, int GT>
+hipError_t launch_quant_mfma(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
+  using TU = Tune<2, 0, true, 2>;
+  hipLaunchKernelGGL((decode_partition_mfma_quant_kernel<DT, QT, D, GT, TU>),
+                     dim3(uint32_t(nwg)), dim3(TU::NW * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+bool mfma_quant_eligible(int dtype, uint32_t head_dim, uint32_t group) {
+  return dtype != kF32 && (head_dim == 32 || head_dim == 64 || head_dim == 128) &&
+         group % 4 == 0;
+}
+
 template <int DT, int QT, int D>
 hipError_t launch_quant_d(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
-  switch (heads_per_workgroup_quant(a.group)) {
+  if constexpr (DT != kF32 && D >= 32 && D <= 128) {
+    if (mfma_quant_eligible(DT, D, a.group)) {
+      switch (heads_per_workgroup_quant(DT, D, a.group)) {
+        case 4: return launch_quant_mfma<DT, QT, D, 4>(a, nwg, stream);
+        case 8: return launch_quant_mfma<DT, QT, D, 8>(a, nwg, stream);
+        case 16: return launch_quant_mfma<DT, QT, D, 16>(a, nwg, stream);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
+  switch (heads_per_workgroup_quant(DT, D, a.group)) {
     case 1: return launch_quant<DT, QT, D, 1>(a, nwg, stream);
     case 2: return launch_quant<DT, QT, D, 2>(a, nwg, stream);
     case 4: return launch_quant<DT, QT, D, 4>(a, nwg, stream);
@@ -1094,7 +1381,9 @@ hipError_t launch_quant_kv(int kv_type, uint32_t head_dim, const DecodeKernelArg
 
 }  // namespace
 
-uint32_t heads_per_workgroup_quant(uint32_t group) {
+uint32_t heads_per_workgroup_quant(int dtype, uint32_t head_dim, uint32_t group) {
+  if (mfma_quant_eligible(dtype, head_dim, group))
+    return group % 16 == 0 ? 16 : group % 8 == 0 ? 8 : 4;
   if (group % 4 == 0) return 4;
   if (group % 2 == 0) return 2;
   return 1;

@@ -124,7 +124,7 @@ hipError_t launch_prefill(int dtype, uint32_t head_dim, const PrefillKernelArgs&
 // (the matrix-core path takes up to 16 heads of a group at once).
 uint32_t heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group);
 // The same for quantized pools.
-uint32_t heads_per_workgroup_quant(uint32_t group);
+uint32_t heads_per_workgroup_quant(int dtype, uint32_t head_dim, uint32_t group);
 
 hipError_t launch_decode_partitions_quant(int dtype, int kv_type, uint32_t head_dim,
                                           const DecodeKernelArgs& a, uint64_t num_workgroups,

@@ -98,10 +98,17 @@ def test_quant_full_workloads(wl, kv):
 @pytest.mark.parametrize("kv", ["i8", "fp8"])
 def test_quant_other_shapes(kv):
     base = workloads.gqa(batch=24)
-    for hq, hkv, d in [(8, 8, 64), (16, 8, 32), (32, 4, 256), (12, 4, 128)]:
+    # groups of 1, 2, 3 (VALU path), 8 at d=256 (VALU), 8 and 16 at d=64/32 (matrix cores)
+    for hq, hkv, d in [(8, 8, 64), (16, 8, 32), (32, 4, 256), (12, 4, 128), (32, 4, 64),
+                       (32, 2, 32)]:
         w = workloads.Workload(**{**base.__dict__, "num_q_heads": hq, "num_kv_heads": hkv,
                                   "head_dim": d, "scale": d ** -0.5})
         _step(w, kv)
+
+
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
+def test_quant_gqa_f16(kv):
+    _step(workloads.gqa(batch=48).with_dtype("f16"), kv)
 
 
 def test_quant_u64_and_single_partition():
