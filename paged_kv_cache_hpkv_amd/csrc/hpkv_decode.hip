@@ -760,10 +760,27 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_hp_ker
 //   * P.V: O^T[d][head] = V^T P^T. The contraction index k = 8(l/16)+j is
 //     mapped to token 16(j/4)+4(l/16)+(j%4), which is exactly where the scores
 //     already sit, so P needs no data movement; V^T is gathered from LDS in
-//     the same token order. P is rounded to the input type for the matrix
+//     the same token order (by the transposing LDS read below, from V rows
+//     padded by 32 bytes). P is rounded to the input type for the matrix
 //     cores and the softmax denominator sums the rounded weights.
 // The next tile's loads are issued before the current tile is computed.
 // ---------------------------------------------------------------------------
+
+// ds_read_b64_tr_b16 (gfx950 transposing LDS read): within each group of 16
+// lanes, lanes 4r..4r+3 fetch the 16 elements of row r of a 4x16 block (8 bytes
+// each) and lane i receives column i of the four rows. Returns this lane's four
+// 16-bit results packed in two words; p must be 8-byte aligned.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ inline uint2 lds_read_tr16(const char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((lds_char*)(const_cast<char*>(p))));
+  uint2 r;
+  __builtin_memcpy(&r, &v, sizeof(r));
+  return r;
+}
 
 template <int DT, int D, int GT, class TU>
 __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_kernel(
@@ -776,15 +793,16 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_k
   constexpr int RPL = kWave / LPR; // rows per wave load
   constexpr int TT = 32;           // tokens per tile
   constexpr int NL = TT / RPL;     // wave loads per tile, for K and for V
-  constexpr int ROWB = D * 2 + 16; // LDS bytes per tile row (16-byte pad)
+  constexpr int KROW = D * 2 + 16; // LDS bytes per K row (16-byte lane reads: distinct banks)
+  constexpr int VROW = D * 2 + 32; // LDS bytes per V row (transposing 8-byte reads likewise)
   constexpr int KS = D / 32;       // score MFMAs per 16 tokens (d steps)
   constexpr int NB = D / 16;       // P.V MFMAs per tile (16-column blocks of d)
 
   __shared__ uint64_t s_row[kMaxPartTokens];
-  __shared__ __attribute__((aligned(16))) char s_tile[NW][2][TT * ROWB];
+  __shared__ __attribute__((aligned(16))) char s_tile[NW][TT * (KROW + VROW)];
   __shared__ float s_m[NW][GT];
   __shared__ float s_l[NW][GT];
-  static_assert(sizeof(float) * GT * D <= 2 * TT * ROWB, "merge buffer must fit the tiles");
+  static_assert(sizeof(float) * GT * D <= TT * (KROW + VROW), "merge buffer must fit the tiles");
 
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t wave = threadIdx.x / kWave;
@@ -811,8 +829,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_k
   float m = -INFINITY, l = 0.0f;  // running max (base 2) and weight sum of head `col`
 
   const uint32_t lr = lane / LPR, lc = lane % LPR;  // row-major load: row, 16-byte chunk
-  char* kt = s_tile[wave][0];
-  char* vt = s_tile[wave][1];
+  char* kt = s_tile[wave];
+  char* vt = s_tile[wave] + TT * KROW;
   const char* kbase = static_cast<const char*>(a.k_cache) + lc * 16;
   const char* vbase = static_cast<const char*>(a.v_cache) + lc * 16;
 
@@ -832,8 +850,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_k
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const uint32_t r = i * RPL + lr;
-        *reinterpret_cast<u32x4*>(kt + r * ROWB + lc * 16) = kr[i];
-        *reinterpret_cast<u32x4*>(vt + r * ROWB + lc * 16) = vr[i];
+        *reinterpret_cast<u32x4*>(kt + r * KROW + lc * 16) = kr[i];
+        *reinterpret_cast<u32x4*>(vt + r * VROW + lc * 16) = vr[i];
       }
     };
     load_tile(tb);
@@ -851,7 +869,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_k
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const u32x4 kop =
-              *reinterpret_cast<const u32x4*>(kt + (16 * g + col) * ROWB + (32 * ks + 8 * q4) * 2);
+              *reinterpret_cast<const u32x4*>(kt + (16 * g + col) * KROW + (32 * ks + 8 * q4) * 2);
           sacc[g] = mfma_16x16x32<DT>(kop, qop[ks], sacc[g]);
         }
       }
@@ -891,18 +909,14 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_k
       l += psum;
       const u32x4 pop = u32x4{pw[0], pw[1], pw[2], pw[3]};
 
+      // V^T: lane (q4, col) fetches row 4*q4 + col/4 (and 16 + that), columns
+      // 16n + 4*(col%4) .. +3, and receives column 16n + col
+      const char* vrow0 = vt + (4 * q4 + col / 4) * VROW + 8 * (col % 4);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        uint32_t vw[4];
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const uint32_t t0 = 16 * (j / 4) + 4 * q4 + (j % 4);
-          const uint32_t e = (16 * n + col) * 2;
-          const uint32_t lo = *reinterpret_cast<const uint16_t*>(vt + t0 * ROWB + e);
-          const uint32_t hi = *reinterpret_cast<const uint16_t*>(vt + (t0 + 1) * ROWB + e);
-          vw[j / 2] = lo | (hi << 16);
-        }
-        acc[n] = mfma_16x16x32<DT>(u32x4{vw[0], vw[1], vw[2], vw[3]}, pop, acc[n]);
+        const uint2 lo = lds_read_tr16(vrow0 + 32 * n);
+        const uint2 hi = lds_read_tr16(vrow0 + 16 * VROW + 32 * n);
+        acc[n] = mfma_16x16x32<DT>(u32x4{lo.x, lo.y, hi.x, hi.y}, pop, acc[n]);
       }
       if (!has_next) break;
       store_tile();
@@ -914,7 +928,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_k
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   __syncthreads();  // every wave is done with its tile before the tiles become merge space
-  float(*s_acc)[GT][D] = reinterpret_cast<float(*)[GT][D]>(&s_tile[0][0][0]);
+  float(*s_acc)[GT][D] = reinterpret_cast<float(*)[GT][D]>(&s_tile[0][0]);
   if (col < GT) {
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
@@ -945,18 +959,6 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_k
 // fetch row r of a 4x16 block; lane i receives column i), from rows padded by
 // 32 bytes so those 8-byte reads fall on distinct banks.
 // ---------------------------------------------------------------------------
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) char lds_char;
-
-__device__ inline uint2 lds_read_tr16(const char* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)((lds_char*)(const_cast<char*>(p))));
-  uint2 r;
-  __builtin_memcpy(&r, &v, sizeof(r));
-  return r;
-}
 
 // Two exact code values (fp32) as a packed 16-bit pair of the q type.
 template <int DT>
