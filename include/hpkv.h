@@ -167,15 +167,20 @@ int hpkv_store_kvcache(int dtype, const void* key, const void* value, void* k_ca
  * Bytes of device workspace hpkv_paged_attention_decode needs for a batch of
  * num_seqs sequences no longer than max_context_len tokens (the split-context
  * partials: one fp32 (max, sum) pair and one fp32 head_dim vector per
- * sequence, query head and context partition). 0 on invalid arguments.
+ * sequence, query head and context partition), counted with the smallest
+ * partition the library uses, so it is enough for every num_kv_heads and for
+ * the quantized decode. 0 on invalid arguments.
  * ------------------------------------------------------------------------- */
 size_t hpkv_paged_attention_decode_workspace_size(int dtype, uint32_t num_seqs,
                                                   uint32_t num_q_heads, uint32_t head_dim,
                                                   uint32_t page_size, uint32_t max_context_len);
 
-/* Context tokens covered by one split-context partition (a library constant
- * for the given arguments; exposed for accounting and tests). */
-uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t head_dim,
+/* Context tokens covered by one split-context partition of
+ * hpkv_paged_attention_decode for this shape (512, or 1024 where one
+ * workgroup serves two KV heads on the matrix cores); exposed for accounting
+ * and tests. 0 on invalid arguments. */
+uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_q_heads,
+                                                      uint32_t num_kv_heads, uint32_t head_dim,
                                                       uint32_t page_size);
 
 /* ---------------------------------------------------------------------------
@@ -238,10 +243,10 @@ int hpkv_paged_attention_decode_partitions(int dtype, int index_type, const void
                                            uint32_t max_context_len, void* workspace,
                                            size_t workspace_bytes, void* out, void* stream);
 int hpkv_paged_attention_decode_reduce(int dtype, const int32_t* context_lens, uint32_t num_seqs,
-                                       uint32_t num_q_heads, uint32_t head_dim,
-                                       uint32_t page_size, uint32_t max_context_len,
-                                       void* workspace, size_t workspace_bytes, void* out,
-                                       void* stream);
+                                       uint32_t num_q_heads, uint32_t num_kv_heads,
+                                       uint32_t head_dim, uint32_t page_size,
+                                       uint32_t max_context_len, void* workspace,
+                                       size_t workspace_bytes, void* out, void* stream);
 
 /* ---------------------------------------------------------------------------
  * hpkv_paged_attention_decode_step  (device)

@@ -70,14 +70,14 @@ def _load():
         "hpkv_slot_mapping": ([i32, vp, u64, vp, u32, u32, vp, vp, u64, vp, vp], i32),
         "hpkv_store_kvcache": ([i32, vp, vp, vp, vp, vp, u64, u32, u64, u32, u32, vp], i32),
         "hpkv_paged_attention_decode_workspace_size": ([i32, u32, u32, u32, u32, u32], sz),
-        "hpkv_paged_attention_decode_partition_tokens": ([i32, u32, u32], u32),
+        "hpkv_paged_attention_decode_partition_tokens": ([i32, u32, u32, u32, u32], u32),
         "hpkv_paged_attention_decode": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, u32, u32, u32,
                                          u32, u32, u64, f32, u32, vp, sz, vp, vp], i32),
         "hpkv_paged_attention_decode_partitions": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, u32,
                                                     u32, u32, u32, u32, u64, f32, u32, vp, sz,
                                                     vp, vp], i32),
-        "hpkv_paged_attention_decode_reduce": ([i32, vp, u32, u32, u32, u32, u32, vp, sz, vp, vp],
-                                               i32),
+        "hpkv_paged_attention_decode_reduce": ([i32, vp, u32, u32, u32, u32, u32, u32, vp, sz,
+                                                vp, vp], i32),
         "hpkv_paged_attention_decode_step": ([i32, i32, vp, vp, vp, vp, vp, vp, u64, vp, vp, u32,
                                               u32, u32, u32, u32, u64, f32, u32, vp, vp, sz, vp,
                                               vp], i32),
@@ -187,9 +187,10 @@ def hpkv_paged_attention_decode_workspace_size(dtype, num_seqs, num_q_heads, hea
         _DTYPE_CODE[dtype], num_seqs, num_q_heads, head_dim, page_size, max_context_len))
 
 
-def hpkv_paged_attention_decode_partition_tokens(dtype, head_dim, page_size):
-    return int(lib.hpkv_paged_attention_decode_partition_tokens(_DTYPE_CODE[dtype], head_dim,
-                                                                page_size))
+def hpkv_paged_attention_decode_partition_tokens(dtype, num_q_heads, num_kv_heads, head_dim,
+                                                 page_size):
+    return int(lib.hpkv_paged_attention_decode_partition_tokens(
+        _DTYPE_CODE[dtype], num_q_heads, num_kv_heads, head_dim, page_size))
 
 
 # -------------------------------------------------------------- device entry points
@@ -251,14 +252,14 @@ def hpkv_paged_attention_decode_partitions(q, k_cache, v_cache, block_table, seq
            lib.hpkv_paged_attention_decode_partitions(*args, _stream(stream, q)))
 
 
-def hpkv_paged_attention_decode_reduce(context_lens, page_size, max_context_len, workspace, out,
-                                       stream=None):
+def hpkv_paged_attention_decode_reduce(context_lens, num_kv_heads, page_size, max_context_len,
+                                       workspace, out, stream=None):
     _contig(context_lens, workspace, out)
     B, hq, d = out.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("hpkv_paged_attention_decode_reduce", lib.hpkv_paged_attention_decode_reduce(
-        _DTYPE_CODE[out.dtype], _ptr(context_lens), B, hq, d, page_size, int(max_context_len),
-        _ptr(workspace), ws_bytes, _ptr(out), _stream(stream, out)))
+        _DTYPE_CODE[out.dtype], _ptr(context_lens), B, hq, num_kv_heads, d, page_size,
+        int(max_context_len), _ptr(workspace), ws_bytes, _ptr(out), _stream(stream, out)))
 
 
 def hpkv_paged_attention_decode_step(q, new_key, new_value, k_cache, v_cache, block_table,

@@ -14,9 +14,11 @@ using hpkv::ReduceKernelArgs;
 
 // Context tokens per split-context partition. 512 tokens keep a sequence of
 // the Llama/GQA shapes at a handful of partitions (enough workgroups to fill
-// 256 CUs at batch 64) while the partials stay ~1-2 % of the KV bytes.
+// 256 CUs at batch 64) while the partials stay ~1-2 % of the KV bytes. The
+// matrix-core kernel that serves two KV heads per workgroup takes 1024.
 constexpr uint32_t kPartTokens = 512;
 static_assert(kPartTokens <= hpkv::kMaxPartTokens, "partition larger than the LDS row table");
+static_assert(kPartTokens <= hpkv::kWidePartTokens, "the workspace is sized for the smaller one");
 
 bool valid_dtype(int dt) { return dt == HPKV_F32 || dt == HPKV_F16 || dt == HPKV_BF16; }
 bool valid_index(int it) { return it == HPKV_INDEX_U32 || it == HPKV_INDEX_U64; }
@@ -44,8 +46,17 @@ bool quant_head_dim_supported(uint32_t head_dim) {
          head_dim == 256;
 }
 
-uint32_t max_parts_for(uint32_t max_context_len) {
-  return max_context_len == 0 ? 1u : (max_context_len + kPartTokens - 1) / kPartTokens;
+uint32_t max_parts_for(uint32_t max_context_len, uint32_t part_tokens) {
+  return max_context_len == 0 ? 1u : (max_context_len + part_tokens - 1) / part_tokens;
+}
+
+// Partition size of the 16/32-bit decode for a shape (quantized pools: kPartTokens).
+uint32_t part_tokens_for(int dtype, uint32_t num_q_heads, uint32_t num_kv_heads,
+                         uint32_t head_dim) {
+  const uint32_t group = num_q_heads / num_kv_heads;
+  return hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads) > 1
+             ? hpkv::kWidePartTokens
+             : kPartTokens;
 }
 
 struct WorkspaceLayout {
@@ -53,8 +64,8 @@ struct WorkspaceLayout {
 };
 
 WorkspaceLayout workspace_layout(uint32_t num_seqs, uint32_t num_q_heads, uint32_t head_dim,
-                                 uint32_t max_context_len) {
-  const uint64_t mp = max_parts_for(max_context_len);
+                                 uint32_t max_context_len, uint32_t part_tokens) {
+  const uint64_t mp = max_parts_for(max_context_len, part_tokens);
   WorkspaceLayout w{0, 0, 0};
   if (mp <= 1) return w;  // every sequence fits one partition: no partials
   const uint64_t rows = uint64_t(num_seqs) * num_q_heads * mp;
@@ -92,16 +103,20 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
        reinterpret_cast<uintptr_t>(v_cache)) % 16 != 0)
     return HPKV_ERR_INVALID_ARG;
-  const WorkspaceLayout w = workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len);
+  const uint32_t group = num_q_heads / num_kv_heads;
+  const uint32_t hpw =
+      quant ? 1u : hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads);
+  const uint32_t part_tokens = hpw > 1 ? hpkv::kWidePartTokens : kPartTokens;
+  const WorkspaceLayout w =
+      workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, part_tokens);
   if (w.bytes > 0 && (!workspace || workspace_bytes < w.bytes)) return HPKV_ERR_WORKSPACE;
   if (w.bytes > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return HPKV_ERR_INVALID_ARG;
 
-  const uint32_t group = num_q_heads / num_kv_heads;
   const uint32_t gt = quant ? hpkv::heads_per_workgroup_quant(dtype, head_dim, group)
                             : hpkv::heads_per_workgroup(dtype, head_dim, group);
-  const uint32_t max_parts = max_parts_for(max_context_len);
-  const uint64_t head_tiles = uint64_t(num_kv_heads) * (group / gt);
+  const uint32_t max_parts = max_parts_for(max_context_len, part_tokens);
+  const uint64_t head_tiles = uint64_t(num_kv_heads / hpw) * (group / gt);
   const uint64_t nwg = head_tiles * max_parts * num_seqs;
   if (nwg > 0xffffffffull / 256) return HPKV_ERR_UNSUPPORTED;  // launch grid limit
 
@@ -124,8 +139,9 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
   a->page_size = page_size;
   a->group = group;
   a->head_tiles = uint32_t(head_tiles);
+  a->kv_per_wg = hpw;
   a->max_parts = max_parts;
-  a->part_tokens = kPartTokens;
+  a->part_tokens = part_tokens;
   a->max_context_len = max_context_len;
   a->page_div = hpkv::make_fastdiv(page_size);
   a->scale_log2 = scale * 1.4426950408889634f;  // log2(e)
@@ -261,19 +277,22 @@ int hpkv_store_kvcache(int dtype, const void* key, const void* value, void* k_ca
                                        static_cast<hipStream_t>(stream)));
 }
 
-uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t head_dim,
+uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_q_heads,
+                                                      uint32_t num_kv_heads, uint32_t head_dim,
                                                       uint32_t page_size) {
-  (void)dtype;
-  (void)head_dim;
   (void)page_size;
-  return kPartTokens;
+  if (!valid_dtype(dtype) || num_q_heads == 0 || num_kv_heads == 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  return part_tokens_for(dtype, num_q_heads, num_kv_heads, head_dim);
 }
 
 size_t hpkv_paged_attention_decode_workspace_size(int dtype, uint32_t num_seqs,
                                                   uint32_t num_q_heads, uint32_t head_dim,
                                                   uint32_t page_size, uint32_t max_context_len) {
   if (!valid_dtype(dtype) || page_size == 0) return 0;
-  return workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len).bytes;
+  // sized for the smallest partition, so it covers every shape
+  return workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, kPartTokens).bytes;
 }
 
 int hpkv_paged_attention_decode_partitions(int dtype, int index_type, const void* q,
@@ -297,17 +316,21 @@ int hpkv_paged_attention_decode_partitions(int dtype, int index_type, const void
 }
 
 int hpkv_paged_attention_decode_reduce(int dtype, const int32_t* context_lens, uint32_t num_seqs,
-                                       uint32_t num_q_heads, uint32_t head_dim,
-                                       uint32_t page_size, uint32_t max_context_len,
-                                       void* workspace, size_t workspace_bytes, void* out,
-                                       void* stream) {
+                                       uint32_t num_q_heads, uint32_t num_kv_heads,
+                                       uint32_t head_dim, uint32_t page_size,
+                                       uint32_t max_context_len, void* workspace,
+                                       size_t workspace_bytes, void* out, void* stream) {
   if (!valid_dtype(dtype)) return HPKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return HPKV_OK;
   if (!context_lens || !out) return HPKV_ERR_NULL;
-  if (num_q_heads == 0 || head_dim == 0 || page_size == 0) return HPKV_ERR_INVALID_ARG;
+  if (num_q_heads == 0 || num_kv_heads == 0 || head_dim == 0 || page_size == 0)
+    return HPKV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return HPKV_ERR_INVALID_ARG;
   if (max_context_len > 0x7fffffffu) return HPKV_ERR_INVALID_ARG;
   if (!decode_head_dim_supported(dtype, head_dim)) return HPKV_ERR_UNSUPPORTED;
-  const WorkspaceLayout w = workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len);
+  const uint32_t part_tokens = part_tokens_for(dtype, num_q_heads, num_kv_heads, head_dim);
+  const WorkspaceLayout w =
+      workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, part_tokens);
   if (w.bytes == 0) return HPKV_OK;  // single partition: nothing to merge
   if (!workspace || workspace_bytes < w.bytes) return HPKV_ERR_WORKSPACE;
   ReduceKernelArgs r;
@@ -318,8 +341,8 @@ int hpkv_paged_attention_decode_reduce(int dtype, const int32_t* context_lens, u
   r.num_seqs = num_seqs;
   r.num_q_heads = num_q_heads;
   r.head_dim = head_dim;
-  r.max_parts = max_parts_for(max_context_len);
-  r.part_tokens = kPartTokens;
+  r.max_parts = max_parts_for(max_context_len, part_tokens);
+  r.part_tokens = part_tokens;
   r.max_context_len = max_context_len;
   return hip_status(hpkv::launch_decode_reduce(dtype, r, static_cast<hipStream_t>(stream)));
 }

@@ -14,8 +14,11 @@ enum : int { kI8 = 3, kFP8 = 4 };
 
 inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : 2; }
 
-// Largest split-context partition the decode kernel's LDS row table holds.
+// Split-context partitions, in context tokens: the size every decode kernel's
+// LDS row table holds, and the larger one of the matrix-core kernel that
+// serves two adjacent KV heads per workgroup (its table holds that many).
 constexpr uint32_t kMaxPartTokens = 512;
+constexpr uint32_t kWidePartTokens = 1024;
 
 // Division by a runtime divisor 1 <= d < 2^31 for numerators n < 2^31:
 // n / d == (n * mul) >> shift with shift = 31 + ceil(log2 d) and
@@ -52,7 +55,8 @@ struct DecodeKernelArgs {
   uint32_t num_kv_heads;
   uint32_t page_size;
   uint32_t group;       // num_q_heads / num_kv_heads
-  uint32_t head_tiles;  // num_kv_heads * (group / heads per workgroup)
+  uint32_t head_tiles;  // (num_kv_heads / kv_per_wg) * (group / heads per workgroup)
+  uint32_t kv_per_wg;   // adjacent KV heads per workgroup (> 1: whole GQA groups)
   uint32_t max_parts;
   uint32_t part_tokens;
   uint32_t max_context_len;
@@ -123,6 +127,10 @@ hipError_t launch_prefill(int dtype, uint32_t head_dim, const PrefillKernelArgs&
 // Query heads served by one decode workgroup for a GQA group of `group` heads
 // (the matrix-core path takes up to 16 heads of a group at once).
 uint32_t heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group);
+// Adjacent KV heads served by one decode workgroup (more than one only when a
+// workgroup takes whole GQA groups on the matrix cores).
+uint32_t kv_heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group,
+                                uint32_t num_kv_heads);
 // The same for quantized pools.
 uint32_t heads_per_workgroup_quant(int dtype, uint32_t head_dim, uint32_t group);
 

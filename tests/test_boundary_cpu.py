@@ -203,8 +203,33 @@ def test_quant_argument_errors():
     assert call(14, 0, dq, base) == hpkv.OK                      # empty batch
 
 
+def test_partition_tokens_per_shape():
+    pt = hpkv.lib.hpkv_paged_attention_decode_partition_tokens
+    assert pt(hpkv.BF16, 32, 32, 128, 16) == 512    # one query head per KV head
+    assert pt(hpkv.BF16, 32, 8, 128, 16) == 1024    # two KV heads (whole groups) per workgroup
+    assert pt(hpkv.F16, 16, 4, 64, 16) == 1024
+    assert pt(hpkv.BF16, 24, 3, 128, 16) == 512     # odd number of KV heads
+    assert pt(hpkv.BF16, 64, 2, 128, 16) == 512     # group of 32: two tiles per group
+    assert pt(hpkv.F32, 32, 8, 128, 16) == 512      # no matrix-core path for fp32
+    assert pt(hpkv.BF16, 32, 8, 256, 16) == 512     # head_dim 256: VALU kernel
+    assert pt(hpkv.BF16, 32, 0, 128, 16) == 0 and pt(hpkv.BF16, 30, 8, 128, 16) == 0
+    assert pt(9, 32, 8, 128, 16) == 0
+
+
+def test_reduce_argument_errors():
+    red = hpkv.lib.hpkv_paged_attention_decode_reduce
+    assert red(hpkv.BF16, FAKE, 4, 32, 0, 128, 16, 4096, FAKE, 1 << 20, FAKE, None) == \
+        hpkv.ERR_INVALID_ARG
+    assert red(hpkv.BF16, FAKE, 4, 30, 8, 128, 16, 4096, FAKE, 1 << 20, FAKE, None) == \
+        hpkv.ERR_INVALID_ARG
+    assert red(hpkv.BF16, FAKE, 4, 32, 8, 128, 16, 4096, None, 0, FAKE, None) == \
+        hpkv.ERR_WORKSPACE
+    assert red(hpkv.BF16, FAKE, 4, 32, 8, 128, 16, 1024, None, 0, FAKE, None) == hpkv.OK  # one part
+    assert red(hpkv.BF16, FAKE, 0, 32, 8, 128, 16, 4096, None, 0, FAKE, None) == hpkv.OK
+
+
 def test_workspace_size_accounting():
-    P = hpkv.lib.hpkv_paged_attention_decode_partition_tokens(hpkv.BF16, 128, 16)
+    P = hpkv.lib.hpkv_paged_attention_decode_partition_tokens(hpkv.BF16, 32, 32, 128, 16)
     assert P >= 16 and P % 16 == 0
     ws = hpkv.lib.hpkv_paged_attention_decode_workspace_size
     assert ws(hpkv.BF16, 64, 32, 128, 16, P) == 0           # one partition: no partials

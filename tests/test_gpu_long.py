@@ -1,7 +1,8 @@
 """Long contexts on the GPU path against the oracle.
 
-Decode over ~70k-token contexts runs 137 split-context partitions per
-sequence, more than one per lane of the reduce kernel's wave. Prefill chunks
+Decode over ~70k-token contexts runs more split-context partitions per
+sequence than the reduce kernel's wave has lanes (137 of 512 tokens; 69 of
+1024 where a workgroup serves two KV heads on the matrix cores). Prefill chunks
 at positions past 4096 and 8192 make a workgroup resolve its keys' pool rows
 in several segments. Both are checked against the oracle (prefill on sampled
 rows), with unused pool rows poisoned by NaN.

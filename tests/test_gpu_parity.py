@@ -234,7 +234,8 @@ def test_partition_and_reduce_entry_points_match_decode():
     ws = hpkv.alloc_workspace(t.q, t.k_cache, w.max_context_len)
     hpkv.hpkv_paged_attention_decode_partitions(t.q, t.k_cache, t.v_cache, bt, sp, ctx, w.scale,
                                                 w.max_context_len, ws, out)
-    hpkv.hpkv_paged_attention_decode_reduce(ctx, w.page_size, w.max_context_len, ws, out)
+    hpkv.hpkv_paged_attention_decode_reduce(ctx, w.num_kv_heads, w.page_size, w.max_context_len,
+                                            ws, out)
     torch.cuda.synchronize()
     assert host_bits(out).tobytes() == ref.tobytes()
 
