@@ -176,12 +176,16 @@ size_t hpkv_paged_attention_decode_workspace_size(int dtype, uint32_t num_seqs,
                                                   uint32_t page_size, uint32_t max_context_len);
 
 /* Context tokens covered by one split-context partition of
- * hpkv_paged_attention_decode for this shape (512, or 1024 where one
- * workgroup serves two KV heads on the matrix cores); exposed for accounting
- * and tests. 0 on invalid arguments. */
-uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_q_heads,
+ * hpkv_paged_attention_decode (and of the _step and _reduce entry points) for
+ * this call shape: 1024 when the batch still gives at least 256 workgroups (one
+ * per CU) with partitions that long, else 512 (the quantized decode always
+ * uses 512).
+ * Exposed for accounting and tests. 0 on invalid arguments. */
+uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_seqs,
+                                                      uint32_t num_q_heads,
                                                       uint32_t num_kv_heads, uint32_t head_dim,
-                                                      uint32_t page_size);
+                                                      uint32_t page_size,
+                                                      uint32_t max_context_len);
 
 /* ---------------------------------------------------------------------------
  * hpkv_paged_attention_decode  (device)

@@ -70,7 +70,8 @@ def _load():
         "hpkv_slot_mapping": ([i32, vp, u64, vp, u32, u32, vp, vp, u64, vp, vp], i32),
         "hpkv_store_kvcache": ([i32, vp, vp, vp, vp, vp, u64, u32, u64, u32, u32, vp], i32),
         "hpkv_paged_attention_decode_workspace_size": ([i32, u32, u32, u32, u32, u32], sz),
-        "hpkv_paged_attention_decode_partition_tokens": ([i32, u32, u32, u32, u32], u32),
+        "hpkv_paged_attention_decode_partition_tokens": ([i32, u32, u32, u32, u32, u32, u32],
+                                                         u32),
         "hpkv_paged_attention_decode": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, u32, u32, u32,
                                          u32, u32, u64, f32, u32, vp, sz, vp, vp], i32),
         "hpkv_paged_attention_decode_partitions": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, u32,
@@ -187,10 +188,11 @@ def hpkv_paged_attention_decode_workspace_size(dtype, num_seqs, num_q_heads, hea
         _DTYPE_CODE[dtype], num_seqs, num_q_heads, head_dim, page_size, max_context_len))
 
 
-def hpkv_paged_attention_decode_partition_tokens(dtype, num_q_heads, num_kv_heads, head_dim,
-                                                 page_size):
+def hpkv_paged_attention_decode_partition_tokens(dtype, num_seqs, num_q_heads, num_kv_heads,
+                                                 head_dim, page_size, max_context_len):
     return int(lib.hpkv_paged_attention_decode_partition_tokens(
-        _DTYPE_CODE[dtype], num_q_heads, num_kv_heads, head_dim, page_size))
+        _DTYPE_CODE[dtype], num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+        max_context_len))
 
 
 # -------------------------------------------------------------- device entry points

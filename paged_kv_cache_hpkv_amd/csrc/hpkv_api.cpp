@@ -12,13 +12,17 @@ namespace {
 using hpkv::DecodeKernelArgs;
 using hpkv::ReduceKernelArgs;
 
-// Context tokens per split-context partition. 512 tokens keep a sequence of
-// the Llama/GQA shapes at a handful of partitions (enough workgroups to fill
-// 256 CUs at batch 64) while the partials stay ~1-2 % of the KV bytes. The
-// matrix-core kernel that serves two KV heads per workgroup takes 1024.
+// Context tokens per split-context partition: 512 (kPartTokens) or 1024
+// (hpkv::kWidePartTokens, where the kernel's row table holds that many and the
+// batch still gives enough workgroups). The partials stay ~1-2 % of the KV bytes.
 constexpr uint32_t kPartTokens = 512;
 static_assert(kPartTokens <= hpkv::kMaxPartTokens, "partition larger than the LDS row table");
 static_assert(kPartTokens <= hpkv::kWidePartTokens, "the workspace is sized for the smaller one");
+// Fewest workgroups a coarser launch shape may leave: one per CU. Measured on
+// MI355X, GQA 32/8 at 16 x 4096 tokens: 256 two-head workgroups with 1024-token
+// partitions beat 1024 one-head workgroups (44 vs 47 us); at 1 x 4096 tokens,
+// 64 one-head workgroups beat 16 two-head ones (13 vs 23 us).
+constexpr uint64_t kMinWorkgroups = 256;
 
 bool valid_dtype(int dt) { return dt == HPKV_F32 || dt == HPKV_F16 || dt == HPKV_BF16; }
 bool valid_index(int it) { return it == HPKV_INDEX_U32 || it == HPKV_INDEX_U64; }
@@ -50,13 +54,40 @@ uint32_t max_parts_for(uint32_t max_context_len, uint32_t part_tokens) {
   return max_context_len == 0 ? 1u : (max_context_len + part_tokens - 1) / part_tokens;
 }
 
-// Partition size of the 16/32-bit decode for a shape (quantized pools: kPartTokens).
-uint32_t part_tokens_for(int dtype, uint32_t num_q_heads, uint32_t num_kv_heads,
-                         uint32_t head_dim) {
+// Launch shape of a decode call: query heads per workgroup (gt), adjacent KV
+// heads per workgroup (hpw) and tokens per partition. Larger work units spread
+// each workgroup's fixed costs (row table, first loads, merge) over more bytes
+// (measured on MI355X: +8 % for the GQA batch with two KV heads and 1024-token
+// partitions, +2-3 % for the VALU kernel with 1024-token partitions), but a
+// small batch needs the finer ones to fill the GPU: the coarsest shape whose
+// grid keeps kMinWorkgroups workgroups is taken, else the finest.
+struct DecodePlan {
+  uint32_t gt, hpw, part_tokens;
+};
+
+DecodePlan plan_decode(int dtype, bool quant, uint32_t num_seqs, uint32_t num_q_heads,
+                       uint32_t num_kv_heads, uint32_t head_dim, uint32_t max_context_len) {
   const uint32_t group = num_q_heads / num_kv_heads;
-  return hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads) > 1
-             ? hpkv::kWidePartTokens
-             : kPartTokens;
+  if (quant) return {hpkv::heads_per_workgroup_quant(dtype, head_dim, group), 1, kPartTokens};
+  const uint32_t gt = hpkv::heads_per_workgroup(dtype, head_dim, group);
+  DecodePlan c[3];
+  int n = 0;
+  if (hpkv::decode_on_matrix_cores(dtype, head_dim, group)) {
+    if (hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads) > 1) {
+      c[n++] = {gt, 2, hpkv::kWidePartTokens};
+      c[n++] = {gt, 2, kPartTokens};
+    }
+    c[n++] = {gt, 1, kPartTokens};
+  } else {
+    c[n++] = {gt, 1, hpkv::kWidePartTokens};
+    c[n++] = {gt, 1, kPartTokens};
+  }
+  for (int i = 0; i + 1 < n; ++i) {
+    const uint64_t grid = uint64_t(num_kv_heads / c[i].hpw) * (group / gt) * num_seqs *
+                          max_parts_for(max_context_len, c[i].part_tokens);
+    if (grid >= kMinWorkgroups) return c[i];
+  }
+  return c[n - 1];
 }
 
 struct WorkspaceLayout {
@@ -104,17 +135,15 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
        reinterpret_cast<uintptr_t>(v_cache)) % 16 != 0)
     return HPKV_ERR_INVALID_ARG;
   const uint32_t group = num_q_heads / num_kv_heads;
-  const uint32_t hpw =
-      quant ? 1u : hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads);
-  const uint32_t part_tokens = hpw > 1 ? hpkv::kWidePartTokens : kPartTokens;
+  const DecodePlan plan = plan_decode(dtype, quant, num_seqs, num_q_heads, num_kv_heads,
+                                      head_dim, max_context_len);
+  const uint32_t hpw = plan.hpw, gt = plan.gt, part_tokens = plan.part_tokens;
   const WorkspaceLayout w =
       workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, part_tokens);
   if (w.bytes > 0 && (!workspace || workspace_bytes < w.bytes)) return HPKV_ERR_WORKSPACE;
   if (w.bytes > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return HPKV_ERR_INVALID_ARG;
 
-  const uint32_t gt = quant ? hpkv::heads_per_workgroup_quant(dtype, head_dim, group)
-                            : hpkv::heads_per_workgroup(dtype, head_dim, group);
   const uint32_t max_parts = max_parts_for(max_context_len, part_tokens);
   const uint64_t head_tiles = uint64_t(num_kv_heads / hpw) * (group / gt);
   const uint64_t nwg = head_tiles * max_parts * num_seqs;
@@ -277,14 +306,18 @@ int hpkv_store_kvcache(int dtype, const void* key, const void* value, void* k_ca
                                        static_cast<hipStream_t>(stream)));
 }
 
-uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_q_heads,
+uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_seqs,
+                                                      uint32_t num_q_heads,
                                                       uint32_t num_kv_heads, uint32_t head_dim,
-                                                      uint32_t page_size) {
+                                                      uint32_t page_size,
+                                                      uint32_t max_context_len) {
   (void)page_size;
   if (!valid_dtype(dtype) || num_q_heads == 0 || num_kv_heads == 0 ||
       num_q_heads % num_kv_heads != 0)
     return 0;
-  return part_tokens_for(dtype, num_q_heads, num_kv_heads, head_dim);
+  return plan_decode(dtype, false, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     max_context_len)
+      .part_tokens;
 }
 
 size_t hpkv_paged_attention_decode_workspace_size(int dtype, uint32_t num_seqs,
@@ -328,7 +361,9 @@ int hpkv_paged_attention_decode_reduce(int dtype, const int32_t* context_lens, u
   if (num_q_heads % num_kv_heads != 0) return HPKV_ERR_INVALID_ARG;
   if (max_context_len > 0x7fffffffu) return HPKV_ERR_INVALID_ARG;
   if (!decode_head_dim_supported(dtype, head_dim)) return HPKV_ERR_UNSUPPORTED;
-  const uint32_t part_tokens = part_tokens_for(dtype, num_q_heads, num_kv_heads, head_dim);
+  const uint32_t part_tokens = plan_decode(dtype, false, num_seqs, num_q_heads, num_kv_heads,
+                                           head_dim, max_context_len)
+                                   .part_tokens;
   const WorkspaceLayout w =
       workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, part_tokens);
   if (w.bytes == 0) return HPKV_OK;  // single partition: nothing to merge

@@ -181,9 +181,11 @@ struct NoTokenHook {
   __device__ void operator()(uint32_t, uint64_t) const {}
 };
 
-template <int DT, int D, int NH, int NTH, class Hook = NoTokenHook, int NKV = 1>
+template <int DT, int D, int NH, int NTH, class Hook = NoTokenHook, int NKV = 1,
+          uint32_t CAP = 0>
 __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem& it,
-                                       uint64_t* s_row, Partition& w, Hook on_token = Hook{}) {
+                                       uint64_t (&s_row)[CAP], Partition& w,
+                                       Hook on_token = Hook{}) {
   const uint32_t tid = threadIdx.x;
   w.s = it.s;
   w.part = it.part;
@@ -207,8 +209,10 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
     return false;
   }
 
+  // (a partition longer than the row table cannot come from the host's plan; it is
+  // refused here rather than written past the table)
   bool bad = first > last || last > a.block_table_len ||
-             uint64_t(n) > (last - first) * uint64_t(a.page_size);
+             uint64_t(n) > (last - first) * uint64_t(a.page_size) || a.part_tokens > CAP;
 
   const uint32_t p0 = w.part * a.part_tokens;
   w.cnt = bad || n == 0 ? 0u : min(uint32_t(n) - p0, a.part_tokens);
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
   static_assert(CPR % CPL == 0 && LPR <= kWave && (LPR & (LPR - 1)) == 0,
                 "unsupported head_dim");
 
-  __shared__ uint64_t s_row[kMaxPartTokens];
+  __shared__ uint64_t s_row[kWidePartTokens];
   __shared__ float s_m[NW][GT];
   __shared__ float s_l[NW][GT];
   __shared__ float s_acc[NW][GT][D];
@@ -1460,6 +1464,10 @@ uint32_t heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group) {
   if (group % 4 == 0) return 4;
   if (group % 2 == 0) return 2;
   return 1;
+}
+
+bool decode_on_matrix_cores(int dtype, uint32_t head_dim, uint32_t group) {
+  return mfma_eligible(dtype, head_dim, group);
 }
 
 uint32_t kv_heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group,

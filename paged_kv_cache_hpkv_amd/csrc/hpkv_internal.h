@@ -14,9 +14,10 @@ enum : int { kI8 = 3, kFP8 = 4 };
 
 inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : 2; }
 
-// Split-context partitions, in context tokens: the size every decode kernel's
-// LDS row table holds, and the larger one of the matrix-core kernel that
-// serves two adjacent KV heads per workgroup (its table holds that many).
+// Split-context partitions, in context tokens, as sizes of the decode kernels'
+// LDS row tables: the quantized kernels and the matrix-core kernel with one KV
+// head per workgroup hold kMaxPartTokens; the VALU kernel and the matrix-core
+// kernel with two KV heads per workgroup hold kWidePartTokens.
 constexpr uint32_t kMaxPartTokens = 512;
 constexpr uint32_t kWidePartTokens = 1024;
 
@@ -127,7 +128,9 @@ hipError_t launch_prefill(int dtype, uint32_t head_dim, const PrefillKernelArgs&
 // Query heads served by one decode workgroup for a GQA group of `group` heads
 // (the matrix-core path takes up to 16 heads of a group at once).
 uint32_t heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group);
-// Adjacent KV heads served by one decode workgroup (more than one only when a
+// Whether the 16/32-bit decode of a shape runs on the matrix cores.
+bool decode_on_matrix_cores(int dtype, uint32_t head_dim, uint32_t group);
+// Most adjacent KV heads one decode workgroup may serve (two only when a
 // workgroup takes whole GQA groups on the matrix cores).
 uint32_t kv_heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group,
                                 uint32_t num_kv_heads);

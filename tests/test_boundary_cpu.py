@@ -204,16 +204,22 @@ def test_quant_argument_errors():
 
 
 def test_partition_tokens_per_shape():
+    """1024-token partitions where the batch still gives >= 256 workgroups with them
+    (KV heads / heads per workgroup x sequences x partitions), else 512."""
     pt = hpkv.lib.hpkv_paged_attention_decode_partition_tokens
-    assert pt(hpkv.BF16, 32, 32, 128, 16) == 512    # one query head per KV head
-    assert pt(hpkv.BF16, 32, 8, 128, 16) == 1024    # two KV heads (whole groups) per workgroup
-    assert pt(hpkv.F16, 16, 4, 64, 16) == 1024
-    assert pt(hpkv.BF16, 24, 3, 128, 16) == 512     # odd number of KV heads
-    assert pt(hpkv.BF16, 64, 2, 128, 16) == 512     # group of 32: two tiles per group
-    assert pt(hpkv.F32, 32, 8, 128, 16) == 512      # no matrix-core path for fp32
-    assert pt(hpkv.BF16, 32, 8, 256, 16) == 512     # head_dim 256: VALU kernel
-    assert pt(hpkv.BF16, 32, 0, 128, 16) == 0 and pt(hpkv.BF16, 30, 8, 128, 16) == 0
-    assert pt(9, 32, 8, 128, 16) == 0
+    # GQA 32/8 on the matrix cores, two KV heads per workgroup: 4 head tiles
+    assert pt(hpkv.BF16, 256, 32, 8, 128, 16, 8192) == 1024    # 4 * 256 * 8
+    assert pt(hpkv.BF16, 8, 32, 8, 128, 16, 8192) == 1024      # 4 * 8 * 8 = 256
+    assert pt(hpkv.BF16, 7, 32, 8, 128, 16, 8192) == 512       # 224 < 256
+    assert pt(hpkv.BF16, 1, 32, 8, 128, 16, 4096) == 512
+    # MHA 32/32 on the VALU kernel: 32 head tiles
+    assert pt(hpkv.BF16, 2, 32, 32, 128, 16, 4096) == 1024     # 32 * 2 * 4 = 256
+    assert pt(hpkv.BF16, 1, 32, 32, 128, 16, 4096) == 512      # 128 < 256
+    assert pt(hpkv.F32, 128, 32, 8, 128, 16, 8192) == 1024     # VALU, 8 heads per tile
+    assert pt(hpkv.BF16, 512, 24, 3, 128, 16, 8192) == 512     # odd Hkv on the matrix cores
+    assert pt(hpkv.BF16, 8, 32, 0, 128, 16, 4096) == 0
+    assert pt(hpkv.BF16, 8, 30, 8, 128, 16, 4096) == 0
+    assert pt(9, 8, 32, 8, 128, 16, 4096) == 0
 
 
 def test_reduce_argument_errors():
@@ -224,13 +230,16 @@ def test_reduce_argument_errors():
         hpkv.ERR_INVALID_ARG
     assert red(hpkv.BF16, FAKE, 4, 32, 8, 128, 16, 4096, None, 0, FAKE, None) == \
         hpkv.ERR_WORKSPACE
-    assert red(hpkv.BF16, FAKE, 4, 32, 8, 128, 16, 1024, None, 0, FAKE, None) == hpkv.OK  # one part
+    assert red(hpkv.BF16, FAKE, 4, 32, 8, 128, 16, 512, None, 0, FAKE, None) == hpkv.OK  # one part
     assert red(hpkv.BF16, FAKE, 0, 32, 8, 128, 16, 4096, None, 0, FAKE, None) == hpkv.OK
 
 
 def test_workspace_size_accounting():
-    P = hpkv.lib.hpkv_paged_attention_decode_partition_tokens(hpkv.BF16, 32, 32, 128, 16)
-    assert P >= 16 and P % 16 == 0
+    """The workspace is counted with the smaller, 512-token partition, so it covers
+    every shape's plan."""
+    P = hpkv.lib.hpkv_paged_attention_decode_partition_tokens(hpkv.BF16, 1, 32, 32, 128, 16,
+                                                              4096)
+    assert P == 512
     ws = hpkv.lib.hpkv_paged_attention_decode_workspace_size
     assert ws(hpkv.BF16, 64, 32, 128, 16, P) == 0           # one partition: no partials
     parts = -(-4096 // P)
