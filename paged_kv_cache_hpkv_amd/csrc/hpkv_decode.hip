@@ -681,104 +681,6 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
 }
 
 // ---------------------------------------------------------------------------
-// One query head per KV head (MHA), head-parallel: the 16-lane row groups of a
-// wave take RPL adjacent KV heads of the same token, so every wave load reads
-// one token's rows of those heads as one contiguous span, and the NW waves of
-// the workgroup together read the token's rows of HB = NW*RPL heads. Each
-// wave walks all tokens of the partition for its heads, so no merge across
-// waves or row groups is needed: each row group writes its head's result.
-// ---------------------------------------------------------------------------
-template <int DT, int D, class TU>
-__global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_hp_kernel(
-    const DecodeKernelArgs a) {
-  constexpr int NW = TU::NW;
-  constexpr int NTH = NW * kWave;
-  constexpr int NLOAD = TU::NLOAD;   // tokens per tile
-  constexpr int EB = Elem<DT>::bytes;
-  constexpr int EPL = 16 / EB;
-  constexpr int LPR = D / EPL;       // lanes per head row
-  constexpr int RPL = kWave / LPR;   // heads per wave
-  constexpr int HB = NW * RPL;       // heads per workgroup
-  static_assert(LPR >= 1 && LPR <= kWave && (LPR & (LPR - 1)) == 0, "unsupported head_dim");
-
-  __shared__ uint64_t s_row[kMaxPartTokens];
-
-  const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t wave = threadIdx.x / kWave;
-  uint32_t bid = blockIdx.x;
-  WorkItem it;
-  const uint32_t hb = bid % a.head_tiles;  // head block
-  bid /= a.head_tiles;
-  it.s = bid % a.num_seqs;
-  it.part = bid / a.num_seqs;
-  it.g = hb * HB;
-  it.h0 = it.g;
-  Partition w;
-  if (!setup_partition<DT, D, HB, NTH>(a, it, s_row, w)) return;
-  const uint32_t cnt = w.cnt;
-
-  const uint32_t hw = wave * RPL + lane / LPR;  // head of this row group within the block
-  const uint32_t c = lane % LPR;
-  const uint64_t orow = w.out_row0 + hw;         // (sequence, query head) row
-
-  const u32x4 qv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
-                                                   (orow * D + c * EPL) * EB);
-  float m = -INFINITY, l = 0.0f, acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-
-  const uint64_t lane_off = (uint64_t(hw) * D + c * EPL) * EB;
-  const char* kbase = static_cast<const char*>(a.k_cache) + lane_off;
-  const char* vbase = static_cast<const char*>(a.v_cache) + lane_off;
-
-  for (uint32_t tb = 0; tb < cnt; tb += NLOAD) {
-    u32x4 kr[NLOAD], vr[NLOAD];
-#pragma unroll
-    for (int k = 0; k < NLOAD; ++k) {
-      const uint32_t t = tb + k;
-      const uint64_t off = s_row[t < cnt ? t : cnt - 1] * EB;
-      kr[k] = load16<TU::NT>(kbase + off);
-      vr[k] = load16<TU::NT>(vbase + off);
-    }
-    float sc[NLOAD];
-#pragma unroll
-    for (int k = 0; k < NLOAD; ++k) {
-      const float z = row_sum<LPR>(dot16<DT>(kr[k], qv)) * a.scale_log2;
-      sc[k] = tb + k < cnt ? z : -INFINITY;
-    }
-    float mt = sc[0];
-#pragma unroll
-    for (int k = 1; k < NLOAD; ++k) mt = fmaxf(mt, sc[k]);
-    const float mn = fmaxf(m, mt);  // tb < cnt: at least sc[0] is finite
-    const float corr = __builtin_amdgcn_exp2f(m - mn);
-    l *= corr;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] *= corr;
-    m = mn;
-#pragma unroll
-    for (int k = 0; k < NLOAD; ++k) {
-      const float p = __builtin_amdgcn_exp2f(sc[k] - mn);
-      l += p;
-      float vf[EPL];
-      widen16<DT>(vr[k], vf);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
-    }
-  }
-
-  if (w.nparts == 1) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e)
-      store_out<DT>(a.out, orow * D + c * EPL + e, l > 0.0f ? acc[e] / l : 0.0f);
-  } else {
-    const uint64_t r = orow * a.max_parts + w.part;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) a.ws_o[r * D + c * EPL + e] = acc[e];
-    if (c == 0) a.ws_ml[r] = make_float2(m, l);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // GQA groups of 4 or more query heads: q.K^T and P.V on the matrix cores.
 //
 // Per wave and 32-token tile (two 16-token groups), with v_mfma_f32_16x16x32
