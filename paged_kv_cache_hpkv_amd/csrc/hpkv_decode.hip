@@ -33,7 +33,10 @@
 //    the address of the last valid row (finite data) and their score is -inf,
 //    so their weight is exactly 0 and NaN garbage in unused rows cannot reach
 //    the accumulators.
+#include <float.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "hpkv_device.h"
 
@@ -974,7 +977,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   static_assert(sizeof(float) * GT * D <= TT * (KROW + VROW), "merge buffer must fit the tiles");
 
   const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t wave = threadIdx.x / kWave;
+  // wave-uniform: kept in a scalar register, so the tile loop branches are scalar
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const WorkItem item = grid_item<GT>(a);
   const uint64_t kvh = item.g;
   auto stage_factors = [&](uint32_t i, uint64_t phys) {
@@ -988,6 +992,14 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   const uint32_t q4 = lane / 16;
   const uint32_t col = lane % 16;
 
+  // Scores are kept raw, ks * (q.value - kz * sum(q)), and scaled by
+  // c = |scale| * log2(e) inside the exponent; a negative scale is a sign flip of q
+  // (exact, and it flips sum(q) with it). Lazy rescaling: the subtracted max is
+  // raised only when a head's max grows by more than 8 (log2 units), so weights stay
+  // below 2^8 and most tiles skip the rescale of the accumulators.
+  const float c = fmaxf(fabsf(a.scale_log2), FLT_MIN);  // > 0 (a zero scale acts as FLT_MIN)
+  const uint32_t qflip = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
+  const float thr = 8.0f / c;
   u32x4 qop[KS];
   float qpart = 0.0f;  // this lane's share of sum(q) of head `col`
 #pragma unroll
@@ -995,7 +1007,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
     qop[ks] = u32x4{0, 0, 0, 0};
     if (col < GT) {
       const char* qp = static_cast<const char*>(a.q) + ((w.out_row0 + col) * D + 32 * ks + 8 * q4) * 2;
-      qop[ks] = *reinterpret_cast<const u32x4*>(qp);
+      qop[ks] = *reinterpret_cast<const u32x4*>(qp) ^ qflip;
       float f[8];
       widen16<DT>(qop[ks], f);
 #pragma unroll
@@ -1008,7 +1020,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   f32x4 acc[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY, l = 0.0f, accz = 0.0f;
+  float l = 0.0f, accz = 0.0f;
+  float mthr = -INFINITY, mc = 0.0f;  // rescale threshold (raw units), subtracted max * c
 
   const uint32_t lr = lane / LPR, lc = lane % LPR;  // row-major load: row, 16-code chunk
   char* kt = s_tile[wave];
@@ -1019,11 +1032,13 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   uint32_t tb = wave * TT;
   if (tb < cnt) {
     u32x4 kr[NL], vr[NL];
-    auto load_tile = [&](uint32_t t0) {
+    // rows past the partition (only in its last tile) reuse its last row
+    auto load_tile = [&](auto full_tag, uint32_t t0) {
+      constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const uint32_t li = t0 + i * RPL + lr;
-        const uint64_t off = s_row[li < cnt ? li : cnt - 1];  // one byte per element
+        const uint64_t off = s_row[FULL || li < cnt ? li : cnt - 1];  // one byte per element
         kr[i] = load16<TU::NT>(kbase + off);
         vr[i] = load16<TU::NT>(vbase + off);
       }
@@ -1041,13 +1056,10 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
         *reinterpret_cast<u32x4*>(vt + r * VROW + lc * 32 + 16) = hi;
       }
     };
-    load_tile(tb);
-    store_tile();
-    while (true) {
-      const uint32_t tn = tb + NW * TT;
-      const bool has_next = tn < cnt;
-      if (has_next) load_tile(tn);
-
+    // scores, online softmax and P.V of the tile at tb; FULL: every token is in the
+    // partition, so no score needs masking
+    auto compute_tile = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
       f32x4 sacc[2];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
@@ -1059,45 +1071,48 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
           sacc[g] = mfma_16x16x32<DT>(kop, qop[ks], sacc[g]);
         }
       }
-      float z[8];
+      float sv[8];
       float4 fac[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t t = tb + 16 * (j / 4) + 4 * q4 + (j % 4);
-        fac[j] = s_fac[t < cnt ? t : cnt - 1];
-        const float zz = fac[j].x * fmaf(-fac[j].y, qsum, sacc[j / 4][j % 4]) * a.scale_log2;
-        z[j] = t < cnt ? zz : -INFINITY;
+        fac[j] = s_fac[FULL || t < cnt ? t : cnt - 1];
+        sv[j] = fac[j].x * fmaf(-fac[j].y, qsum, sacc[j / 4][j % 4]);
+        if constexpr (!FULL) {
+          if (t >= cnt) sv[j] = -INFINITY;
+        }
       }
-      float mt = z[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) mt = fmaxf(mt, z[j]);
+      float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m, mt);
-      const float mu = mn == -INFINITY ? 0.0f : mn;
-      const float corr = __builtin_amdgcn_exp2f(m - mu);
-      m = mn;
-      l *= corr;
-      accz *= corr;
+      const bool need = mt > mthr;
+      if (__any(need)) {
+        const float mcn = need ? mt * c : mc;
+        // no earlier weights on first use (mthr still -inf): the accumulators are zero
+        const float corr = mthr == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mc - mcn);
+        if (need) mthr = mt + thr;
+        mc = mcn;
+        l *= corr;
+        accz *= corr;
 #pragma unroll
-      for (int n = 0; n < NB; ++n) acc[n] *= corr;
-
+        for (int n = 0; n < NB; ++n) acc[n] *= corr;
+      }
+      // masked scores are -inf and c > 0, so their weight is exactly 0. Columns
+      // col >= GT carry q = 0 and finite weights; a column of an MFMA result depends
+      // only on the same column of its B operand, so they never reach a served head.
       uint32_t pw[4];
       float psum = 0.0f, zsum = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(z[j] - mu);
-        const float p1 = __builtin_amdgcn_exp2f(z[j + 1] - mu);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[j], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[j + 1], c, -mc));
         const uint32_t b0 = round16<DT>(p0 * fac[j].z);
         const uint32_t b1 = round16<DT>(p1 * fac[j + 1].z);
         psum += p0 + p1;
         zsum = fmaf(widen_bits16<DT>(b0), fac[j].w, zsum);
         zsum = fmaf(widen_bits16<DT>(b1), fac[j + 1].w, zsum);
         pw[j / 2] = b0 | (b1 << 16);
-      }
-      if (col >= GT) {
-        pw[0] = pw[1] = pw[2] = pw[3] = 0u;
-        psum = zsum = 0.0f;
       }
       l += psum;
       accz += zsum;
@@ -1112,6 +1127,19 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
         const uint2 hi = lds_read_tr16(vrow0 + 16 * VROW + 32 * n);
         acc[n] = mfma_16x16x32<DT>(u32x4{lo.x, lo.y, hi.x, hi.y}, pop, acc[n]);
       }
+    };
+    if (tb + TT <= cnt) load_tile(std::true_type{}, tb);
+    else load_tile(std::false_type{}, tb);
+    store_tile();
+    while (true) {
+      const uint32_t tn = tb + NW * TT;
+      const bool has_next = tn < cnt;
+      if (has_next) {
+        if (tn + TT <= cnt) load_tile(std::true_type{}, tn);
+        else load_tile(std::false_type{}, tn);
+      }
+      if (tb + TT <= cnt) compute_tile(std::true_type{});
+      else compute_tile(std::false_type{});
       if (!has_next) break;
       store_tile();
       tb = tn;
@@ -1131,8 +1159,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
 #pragma unroll
       for (int r = 0; r < 4; ++r) s_acc[wave][col][16 * n + 4 * q4 + r] = acc[n][r] - accz;
     }
-    if (q4 == 0) {
-      s_m[wave][col] = m;
+    if (q4 == 0) {  // a wave that saw no token of the head reports max -inf and sum 0
+      s_m[wave][col] = mthr == -INFINITY ? -INFINITY : mc;
       s_l[wave][col] = l;
     }
   }
