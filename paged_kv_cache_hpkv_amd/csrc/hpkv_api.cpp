@@ -60,7 +60,10 @@ uint32_t max_parts_for(uint32_t max_context_len, uint32_t part_tokens) {
 // (measured on MI355X: +8 % for the GQA batch with two KV heads and 1024-token
 // partitions, +2-3 % for the VALU kernel with 1024-token partitions), but a
 // small batch needs the finer ones to fill the GPU: the coarsest shape whose
-// grid keeps kMinWorkgroups workgroups is taken, else the finest.
+// grid keeps kMinWorkgroups workgroups is taken, else the finest. Quantized
+// pools keep 512-token partitions; their VALU kernel may serve two KV heads
+// (a token's codes of one head are a single 128-byte line at d=128, and such
+// rows stream markedly slower than two heads' 256 contiguous bytes).
 struct DecodePlan {
   uint32_t gt, hpw, part_tokens;
 };
@@ -68,22 +71,28 @@ struct DecodePlan {
 DecodePlan plan_decode(int dtype, bool quant, uint32_t num_seqs, uint32_t num_q_heads,
                        uint32_t num_kv_heads, uint32_t head_dim, uint32_t max_context_len) {
   const uint32_t group = num_q_heads / num_kv_heads;
-  if (quant) return {hpkv::heads_per_workgroup_quant(dtype, head_dim, group), 1, kPartTokens};
-  const uint32_t gt = hpkv::heads_per_workgroup(dtype, head_dim, group);
-  DecodePlan c[3];
+  DecodePlan c[3];  // candidate shapes, coarsest first
   int n = 0;
-  if (hpkv::decode_on_matrix_cores(dtype, head_dim, group)) {
+  if (quant) {
+    const uint32_t gt = hpkv::heads_per_workgroup_quant(dtype, head_dim, group);
+    if (!hpkv::decode_quant_on_matrix_cores(dtype, head_dim, group) && gt == group &&
+        num_kv_heads % 2 == 0)
+      c[n++] = {gt, 2, kPartTokens};
+    c[n++] = {gt, 1, kPartTokens};
+  } else if (hpkv::decode_on_matrix_cores(dtype, head_dim, group)) {
+    const uint32_t gt = hpkv::heads_per_workgroup(dtype, head_dim, group);
     if (hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads) > 1) {
       c[n++] = {gt, 2, hpkv::kWidePartTokens};
       c[n++] = {gt, 2, kPartTokens};
     }
     c[n++] = {gt, 1, kPartTokens};
   } else {
+    const uint32_t gt = hpkv::heads_per_workgroup(dtype, head_dim, group);
     c[n++] = {gt, 1, hpkv::kWidePartTokens};
     c[n++] = {gt, 1, kPartTokens};
   }
   for (int i = 0; i + 1 < n; ++i) {
-    const uint64_t grid = uint64_t(num_kv_heads / c[i].hpw) * (group / gt) * num_seqs *
+    const uint64_t grid = uint64_t(num_kv_heads / c[i].hpw) * (group / c[i].gt) * num_seqs *
                           max_parts_for(max_context_len, c[i].part_tokens);
     if (grid >= kMinWorkgroups) return c[i];
   }

@@ -261,14 +261,13 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
     if (w.cnt > 0) {
       constexpr int EB = Elem<DT>::bytes;
       constexpr int CH = NKV * D * EB / 16;  // 16-byte chunks of the heads' rows
-      static_assert(CH <= NTH, "one chunk per thread");
       const uint64_t dst = s_row[w.cnt - 1] * EB;
       const uint64_t src = (uint64_t(w.s) * a.num_kv_heads + w.g) * D * EB;
-      if (tid < uint32_t(CH)) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.new_k) + src + tid * 16);
-        const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.new_v) + src + tid * 16);
-        *reinterpret_cast<u32x4*>(const_cast<char*>(static_cast<const char*>(a.k_cache)) + dst + tid * 16) = kv;
-        *reinterpret_cast<u32x4*>(const_cast<char*>(static_cast<const char*>(a.v_cache)) + dst + tid * 16) = vv;
+      for (uint32_t i = tid; i < uint32_t(CH); i += NTH) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.new_k) + src + i * 16);
+        const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.new_v) + src + i * 16);
+        *reinterpret_cast<u32x4*>(const_cast<char*>(static_cast<const char*>(a.k_cache)) + dst + i * 16) = kv;
+        *reinterpret_cast<u32x4*>(const_cast<char*>(static_cast<const char*>(a.v_cache)) + dst + i * 16) = vv;
       }
       if (slot_writer) {
         const uint64_t row = s_row[w.cnt - 1] / D;  // (slot * Hkv + g)
@@ -512,7 +511,11 @@ __device__ inline void codes16(const u32x4 v, float* f) {
   }
 }
 
-template <int DT, int QT, int D, int GT, class TU>
+// HPW adjacent KV heads per workgroup (whole GQA groups, GT == group): a token's
+// codes of those heads are HPW*D contiguous bytes, read as one row by HPW*D/16
+// lanes; each aligned group of D/16 lanes holds one head (lane head hw) and keeps
+// that head's softmax state. The query heads of the workgroup are contiguous.
+template <int DT, int QT, int D, int GT, class TU, int HPW>
 __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_kernel(
     const DecodeKernelArgs a) {
   constexpr int NW = TU::NW;
@@ -520,39 +523,50 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
   constexpr int NLOAD = TU::NLOAD;
   constexpr int EQ = Elem<DT>::bytes;  // bytes of a q / out element
   constexpr int EPL = 16;              // codes per 16-byte chunk
-  constexpr int LPR = D / EPL;         // lanes per token row
+  constexpr int LPH = D / EPL;         // lanes per head row
+  constexpr int LPR = HPW * LPH;       // lanes per token row (the workgroup's heads)
   constexpr int RPL = kWave / LPR;     // token rows per wave load
   constexpr int TT = RPL * NLOAD;      // tokens per wave tile
-  static_assert(D % EPL == 0 && LPR <= kWave && (LPR & (LPR - 1)) == 0, "unsupported head_dim");
+  constexpr int GW = HPW * GT;         // query heads of the workgroup
+  static_assert(D % EPL == 0 && LPR <= kWave && (LPH & (LPH - 1)) == 0 && (HPW & (HPW - 1)) == 0,
+                "unsupported head_dim");
   constexpr float kBias = QT == kI8 ? 128.0f : 0.0f;
 
   __shared__ uint64_t s_row[kMaxPartTokens];
-  __shared__ float4 s_fac[kMaxPartTokens];  // (ks, kz + bias, vs, vz + bias) of each token
-  __shared__ float s_m[NW][GT];
-  __shared__ float s_l[NW][GT];
-  __shared__ float s_acc[NW][GT][D];
+  __shared__ float4 s_fac[kMaxPartTokens][HPW];  // (ks, kz + bias, vs, vz + bias) per token, head
+  __shared__ float s_m[NW][GW];
+  __shared__ float s_l[NW][GW];
+  __shared__ float s_acc[NW][GW][D];
 
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t wave = threadIdx.x / kWave;
   const WorkItem item = grid_item<GT>(a);
   const uint64_t kvh = item.g;
   auto stage_factors = [&](uint32_t i, uint64_t phys) {
-    const uint64_t f = phys * a.num_kv_heads + kvh;
-    s_fac[i] = make_float4(a.k_scale[f], a.k_zero[f] + kBias, a.v_scale[f], a.v_zero[f] + kBias);
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+      const uint64_t f = phys * a.num_kv_heads + kvh + h;
+      s_fac[i][h] =
+          make_float4(a.k_scale[f], a.k_zero[f] + kBias, a.v_scale[f], a.v_zero[f] + kBias);
+    }
   };
   Partition w;
-  if (!setup_partition<DT, D, GT, NTH>(a, item, s_row, w, stage_factors)) return;
+  if (!setup_partition<DT, D, GW, NTH, decltype(stage_factors), HPW>(a, item, s_row, w,
+                                                                      stage_factors))
+    return;
   const uint32_t cnt = w.cnt;
   const uint64_t out_row0 = w.out_row0;
 
   const uint32_t row = lane / LPR;
-  const uint32_t c = lane % LPR;
+  const uint32_t hw = (lane % LPR) / LPH;  // the lane's KV head within the workgroup's
+  const uint32_t c = lane % LPH;           // the lane's chunk of that head's row
 
   // q of the lane's 16 elements of each head, and sum(q) over the head
   float qf[GT][EPL], qsum[GT];
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
-    const char* qp = static_cast<const char*>(a.q) + ((out_row0 + hh) * D + c * EPL) * EQ;
+    const char* qp =
+        static_cast<const char*>(a.q) + ((out_row0 + hw * GT + hh) * D + c * EPL) * EQ;
 #pragma unroll
     for (int h2 = 0; h2 < EPL * EQ / 16; ++h2) {
       float t[16 / EQ];
@@ -563,7 +577,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
     float sq = 0.0f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) sq += qf[hh][e];
-    qsum[hh] = row_sum<LPR>(sq);
+    qsum[hh] = row_sum<LPH>(sq);
   }
 
   float m[GT], l[GT], accz[GT], acc[GT][EPL];
@@ -576,8 +590,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
     for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.0f;
   }
 
-  const char* kbase = static_cast<const char*>(a.k_cache) + c * 16;
-  const char* vbase = static_cast<const char*>(a.v_cache) + c * 16;
+  const char* kbase = static_cast<const char*>(a.k_cache) + hw * D + c * 16;
+  const char* vbase = static_cast<const char*>(a.v_cache) + hw * D + c * 16;
 
   for (uint32_t tb = wave * TT; tb < cnt; tb += NW * TT) {
     u32x4 kr[NLOAD], vr[NLOAD];
@@ -589,7 +603,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
       const uint64_t off = s_row[ti];
       kr[k] = load16<TU::NT>(kbase + off);
       vr[k] = load16<TU::NT>(vbase + off);
-      fac[k] = s_fac[ti];
+      fac[k] = s_fac[ti][hw];
     }
 
     float sc[GT][NLOAD];
@@ -603,7 +617,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
         float d0 = 0.0f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) d0 = fmaf(qf[hh][e], kf[e], d0);
-        const float dot = row_sum<LPR>(d0);
+        const float dot = row_sum<LPH>(d0);
         const float z = fac[k].x * fmaf(-fac[k].y, qsum[hh], dot) * a.scale_log2;
         sc[hh][k] = valid ? z : -INFINITY;
       }
@@ -671,16 +685,16 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][hh][c * EPL + e] = acc[hh][e];
+      for (int e = 0; e < EPL; ++e) s_acc[wave][hw * GT + hh][c * EPL + e] = acc[hh][e];
       if (c == 0) {
-        s_m[wave][hh] = m[hh];
-        s_l[wave][hh] = l[hh];
+        s_m[wave][hw * GT + hh] = m[hh];
+        s_l[wave][hw * GT + hh] = l[hh];
       }
     }
   }
   __syncthreads();
 
-  finish_partition<DT, D, GT, NW>(a, w, s_m, s_l, s_acc);
+  finish_partition<DT, D, GW, NW>(a, w, s_m, s_l, s_acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1304,10 +1318,22 @@ template <int DT, int QT, int D, int GT>
 hipError_t launch_quant(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
   // Two-wave workgroups keep the most waves resident (the loop is latency-bound:
   // converting and FMA-ing one-byte codes leaves no loads in flight for long);
-  // 4-head tiles hold 64 q floats per lane, so they load two rows per lane.
+  // 4-head tiles hold 64 q floats per lane, so they load two rows per lane. Two
+  // adjacent KV heads per workgroup read 2*d contiguous bytes of each token row:
+  // rows of one 128-byte line per head stream markedly slower on MI355X.
   using TU = Tune<2, GT >= 4 ? 2 : 8, true, 2>;
-  hipLaunchKernelGGL((decode_partition_quant_kernel<DT, QT, D, GT, TU>), dim3(uint32_t(nwg)),
-                     dim3(TU::NW * kWave), 0, stream, a);
+  switch (a.kv_per_wg) {
+    case 1:
+      hipLaunchKernelGGL((decode_partition_quant_kernel<DT, QT, D, GT, TU, 1>),
+                         dim3(uint32_t(nwg)), dim3(TU::NW * kWave), 0, stream, a);
+      break;
+    case 2:
+      hipLaunchKernelGGL((decode_partition_quant_kernel<DT, QT, D, GT, TU, 2>),
+                         dim3(uint32_t(nwg)), dim3(TU::NW * kWave), 0, stream, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -1398,6 +1424,10 @@ uint32_t heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group) {
 
 bool decode_on_matrix_cores(int dtype, uint32_t head_dim, uint32_t group) {
   return mfma_eligible(dtype, head_dim, group);
+}
+
+bool decode_quant_on_matrix_cores(int dtype, uint32_t head_dim, uint32_t group) {
+  return mfma_quant_eligible(dtype, head_dim, group);
 }
 
 uint32_t kv_heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group,

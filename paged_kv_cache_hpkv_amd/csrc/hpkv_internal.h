@@ -128,8 +128,10 @@ hipError_t launch_prefill(int dtype, uint32_t head_dim, const PrefillKernelArgs&
 // Query heads served by one decode workgroup for a GQA group of `group` heads
 // (the matrix-core path takes up to 16 heads of a group at once).
 uint32_t heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group);
-// Whether the 16/32-bit decode of a shape runs on the matrix cores.
+// Whether the 16/32-bit decode of a shape runs on the matrix cores, and the
+// same for quantized pools.
 bool decode_on_matrix_cores(int dtype, uint32_t head_dim, uint32_t group);
+bool decode_quant_on_matrix_cores(int dtype, uint32_t head_dim, uint32_t group);
 // Most adjacent KV heads one decode workgroup may serve (two only when a
 // workgroup takes whole GQA groups on the matrix cores).
 uint32_t kv_heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group,
