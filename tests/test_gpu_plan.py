@@ -1,0 +1,101 @@
+"""GPU parity across the decode launch plan's shapes.
+
+The decode picks a launch shape per call: the coarsest one (two KV heads per
+workgroup and/or 1024-token partitions) whose grid still has 256 workgroups,
+else finer ones. Batch sizes here straddle those thresholds so that every
+shape runs: for each case the partition size the library reports is checked
+against the planned one, then the full step (slot mapping, store, decode) is
+compared with the oracle, and the split partition/reduce entry points must
+reproduce the decode bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_hpkv_amd as hpkv
+import workloads
+from paths import check_step, decode_errors, host_bits, host_threads, used_slots
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _shape(name, ctx, hq, hkv, d=128, dtype="bf16", bs=16, seed=11):
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx, dtype=np.int32)
+    num_pages, seq_ptr, bt = workloads._random_pool_tables(rng, ctx, bs, "u32")
+    return workloads.Workload(name, dtype, "u32", hq, hkv, d, bs, num_pages, ctx, seq_ptr, bt,
+                              d ** -0.5, chunks=workloads._decode_step_chunks(ctx), seed=seed)
+
+
+# (name, context lengths, Hq, Hkv, planned partition tokens)
+CASES = [
+    # matrix cores, GQA 32/8: two KV heads & 1024 (4*8*8 = 256 workgroups) ...
+    ("mfma-2h-1024", [8192] * 8, 32, 8, 1024),
+    # ... two KV heads & 512 (4*7*8 = 224 < 256; 4*7*16 = 448) ...
+    ("mfma-2h-512", [8192] * 6 + [1000], 32, 8, 512),
+    # ... one KV head & 512 (4*1*4 = 16 and 4*1*8 = 32 are below 256)
+    ("mfma-1h-512", [4096], 32, 8, 512),
+    # VALU kernel (MHA 32/32): 1024 (32*2*4 = 256), then 512 (32*1*4 = 128)
+    ("valu-1024", [4096, 2500], 32, 32, 1024),
+    ("valu-512", [4096], 32, 32, 512),
+]
+
+
+@pytest.mark.parametrize("name,ctx,hq,hkv,part", CASES, ids=[c[0] for c in CASES])
+def test_decode_plan_shapes(name, ctx, hq, hkv, part):
+    w = _shape(name, ctx, hq, hkv)
+    got = hpkv.hpkv_paged_attention_decode_partition_tokens(
+        w.torch_dtype, w.num_seqs, hq, hkv, w.head_dim, w.page_size, w.max_context_len)
+    assert got == part
+    r = check_step(w)
+    print(f"[plan] {name} part={part} max err {r['max_err']:.3e}", flush=True)
+    # the split entry points plan the same partitions as the one-call decode
+    t = r["tensors"]
+    bt = torch.from_numpy(w.block_table).to(DEV)
+    sp = torch.from_numpy(w.seq_ptr).to(DEV)
+    ctx_t = torch.from_numpy(w.context_lens).to(DEV)
+    ws = hpkv.alloc_workspace(t.q, t.k_cache, w.max_context_len)
+    out = torch.full_like(t.q, float("nan"))
+    hpkv.hpkv_paged_attention_decode_partitions(t.q, t.k_cache, t.v_cache, bt, sp, ctx_t, w.scale,
+                                                w.max_context_len, ws, out)
+    hpkv.hpkv_paged_attention_decode_reduce(ctx_t, hkv, w.page_size, w.max_context_len, ws, out)
+    torch.cuda.synchronize()
+    assert host_bits(out).tobytes() == host_bits(r["out"]).tobytes()
+
+
+# quantized pools, VALU kernel (MHA 32/32): two KV heads per workgroup when
+# 16 head pairs x sequences x partitions >= 256, else one
+QCASES = [("q-2h", [4096] * 4, 32, 32), ("q-1h", [4096], 32, 32), ("q-2h-g2", [3000] * 16, 16, 8)]
+
+
+@pytest.mark.parametrize("kv", ["fp8", "i8"])
+@pytest.mark.parametrize("name,ctx,hq,hkv", QCASES, ids=[c[0] for c in QCASES])
+def test_quant_decode_plan_shapes(name, ctx, hq, hkv, kv):
+    w = _shape(name, ctx, hq, hkv, seed=13)
+    print(f"[plan quant] {name} {kv}", flush=True)
+    t = workloads.make_tensors(w, DEV)
+    qt = workloads.make_quant_tensors(w, kv, DEV)
+    used = torch.zeros(w.num_pages * w.page_size, dtype=torch.bool)
+    used[torch.from_numpy(used_slots(w))] = True
+    pages = used.view(w.num_pages, w.page_size).any(1).to(DEV)
+    for sc in (qt.k_scale, qt.v_scale):  # pages no sequence references: NaN scales
+        sc[~pages] = float("nan")
+    bt = torch.from_numpy(w.block_table).to(DEV)
+    sp = torch.from_numpy(w.seq_ptr).to(DEV)
+    ctx_t = torch.from_numpy(w.context_lens).to(DEV)
+    out = torch.empty_like(t.q)
+    ws = hpkv.alloc_workspace(t.q, qt.k_codes, w.max_context_len)
+    hpkv.hpkv_paged_attention_decode_quant(kv, t.q, qt.k_codes, qt.v_codes, qt.k_scale,
+                                           qt.k_zero, qt.v_scale, qt.v_zero, bt, sp, ctx_t,
+                                           w.scale, w.max_context_len, ws, out)
+    torch.cuda.synchronize()
+    hs = {n: getattr(qt, n).cpu().numpy() for n in
+          ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero")}
+    _, ref = oracle.paged_attention_decode_quant(
+        w.dtype, kv, host_bits(t.q), hs["k_codes"], hs["v_codes"], hs["k_scale"], hs["k_zero"],
+        hs["v_scale"], hs["v_zero"], w.block_table, w.seq_ptr, w.context_lens, w.scale,
+        host_threads())
+    max_err, ratio, finite = decode_errors(w.dtype, host_bits(out), ref)
+    assert finite and ratio <= 1.0, max_err
