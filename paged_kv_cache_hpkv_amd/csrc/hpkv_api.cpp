@@ -88,6 +88,8 @@ DecodePlan plan_decode(int dtype, bool quant, uint32_t num_seqs, uint32_t num_q_
     c[n++] = {gt, 1, kPartTokens};
   } else {
     const uint32_t gt = hpkv::heads_per_workgroup(dtype, head_dim, group);
+    if (hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads) > 1)
+      c[n++] = {gt, 2, hpkv::kWidePartTokens};
     c[n++] = {gt, 1, hpkv::kWidePartTokens};
     c[n++] = {gt, 1, kPartTokens};
   }

@@ -8,17 +8,21 @@
 // section "Element lookup through the block table").
 //
 // Design (HBM-bound gather; arithmetic intensity <= Hq/Hkv flop per byte):
-//  * One workgroup (4 waves) per (sequence, KV head, query-head tile,
-//    context partition of part_tokens tokens). All query heads of the tile
-//    are served from one pass over the partition's K and V, so a GQA group
-//    reads its KV once.
+//  * One workgroup per (sequence, head tile, context partition of part_tokens
+//    tokens); a head tile is a tile of query heads of one KV head, or the
+//    whole groups of two adjacent KV heads. All query heads of the tile are
+//    served from one pass over the partition's K and V, so a GQA group reads
+//    its KV once. The host picks the tile and the partition size per call.
+//  * Kernels: the VALU kernel below (one query head per KV head, fp32, groups
+//    not divisible by 4), the matrix-core kernel (16-bit GQA groups of 4+),
+//    and both for quantized pools; the reduce kernel merges the partitions.
 //  * The workgroup first resolves every token of its partition to a pool row
 //    through the block table and keeps the row offsets in LDS; the token
 //    loop then needs no division and no table reads.
-//  * A 16-byte vector load per lane; a token row of head_dim elements is
-//    covered by LPR = head_dim*bytes/16 adjacent lanes, so one wave load
-//    fetches RPL = 64/LPR whole rows (coalesced 2x128 B per 256 B row at
-//    d=128 bf16). Each wave keeps 8 K and 8 V loads in flight per tile.
+//  * VALU kernel: a 16-byte vector load per lane; a token row of head_dim
+//    elements is covered by LPR = head_dim*bytes/16 adjacent lanes, so one
+//    wave load fetches RPL = 64/LPR whole rows (coalesced 2x128 B per 256 B
+//    row at d=128 bf16). Each wave keeps 8 K and 8 V loads in flight per tile.
 //  * q.k partial sums are reduced across the LPR lanes of a row with DPP
 //    (quad_perm, row_half_mirror, row_mirror); every lane of the row then
 //    holds the score, so the same lanes weight their own V chunk: no LDS
@@ -315,7 +319,11 @@ __device__ inline void finish_partition(const DecodeKernelArgs& a, const Partiti
   }
 }
 
-template <int DT, int D, int GT, class TU>
+// HPW adjacent KV heads per workgroup (whole GQA groups, GT == group): a token's
+// rows of those heads are HPW*D contiguous elements, read as one row by HPW*LPH
+// lanes; each aligned group of LPH lanes holds one head (lane head hw) and keeps
+// that head's softmax state. The query heads of the workgroup are contiguous.
+template <int DT, int D, int GT, class TU, int HPW>
 __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel(
     const DecodeKernelArgs a) {
   constexpr int NW = TU::NW;
@@ -325,27 +333,31 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
   constexpr int EPL = 16 / EB;       // elements per 16-byte chunk
   constexpr int CPR = D / EPL;       // chunks per token row
   constexpr int CPL = TU::CPL < CPR ? TU::CPL : CPR;  // chunks per lane
-  constexpr int LPR = CPR / CPL;     // lanes per token row
+  constexpr int LPH = CPR / CPL;     // lanes per head row
+  constexpr int LPR = HPW * LPH;     // lanes per token row (the workgroup's heads)
   constexpr int RPL = kWave / LPR;   // token rows per wave load
   constexpr int TT = RPL * NLOAD;    // tokens per wave tile
   constexpr int VPL = CPL * EPL;     // elements of a row per lane
-  static_assert(CPR % CPL == 0 && LPR <= kWave && (LPR & (LPR - 1)) == 0,
+  constexpr int GW = HPW * GT;       // query heads of the workgroup
+  static_assert(CPR % CPL == 0 && LPR <= kWave && (LPH & (LPH - 1)) == 0 &&
+                    (HPW & (HPW - 1)) == 0,
                 "unsupported head_dim");
 
   __shared__ uint64_t s_row[kWidePartTokens];
-  __shared__ float s_m[NW][GT];
-  __shared__ float s_l[NW][GT];
-  __shared__ float s_acc[NW][GT][D];
+  __shared__ float s_m[NW][GW];
+  __shared__ float s_l[NW][GW];
+  __shared__ float s_acc[NW][GW][D];
 
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t wave = threadIdx.x / kWave;
   Partition w;
-  if (!setup_partition<DT, D, GT, NTH>(a, grid_item<GT>(a), s_row, w)) return;
+  if (!setup_partition<DT, D, GW, NTH, NoTokenHook, HPW>(a, grid_item<GT>(a), s_row, w)) return;
   const uint32_t cnt = w.cnt;
   const uint64_t out_row0 = w.out_row0;
 
-  const uint32_t row = lane / LPR;  // which row of a wave load this lane reads
-  const uint32_t c = lane % LPR;    // lane's chunks of that row: j*LPR + c, j < CPL
+  const uint32_t row = lane / LPR;         // which row of a wave load this lane reads
+  const uint32_t hw = (lane % LPR) / LPH;  // the lane's KV head within the workgroup's
+  const uint32_t c = lane % LPH;           // lane's chunks of the head row: j*LPH + c, j < CPL
 
   u32x4 qv[GT][CPL];
 #pragma unroll
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const char* qp = static_cast<const char*>(a.q) +
-                       ((out_row0 + hh) * D + (j * LPR + c) * EPL) * EB;
+                       ((out_row0 + hw * GT + hh) * D + (j * LPH + c) * EPL) * EB;
       qv[hh][j] = *reinterpret_cast<const u32x4*>(qp);
     }
   }
@@ -367,8 +379,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
     for (int e = 0; e < VPL; ++e) acc[hh][e] = 0.0f;
   }
 
-  const char* kbase = static_cast<const char*>(a.k_cache) + c * 16;
-  const char* vbase = static_cast<const char*>(a.v_cache) + c * 16;
+  const char* kbase = static_cast<const char*>(a.k_cache) + hw * D * EB + c * 16;
+  const char* vbase = static_cast<const char*>(a.v_cache) + hw * D * EB + c * 16;
 
   for (uint32_t tb = wave * TT; tb < cnt; tb += NW * TT) {
     u32x4 kr[NLOAD][CPL], vr[NLOAD][CPL];
@@ -377,9 +389,9 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
       const uint32_t li = tb + k * RPL + row;
       const uint64_t off = s_row[li < cnt ? li : cnt - 1] * EB;
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) kr[k][j] = load16<TU::NT>(kbase + off + j * LPR * 16);
+      for (int j = 0; j < CPL; ++j) kr[k][j] = load16<TU::NT>(kbase + off + j * LPH * 16);
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) vr[k][j] = load16<TU::NT>(vbase + off + j * LPR * 16);
+      for (int j = 0; j < CPL; ++j) vr[k][j] = load16<TU::NT>(vbase + off + j * LPH * 16);
     }
 
     float sc[GT][NLOAD];
@@ -391,7 +403,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
         float part_dot = dot16<DT>(kr[k][0], qv[hh][0]);
 #pragma unroll
         for (int j = 1; j < CPL; ++j) part_dot += dot16<DT>(kr[k][j], qv[hh][j]);
-        const float z = row_sum<LPR>(part_dot) * a.scale_log2;
+        const float z = row_sum<LPH>(part_dot) * a.scale_log2;
         sc[hh][k] = valid ? z : -INFINITY;
       }
     }
@@ -459,17 +471,17 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
       for (int j = 0; j < CPL; ++j) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
-          s_acc[wave][hh][(j * LPR + c) * EPL + e] = acc[hh][j * EPL + e];
+          s_acc[wave][hw * GT + hh][(j * LPH + c) * EPL + e] = acc[hh][j * EPL + e];
       }
       if (c == 0) {
-        s_m[wave][hh] = m[hh];
-        s_l[wave][hh] = l[hh];
+        s_m[wave][hw * GT + hh] = m[hh];
+        s_l[wave][hw * GT + hh] = l[hh];
       }
     }
   }
   __syncthreads();
 
-  finish_partition<DT, D, GT, NW>(a, w, s_m, s_l, s_acc);
+  finish_partition<DT, D, GW, NW>(a, w, s_m, s_l, s_acc);
 }
 
 
@@ -1243,8 +1255,22 @@ struct DefaultTune {
 template <int DT, int D, int GT>
 hipError_t launch_pd(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
   using TU = typename DefaultTune<DT, D, GT>::type;
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, GT, TU>), dim3(uint32_t(nwg)),
-                     dim3(TU::NW * kWave), 0, stream, a);
+  switch (a.kv_per_wg) {
+    case 1:
+      hipLaunchKernelGGL((decode_partition_kernel<DT, D, GT, TU, 1>), dim3(uint32_t(nwg)),
+                         dim3(TU::NW * kWave), 0, stream, a);
+      break;
+    case 2:
+      if constexpr (2 * D * Elem<DT>::bytes <= 16 * kWave) {
+        hipLaunchKernelGGL((decode_partition_kernel<DT, D, GT, TU, 2>), dim3(uint32_t(nwg)),
+                           dim3(TU::NW * kWave), 0, stream, a);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -1432,9 +1458,10 @@ bool decode_quant_on_matrix_cores(int dtype, uint32_t head_dim, uint32_t group) 
 
 uint32_t kv_heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group,
                                 uint32_t num_kv_heads) {
-  if (!mfma_eligible(dtype, head_dim, group) || heads_per_workgroup(dtype, head_dim, group) != group)
-    return 1;
-  return num_kv_heads % 2 == 0 ? 2u : 1u;
+  if (heads_per_workgroup(dtype, head_dim, group) != group || num_kv_heads % 2 != 0) return 1;
+  if (mfma_eligible(dtype, head_dim, group)) return 2;
+  // VALU kernel: the two heads' rows must fit one wave's lanes (16 bytes each)
+  return 2 * head_dim * uint32_t(dtype_bytes(dtype)) <= 16u * kWave ? 2u : 1u;
 }
 
 hipError_t launch_decode_partitions(int dtype, uint32_t head_dim, const DecodeKernelArgs& a,
