@@ -71,7 +71,7 @@ struct DecodePlan {
 DecodePlan plan_decode(int dtype, bool quant, uint32_t num_seqs, uint32_t num_q_heads,
                        uint32_t num_kv_heads, uint32_t head_dim, uint32_t max_context_len) {
   const uint32_t group = num_q_heads / num_kv_heads;
-  DecodePlan c[3];  // candidate shapes, coarsest first
+  DecodePlan c[4];  // candidate shapes, coarsest first
   int n = 0;
   if (quant) {
     const uint32_t gt = hpkv::heads_per_workgroup_quant(dtype, head_dim, group);
@@ -88,8 +88,9 @@ DecodePlan plan_decode(int dtype, bool quant, uint32_t num_seqs, uint32_t num_q_
     c[n++] = {gt, 1, kPartTokens};
   } else {
     const uint32_t gt = hpkv::heads_per_workgroup(dtype, head_dim, group);
-    if (hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads) > 1)
-      c[n++] = {gt, 2, hpkv::kWidePartTokens};
+    for (uint32_t h = hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads); h > 1;
+         h /= 2)
+      c[n++] = {gt, h, hpkv::kWidePartTokens};
     c[n++] = {gt, 1, hpkv::kWidePartTokens};
     c[n++] = {gt, 1, kPartTokens};
   }

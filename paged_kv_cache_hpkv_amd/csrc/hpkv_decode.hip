@@ -1268,6 +1268,14 @@ hipError_t launch_pd(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream
       } else {
         return hipErrorInvalidValue;
       }
+    case 4:
+      if constexpr (4 * D * Elem<DT>::bytes <= 16 * kWave) {
+        hipLaunchKernelGGL((decode_partition_kernel<DT, D, GT, TU, 4>), dim3(uint32_t(nwg)),
+                           dim3(TU::NW * kWave), 0, stream, a);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
     default:
       return hipErrorInvalidValue;
   }
@@ -1460,8 +1468,13 @@ uint32_t kv_heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group,
                                 uint32_t num_kv_heads) {
   if (heads_per_workgroup(dtype, head_dim, group) != group || num_kv_heads % 2 != 0) return 1;
   if (mfma_eligible(dtype, head_dim, group)) return 2;
-  // VALU kernel: the two heads' rows must fit one wave's lanes (16 bytes each)
-  return 2 * head_dim * uint32_t(dtype_bytes(dtype)) <= 16u * kWave ? 2u : 1u;
+  // VALU kernel: heads until a token's row for the workgroup is ~512 contiguous
+  // bytes (measured on MI355X: 256-byte head rows stream best two at a time,
+  // 128-byte ones four at a time; wider rows were slower), at most 4
+  const uint32_t row = head_dim * uint32_t(dtype_bytes(dtype));
+  uint32_t h = 1;
+  while (h < 4 && 2 * h * row <= 512 && num_kv_heads % (2 * h) == 0) h *= 2;
+  return h;
 }
 
 hipError_t launch_decode_partitions(int dtype, uint32_t head_dim, const DecodeKernelArgs& a,

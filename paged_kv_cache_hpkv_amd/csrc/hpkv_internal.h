@@ -132,8 +132,9 @@ uint32_t heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group);
 // same for quantized pools.
 bool decode_on_matrix_cores(int dtype, uint32_t head_dim, uint32_t group);
 bool decode_quant_on_matrix_cores(int dtype, uint32_t head_dim, uint32_t group);
-// Most adjacent KV heads one decode workgroup may serve (two only when a
-// workgroup takes whole GQA groups on the matrix cores).
+// Most adjacent KV heads one decode workgroup may serve (whole GQA groups and
+// an even number of KV heads only): two on the matrix cores; on the VALU kernel
+// as many as make a token's row for the workgroup ~512 contiguous bytes, up to 4.
 uint32_t kv_heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group,
                                 uint32_t num_kv_heads);
 // The same for quantized pools.

@@ -29,23 +29,25 @@ def _shape(name, ctx, hq, hkv, d=128, dtype="bf16", bs=16, seed=11):
                               d ** -0.5, chunks=workloads._decode_step_chunks(ctx), seed=seed)
 
 
-# (name, context lengths, Hq, Hkv, planned partition tokens)
+# (name, context lengths, Hq, Hkv, planned partition tokens, head_dim)
 CASES = [
     # matrix cores, GQA 32/8: two KV heads & 1024 (4*8*8 = 256 workgroups) ...
-    ("mfma-2h-1024", [8192] * 8, 32, 8, 1024),
+    ("mfma-2h-1024", [8192] * 8, 32, 8, 1024, 128),
     # ... two KV heads & 512 (4*7*8 = 224 < 256; 4*7*16 = 448) ...
-    ("mfma-2h-512", [8192] * 6 + [1000], 32, 8, 512),
+    ("mfma-2h-512", [8192] * 6 + [1000], 32, 8, 512, 128),
     # ... one KV head & 512 (4*1*4 = 16 and 4*1*8 = 32 are below 256)
-    ("mfma-1h-512", [4096], 32, 8, 512),
+    ("mfma-1h-512", [4096], 32, 8, 512, 128),
     # VALU kernel (MHA 32/32): 1024 (32*2*4 = 256), then 512 (32*1*4 = 128)
-    ("valu-1024", [4096, 2500], 32, 32, 1024),
-    ("valu-512", [4096], 32, 32, 512),
+    ("valu-1024", [4096, 2500], 32, 32, 1024, 128),
+    ("valu-512", [4096], 32, 32, 512, 128),
+    # VALU kernel at d=64 (128-byte head rows): four KV heads & 1024 (4*16*4 = 256)
+    ("valu-4h-1024-d64", [4096] * 16, 16, 16, 1024, 64),
 ]
 
 
-@pytest.mark.parametrize("name,ctx,hq,hkv,part", CASES, ids=[c[0] for c in CASES])
-def test_decode_plan_shapes(name, ctx, hq, hkv, part):
-    w = _shape(name, ctx, hq, hkv)
+@pytest.mark.parametrize("name,ctx,hq,hkv,part,d", CASES, ids=[c[0] for c in CASES])
+def test_decode_plan_shapes(name, ctx, hq, hkv, part, d):
+    w = _shape(name, ctx, hq, hkv, d=d)
     got = hpkv.hpkv_paged_attention_decode_partition_tokens(
         w.torch_dtype, w.num_seqs, hq, hkv, w.head_dim, w.page_size, w.max_context_len)
     assert got == part
