@@ -920,11 +920,13 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
 // ---------------------------------------------------------------------------
 // Quantized pools, GQA groups of 4 or more query heads, 16-bit q: the matrix-
 // core kernel above on one-byte codes. Each lane loads 16 codes of a row
-// (half the bytes per token of a 16-bit pool) and writes them to the wave's
-// LDS tile as exact 16-bit values (int8 codes as code + 128 in 0..255, E4M3
-// values; both are exact in bf16 and in f16), so the two products are those
-// of the 16-bit kernel over raw code values. The page factors of token t enter
-// around them:
+// (half the bytes per token of a 16-bit pool). V codes go to the wave's LDS tile
+// as exact 16-bit values (int8 codes as code + 128 in 0..255, E4M3 values; both
+// exact in bf16 and in f16); K stays one byte per code in LDS, and each lane
+// converts the 8 codes of its operand as it reads them. Every code is converted
+// once either way, and the smaller tile lets four workgroups share a CU instead
+// of three. The two products are those of the 16-bit kernel over raw code
+// values; the page factors of token t enter around them:
 //   score = ks_t * (q . value_t - kz_t * sum(q)),   weight' = p_t * vs_t,
 //   out   = (sum_t weight'_t value_t - sum_t weight'_t vz_t) / sum_t p_t,
 // with the bias of int8 codes folded into the zero points. V^T is read with the
@@ -979,6 +981,34 @@ __device__ inline void codes16_to_bits16(const u32x4 c, u32x4& lo, u32x4& hi) {
              pack_exact16<DT>(f[12], f[13]), pack_exact16<DT>(f[14], f[15])};
 }
 
+// Eight codes (two words) as exact 16-bit values of the q type: one operand.
+template <int DT, int QT>
+__device__ inline u32x4 codes8_to_bits16(const uint2 c) {
+  const uint32_t w[2] = {c.x, c.y};
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if constexpr (QT == kFP8) {  // packed scaled conversion with scale 1: exact
+      if constexpr (DT == kBF16) {
+        const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+        const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+        __builtin_memcpy(&r[2 * i], &a, 4);
+        __builtin_memcpy(&r[2 * i + 1], &b, 4);
+      } else {
+        const auto a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
+        const auto b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
+        __builtin_memcpy(&r[2 * i], &a, 4);
+        __builtin_memcpy(&r[2 * i + 1], &b, 4);
+      }
+    } else {  // int8 as code + 128 (sign bit flipped): 0..255, exact in fp32 and 16 bits
+      const uint32_t u = w[i] ^ 0x80808080u;
+      r[2 * i] = pack_exact16<DT>(float(u & 0xffu), float((u >> 8) & 0xffu));
+      r[2 * i + 1] = pack_exact16<DT>(float((u >> 16) & 0xffu), float(u >> 24));
+    }
+  }
+  return u32x4{r[0], r[1], r[2], r[3]};
+}
+
 template <int DT, int QT, int D, int GT, class TU>
 __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_quant_kernel(
     const DecodeKernelArgs a) {
@@ -989,7 +1019,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   constexpr int RPL = kWave / LPR;  // rows per wave load
   constexpr int TT = 32;            // tokens per tile
   constexpr int NL = TT / RPL;      // wave loads per tile, for K and for V
-  constexpr int KROW = D * 2 + 16;  // LDS bytes per K row (16-byte lane reads)
+  constexpr int KROW = D + 16;      // LDS bytes per K row of codes (8-byte lane reads)
   constexpr int VROW = D * 2 + 32;  // LDS bytes per V row (transposing 8-byte reads)
   constexpr int KS = D / 32;
   constexpr int NB = D / 16;
@@ -1073,10 +1103,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const uint32_t r = i * RPL + lr;
+        *reinterpret_cast<u32x4*>(kt + r * KROW + lc * 16) = kr[i];  // K stays codes
         u32x4 lo, hi;
-        codes16_to_bits16<DT, QT>(kr[i], lo, hi);
-        *reinterpret_cast<u32x4*>(kt + r * KROW + lc * 32) = lo;
-        *reinterpret_cast<u32x4*>(kt + r * KROW + lc * 32 + 16) = hi;
         codes16_to_bits16<DT, QT>(vr[i], lo, hi);
         *reinterpret_cast<u32x4*>(vt + r * VROW + lc * 32) = lo;
         *reinterpret_cast<u32x4*>(vt + r * VROW + lc * 32 + 16) = hi;
@@ -1092,9 +1120,9 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
         sacc[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 kop =
-              *reinterpret_cast<const u32x4*>(kt + (16 * g + col) * KROW + (32 * ks + 8 * q4) * 2);
-          sacc[g] = mfma_16x16x32<DT>(kop, qop[ks], sacc[g]);
+          const uint2 kc =
+              *reinterpret_cast<const uint2*>(kt + (16 * g + col) * KROW + 32 * ks + 8 * q4);
+          sacc[g] = mfma_16x16x32<DT>(codes8_to_bits16<DT, QT>(kc), qop[ks], sacc[g]);
         }
       }
       float sv[8];
