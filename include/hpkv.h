@@ -165,11 +165,13 @@ int hpkv_store_kvcache(int dtype, const void* key, const void* value, void* k_ca
  * hpkv_paged_attention_decode_workspace_size  (host)
  *
  * Bytes of device workspace hpkv_paged_attention_decode needs for a batch of
- * num_seqs sequences no longer than max_context_len tokens (the split-context
- * partials: one fp32 (max, sum) pair and one fp32 head_dim vector per
- * sequence, query head and context partition), counted with the smallest
+ * num_seqs sequences no longer than max_context_len tokens: the split-context
+ * partials (one fp32 (max, sum) pair and one fp32 head_dim vector per
+ * sequence, query head and context partition), then the dispatch order of the
+ * (sequence, partition) pairs (one uint32 each), counted with the smallest
  * partition the library uses, so it is enough for every num_kv_heads and for
- * the quantized decode. 0 on invalid arguments.
+ * the quantized decode. 0 when every sequence fits one partition (no
+ * workspace is then read or written) and on invalid arguments.
  * ------------------------------------------------------------------------- */
 size_t hpkv_paged_attention_decode_workspace_size(int dtype, uint32_t num_seqs,
                                                   uint32_t num_q_heads, uint32_t head_dim,
@@ -220,8 +222,13 @@ uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_se
  * Malformed contents (caller error): a sequence with n < 0,
  * n > max_context_len, n beyond its slice, or a page id >= num_pages in the
  * pages it reads, gets NaN in all its outputs.
- * Two kernels are enqueued: the split-context partition pass, then the
- * log-sum-exp reduce (skipped per sequence when one partition covers it).
+ * Enqueued: a one-workgroup ordering pass that lists the (sequence,
+ * partition) pairs longest partition first in the workspace (skipped when the
+ * grid has at most 512 workgroups, or no workspace is needed), the
+ * split-context partition pass, which takes its work in that order so the
+ * launch does not end on a few long partitions, then the log-sum-exp reduce
+ * (skipped per sequence when one partition covers it). Results do not depend
+ * on the order.
  * ------------------------------------------------------------------------- */
 int hpkv_paged_attention_decode(int dtype, int index_type, const void* q, const void* k_cache,
                                 const void* v_cache, const void* block_table,
@@ -232,9 +239,10 @@ int hpkv_paged_attention_decode(int dtype, int index_type, const void* q, const 
                                 uint32_t max_context_len, void* workspace, size_t workspace_bytes,
                                 void* out, void* stream);
 
-/* The two launches of hpkv_paged_attention_decode, separately: the partition
- * pass (writes `out` for sequences covered by one partition, partials for the
- * rest) and the reduce (merges the partials into `out`). Calling them in this
+/* The two passes of hpkv_paged_attention_decode, separately: the partition
+ * pass (the ordering kernel, then the partition kernel, which writes `out` for
+ * sequences covered by one partition and partials for the rest) and the
+ * reduce (merges the partials into `out`). Calling them in this
  * order on one stream with the same arguments is equivalent to
  * hpkv_paged_attention_decode. Used to time the kernels one by one. */
 int hpkv_paged_attention_decode_partitions(int dtype, int index_type, const void* q,

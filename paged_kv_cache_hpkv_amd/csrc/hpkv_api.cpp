@@ -23,6 +23,9 @@ static_assert(kPartTokens <= hpkv::kWidePartTokens, "the workspace is sized for 
 // partitions beat 1024 one-head workgroups (44 vs 47 us); at 1 x 4096 tokens,
 // 64 one-head workgroups beat 16 two-head ones (13 vs 23 us).
 constexpr uint64_t kMinWorkgroups = 256;
+// Grids up to this many workgroups are resident on the 256 CUs at once (two
+// per CU), so their dispatch order does not matter.
+constexpr uint64_t kOrderMinWorkgroups = 512;
 
 bool valid_dtype(int dt) { return dt == HPKV_F32 || dt == HPKV_F16 || dt == HPKV_BF16; }
 bool valid_index(int it) { return it == HPKV_INDEX_U32 || it == HPKV_INDEX_U64; }
@@ -103,19 +106,21 @@ DecodePlan plan_decode(int dtype, bool quant, uint32_t num_seqs, uint32_t num_q_
 }
 
 struct WorkspaceLayout {
-  size_t ml_offset, o_offset, bytes;
+  size_t ml_offset, o_offset, order_offset, bytes;
 };
 
 WorkspaceLayout workspace_layout(uint32_t num_seqs, uint32_t num_q_heads, uint32_t head_dim,
                                  uint32_t max_context_len, uint32_t part_tokens) {
   const uint64_t mp = max_parts_for(max_context_len, part_tokens);
-  WorkspaceLayout w{0, 0, 0};
+  WorkspaceLayout w{0, 0, 0, 0};
   if (mp <= 1) return w;  // every sequence fits one partition: no partials
   const uint64_t rows = uint64_t(num_seqs) * num_q_heads * mp;
   const uint64_t ml_bytes = (rows * sizeof(float2) + 255) & ~uint64_t(255);
+  const uint64_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~uint64_t(255);
   w.ml_offset = 0;
   w.o_offset = ml_bytes;
-  w.bytes = ml_bytes + rows * head_dim * sizeof(float);
+  w.order_offset = ml_bytes + o_bytes;  // then one u32 per (sequence, partition)
+  w.bytes = w.order_offset + uint64_t(num_seqs) * mp * sizeof(uint32_t);
   return w;
 }
 
@@ -192,6 +197,11 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
   a->slots_out = nullptr;
   a->kv_type = quant ? kv_type : dtype;
   a->k_scale = a->k_zero = a->v_scale = a->v_zero = nullptr;
+  // Longest-first dispatch pays when the grid is deeper than what the chip
+  // holds at once; smaller grids keep the plain order and skip the pass.
+  a->order = w.bytes > 0 && nwg > kOrderMinWorkgroups
+                 ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + w.order_offset)
+                 : nullptr;
   *num_workgroups = nwg;
   return 1;  // ready to launch
 }

@@ -167,7 +167,8 @@ __device__ inline WorkItem grid_item(const DecodeKernelArgs& a) {
     }
   }
   const uint32_t ht = bid % a.head_tiles;
-  bid /= a.head_tiles;
+  bid /= a.head_tiles;  // (sequence, partition) pair, partition-major
+  if (a.order != nullptr) bid = a.order[bid];
   WorkItem it;
   it.s = bid % a.num_seqs;
   it.part = bid / a.num_seqs;
@@ -175,6 +176,109 @@ __device__ inline WorkItem grid_item(const DecodeKernelArgs& a) {
   it.g = (ht / tiles_per_group) * a.kv_per_wg;
   it.h0 = it.g * a.group + (ht % tiles_per_group) * GT;
   return it;
+}
+
+// Longest-first dispatch of the split-context work. A launch in which
+// partitions of every length (full ones of long contexts, short tails, short
+// contexts) are dispatched in partition-major order ends with a few long
+// workgroups still running on a mostly idle chip. The ordering pass sorts
+// the (sequence, partition) pairs j = s + num_seqs * part by the length of
+// their partition, longest first (list scheduling with the longest jobs first,
+// which bounds that tail by the shortest jobs): 17 classes, full partitions,
+// then 16 bands of partial ones from long to short, then empty pairs (past the
+// context, or of a malformed length). The sort is stable, so within a class
+// the pairs keep the partition-major order and the XCD placement above. One
+// workgroup: wave w sorts the contiguous slice w of the pairs in a count pass
+// and a scatter pass that ranks each pair among its class with a ballot,
+// between them an exclusive scan over (class, wave) in LDS.
+constexpr int kOrderWaves = 16;
+constexpr uint32_t kOrderClasses = 17;
+constexpr uint32_t kOrderLdsSeqs = 8192;  // batches up to this size read lengths from LDS
+
+__device__ inline uint32_t order_class(const DecodeKernelArgs& a, const int32_t* lens,
+                                       uint32_t j) {
+  const uint32_t s = j % a.num_seqs, part = j / a.num_seqs;
+  const int32_t n = lens[s];
+  const uint32_t p0 = part * a.part_tokens;  // < max_context_len + part_tokens < 2^32
+  if (n <= 0 || uint32_t(n) > a.max_context_len || uint32_t(n) <= p0) return kOrderClasses - 1;
+  const uint32_t len = min(uint32_t(n) - p0, a.part_tokens);
+  return (a.part_tokens - len) * 16u / a.part_tokens;  // 0 (full) .. 15
+}
+
+__global__ __launch_bounds__(kOrderWaves * kWave) void decode_order_kernel(
+    const DecodeKernelArgs a) {
+  __shared__ uint32_t s_cnt[kOrderClasses][kOrderWaves];
+  __shared__ int32_t s_len[kOrderLdsSeqs];
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t n = a.num_seqs * a.max_parts;
+  // the lengths are read once per pair in each pass: stage them in LDS
+  const int32_t* lens = a.context_lens;
+  if (a.num_seqs <= kOrderLdsSeqs) {
+    for (uint32_t i = threadIdx.x; i < a.num_seqs; i += kOrderWaves * kWave)
+      s_len[i] = a.context_lens[i];
+    __syncthreads();
+    lens = s_len;
+  }
+  const uint32_t per = ((n + kOrderWaves - 1) / kOrderWaves + kWave - 1) / kWave * kWave;
+  const uint32_t lo = min(n, wave * per), hi = min(n, lo + per);
+
+  uint32_t cnt[kOrderClasses];
+#pragma unroll
+  for (uint32_t k = 0; k < kOrderClasses; ++k) cnt[k] = 0;
+  for (uint32_t j0 = lo; j0 < hi; j0 += kWave) {
+    const uint32_t j = j0 + lane;
+    const uint32_t c = j < hi ? order_class(a, lens, j) : kOrderClasses;
+#pragma unroll
+    for (uint32_t k = 0; k < kOrderClasses; ++k) cnt[k] += __popcll(__ballot(c == k));
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (uint32_t k = 0; k < kOrderClasses; ++k) s_cnt[k][wave] = cnt[k];
+  }
+  __syncthreads();
+
+  // First position of (class k, this wave): every pair of the classes before
+  // k, then the pairs of class k in the slices before this one. Lane k < 17
+  // sums its class over the waves; an exclusive scan over those lanes adds
+  // the classes before it.
+  uint32_t before = 0, total = 0;
+  if (lane < kOrderClasses) {
+    for (uint32_t v = 0; v < uint32_t(kOrderWaves); ++v) {
+      const uint32_t c = s_cnt[lane][v];
+      total += c;
+      before += v < wave ? c : 0u;
+    }
+  }
+  uint32_t incl = total;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o);
+    if (lane >= uint32_t(o)) incl += t;
+  }
+  const uint32_t start = incl - total + before;
+  uint32_t base[kOrderClasses];
+#pragma unroll
+  for (uint32_t k = 0; k < kOrderClasses; ++k) base[k] = __builtin_amdgcn_readlane(start, k);
+  const uint64_t below = (uint64_t(1) << lane) - 1;  // lanes before this one
+  for (uint32_t j0 = lo; j0 < hi; j0 += kWave) {
+    const uint32_t j = j0 + lane;
+    const uint32_t c = j < hi ? order_class(a, lens, j) : kOrderClasses;
+    uint32_t pos = n;
+#pragma unroll
+    for (uint32_t k = 0; k < kOrderClasses; ++k) {
+      const uint64_t m = __ballot(c == k);
+      if (c == k) pos = base[k] + uint32_t(__popcll(m & below));
+      base[k] += uint32_t(__popcll(m));
+    }
+    if (pos < n) a.order[pos] = j;
+  }
+}
+
+hipError_t launch_order(const DecodeKernelArgs& a, hipStream_t stream) {
+  if (a.order == nullptr) return hipSuccess;
+  hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderWaves * kWave), 0, stream, a);
+  return hipGetLastError();
 }
 
 // Checks the item's sequence length and table slice, and resolves each token
@@ -1468,6 +1572,8 @@ uint32_t heads_per_workgroup_quant(int dtype, uint32_t head_dim, uint32_t group)
 hipError_t launch_decode_partitions_quant(int dtype, int kv_type, uint32_t head_dim,
                                           const DecodeKernelArgs& a, uint64_t num_workgroups,
                                           hipStream_t stream) {
+  const hipError_t e = launch_order(a, stream);
+  if (e != hipSuccess) return e;
   switch (dtype) {
     case kF32: return launch_quant_kv<kF32>(kv_type, head_dim, a, num_workgroups, stream);
     case kF16: return launch_quant_kv<kF16>(kv_type, head_dim, a, num_workgroups, stream);
@@ -1507,6 +1613,8 @@ uint32_t kv_heads_per_workgroup(int dtype, uint32_t head_dim, uint32_t group,
 
 hipError_t launch_decode_partitions(int dtype, uint32_t head_dim, const DecodeKernelArgs& a,
                                     uint64_t num_workgroups, hipStream_t stream) {
+  const hipError_t e = launch_order(a, stream);
+  if (e != hipSuccess) return e;
   switch (dtype) {
     case kF32: return launch_dt<kF32>(head_dim, a, num_workgroups, stream);
     case kF16: return launch_dt<kF16>(head_dim, a, num_workgroups, stream);

@@ -77,6 +77,11 @@ struct DecodeKernelArgs {
   const float* k_zero;
   const float* v_scale;
   const float* v_zero;
+  // Dispatch order of the (sequence, partition) pairs, longest partitions
+  // first: [num_seqs * max_parts] pair indices s + num_seqs * part, written by
+  // the ordering pass ahead of the partition pass. Null: plain partition-major
+  // order.
+  uint32_t* order;
 };
 
 struct ReduceKernelArgs {

@@ -101,3 +101,102 @@ def test_quant_decode_plan_shapes(name, ctx, hq, hkv, kv):
         host_threads())
     max_err, ratio, finite = decode_errors(w.dtype, host_bits(out), ref)
     assert finite and ratio <= 1.0, max_err
+
+
+def _expected_order(ctx, num_seqs, max_parts, part, max_ctx):
+    """The dispatch order the ordering pass must write: pairs j = s + B * p stably
+    sorted by length class (full partitions, 16 bands of partial ones from long to
+    short, then empty or malformed pairs)."""
+    j = np.arange(num_seqs * max_parts, dtype=np.int64)
+    n = np.asarray(ctx, dtype=np.int64)[j % num_seqs]
+    p0 = (j // num_seqs) * part
+    ln = np.clip(n - p0, 0, part)
+    cls = np.where((n <= 0) | (n > max_ctx) | (n <= p0), 16, (part - ln) * 16 // part)
+    return np.argsort(cls, kind="stable").astype(np.uint32)
+
+
+def _pad256(b):
+    return -(-b // 256) * 256
+
+
+@pytest.mark.parametrize("name,ctx,hq,hkv,bad", [
+    ("gqa-mixed", np.random.default_rng(5).integers(1, 5001, 300), 32, 8, True),
+    ("mha-mixed", np.random.default_rng(6).integers(1, 3001, 40), 32, 32, False),
+    ("small-grid", [2000] * 8, 8, 8, False),
+])
+def test_decode_dispatch_order(name, ctx, hq, hkv, bad):
+    """The ordering pass writes, at the end of the workspace, the longest-first
+    permutation of the (sequence, partition) pairs; grids that the chip holds at
+    once (512 workgroups or fewer) skip it. Malformed lengths sort last and still
+    give NaN rows."""
+    w = _shape(name, ctx, hq, hkv, seed=17)
+    t = workloads.make_tensors(w, DEV)
+    bt = torch.from_numpy(w.block_table).to(DEV)
+    sp = torch.from_numpy(w.seq_ptr).to(DEV)
+    lens = w.context_lens.copy()
+    if bad:
+        lens[3], lens[10] = -3, w.max_context_len + 7
+    ctx_t = torch.from_numpy(lens).to(DEV)
+    part = hpkv.hpkv_paged_attention_decode_partition_tokens(
+        w.torch_dtype, w.num_seqs, hq, hkv, w.head_dim, w.page_size, w.max_context_len)
+    mp = -(-int(w.max_context_len) // part)
+    rows = w.num_seqs * hq * mp
+    off = _pad256(rows * 8) + _pad256(rows * w.head_dim * 4)
+    ws = hpkv.alloc_workspace(t.q, t.k_cache, w.max_context_len)
+    assert ws is not None and ws.numel() >= off + 4 * w.num_seqs * mp
+    ws.fill_(0xFF)
+    out = torch.empty_like(t.q)
+    hpkv.hpkv_paged_attention_decode_partitions(t.q, t.k_cache, t.v_cache, bt, sp, ctx_t, w.scale,
+                                                w.max_context_len, ws, out)
+    torch.cuda.synchronize()
+    got = ws[off:off + 4 * w.num_seqs * mp].cpu().numpy().view(np.uint32)
+    print(f"[order] {name} part={part} pairs={w.num_seqs * mp}", flush=True)
+    if name == "small-grid":
+        assert np.all(got == 0xFFFFFFFF)
+        return
+    exp = _expected_order(lens, w.num_seqs, mp, part, w.max_context_len)
+    assert np.array_equal(got, exp)
+    if bad:
+        hpkv.hpkv_paged_attention_decode_reduce(ctx_t, hkv, w.page_size, w.max_context_len, ws,
+                                                out)
+        torch.cuda.synchronize()
+        o = out.float().cpu()
+        assert torch.isnan(o[3]).all() and torch.isnan(o[10]).all()
+        good = torch.ones(w.num_seqs, dtype=torch.bool)
+        good[[3, 10]] = False
+        assert torch.isfinite(o[good]).all()
+
+
+def test_decode_dispatch_order_many_seqs():
+    """Batches above 8192 sequences read the lengths from global memory instead
+    of LDS in the ordering pass; the order must be the same permutation."""
+    rng = np.random.default_rng(21)
+    B, bs, d = 8300, 16, 64
+    ctx = rng.integers(0, 2049, B).astype(np.int32)
+    ctx[::97] = 2048  # the longest context sets max_context_len
+    pages = -(-ctx // bs)
+    seq_ptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.uint32)
+    num_pages = int(seq_ptr[-1])
+    bt = torch.arange(num_pages, dtype=torch.int32, device=DEV)
+    sp = torch.from_numpy(seq_ptr.view(np.int32)).to(DEV)
+    ctx_t = torch.from_numpy(ctx).to(DEV)
+    kc = torch.zeros(num_pages, bs, 1, d, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    q = torch.ones(B, 1, d, dtype=torch.bfloat16, device=DEV)
+    max_ctx = int(ctx.max())
+    part = hpkv.hpkv_paged_attention_decode_partition_tokens(torch.bfloat16, B, 1, 1, d, bs,
+                                                             max_ctx)
+    mp = -(-max_ctx // part)
+    print(f"[order] many-seqs B={B} part={part} pairs={B * mp}", flush=True)
+    rows = B * mp
+    off = _pad256(rows * 8) + _pad256(rows * d * 4)
+    ws = hpkv.alloc_workspace(q, kc, max_ctx)
+    ws.fill_(0xFF)
+    out = torch.empty_like(q)
+    hpkv.hpkv_paged_attention_decode_partitions(q, kc, vc, bt, sp, ctx_t, d ** -0.5, max_ctx, ws,
+                                                out)
+    hpkv.hpkv_paged_attention_decode_reduce(ctx_t, 1, bs, max_ctx, ws, out)
+    torch.cuda.synchronize()
+    got = ws[off:off + 4 * B * mp].cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, _expected_order(ctx, B, mp, part, max_ctx))
+    assert torch.equal(out.float().cpu(), torch.zeros(B, 1, d))  # V rows are zeros
