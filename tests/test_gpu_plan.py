@@ -200,3 +200,37 @@ def test_decode_dispatch_order_many_seqs():
     got = ws[off:off + 4 * B * mp].cpu().numpy().view(np.uint32)
     assert np.array_equal(got, _expected_order(ctx, B, mp, part, max_ctx))
     assert torch.equal(out.float().cpu(), torch.zeros(B, 1, d))  # V rows are zeros
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (32, 32)])
+def test_merge_with_malformed_page_in_a_middle_partition(hq, hkv):
+    """The partition pass merges each sequence's partitions in whichever workgroup
+    finishes last; a partition that finds a page id past the pool still counts
+    itself, so its sequence gets NaN rows and every other sequence the bits of a
+    clean run."""
+    ctx = [5000, 3000, 4096, 700, 2049, 5000, 1]
+    w = _shape("merge-bad", ctx, hq, hkv, seed=23)
+    t = workloads.make_tensors(w, DEV)
+    sp = torch.from_numpy(w.seq_ptr).to(DEV)
+    ctx_t = torch.from_numpy(w.context_lens).to(DEV)
+    ws = hpkv.alloc_workspace(t.q, t.k_cache, w.max_context_len)
+
+    def run(bt_host):
+        out = torch.full_like(t.q, float("nan"))
+        hpkv.hpkv_paged_attention_decode(t.q, t.k_cache, t.v_cache,
+                                         torch.from_numpy(bt_host).to(DEV), sp, ctx_t, w.scale,
+                                         w.max_context_len, ws, out)
+        torch.cuda.synchronize()
+        return host_bits(out)
+
+    good = run(w.block_table).copy()
+    bt = w.block_table.copy()
+    bt[int(w.seq_ptr[0]) + 1500 // w.page_size] = w.num_pages + 3  # token 1500 of sequence 0
+    out = run(bt)
+    outf = oracle.widen_dtype(w.dtype, out)
+    print(f"[merge-bad] {hq}/{hkv}", flush=True)
+    assert np.isnan(outf[0]).all()
+    for s in range(1, len(ctx)):
+        assert out[s].tobytes() == good[s].tobytes(), s
+    r = check_step(w)  # and the clean run matches the oracle
+    assert r["max_err"] < 2e-2
