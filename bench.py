@@ -2,8 +2,7 @@
 
 A step is one pass of the whole path over one synthetic batch (one layer):
 slot mapping of the new tokens, store of their K/V rows into the page pools,
-then paged decode attention of every sequence (ordering pass, then the partition
-kernels, whose last workgroup per sequence merges the split context).
+then paged decode attention of every sequence (partition + reduce kernels).
 A plain decode step (one new token per sequence, stored at ctx-1) runs as the
 fused hpkv_paged_attention_decode_step, which stores the row inside the decode
 launch; --unfused times the three separate calls instead.
@@ -205,7 +204,7 @@ def cpu_baseline(w, t, out_gpu):
 
 class QuantStep:
     """A decode step over quantized pools: slot mapping, the quantizing store of the new
-    rows, then decode (ordering pass + partition pass with the merge)."""
+    rows, then decode (partition + reduce)."""
 
     def __init__(self, w, t, qt, kv):
         import paged_kv_cache_hpkv_amd as hpkv
@@ -312,7 +311,7 @@ def main_quant(args, dev):
             "step": "slot mapping + quantizing store + quantized decode (separate launches)",
         },
         "roofline": {
-            "kernel": "decode_order_kernel + decode_partition[_mfma]_quant_kernel (merge included)",
+            "kernel": "decode_order_kernel + decode_partition_quant_kernel + decode_reduce_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

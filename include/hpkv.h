@@ -167,11 +167,10 @@ int hpkv_store_kvcache(int dtype, const void* key, const void* value, void* k_ca
  * Bytes of device workspace hpkv_paged_attention_decode needs for a batch of
  * num_seqs sequences no longer than max_context_len tokens: the split-context
  * partials (one fp32 (max, sum) pair and one fp32 head_dim vector per
- * sequence, query head and context partition), the dispatch order of the
- * (sequence, partition) pairs (one uint32 each) and the merge's arrival
- * counters (at most one uint32 per sequence and query head), counted with the
- * smallest partition the library uses, so it is enough for every num_kv_heads
- * and for the quantized decode. 0 when every sequence fits one partition (no
+ * sequence, query head and context partition), then the dispatch order of the
+ * (sequence, partition) pairs (one uint32 each), counted with the smallest
+ * partition the library uses, so it is enough for every num_kv_heads and for
+ * the quantized decode. 0 when every sequence fits one partition (no
  * workspace is then read or written) and on invalid arguments.
  * ------------------------------------------------------------------------- */
 size_t hpkv_paged_attention_decode_workspace_size(int dtype, uint32_t num_seqs,
@@ -223,15 +222,13 @@ uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_se
  * Malformed contents (caller error): a sequence with n < 0,
  * n > max_context_len, n beyond its slice, or a page id >= num_pages in the
  * pages it reads, gets NaN in all its outputs.
- * Enqueued when a sequence may need more than one partition (a workspace is
- * needed): a one-workgroup ordering pass that zeroes the merge counters and
- * lists the (sequence, partition) pairs longest partition first in the
- * workspace (the list is skipped for grids of at most 512 workgroups); then
- * the split-context partition pass, which takes its work in that order so the
- * launch does not end on a few long partitions. The last workgroup to finish
- * a sequence's partitions for its query heads merges them (log-sum-exp rule)
- * into `out`; a sequence covered by one partition is written directly.
- * Results do not depend on the order in which partitions finish.
+ * Enqueued: a one-workgroup ordering pass that lists the (sequence,
+ * partition) pairs longest partition first in the workspace (skipped when the
+ * grid has at most 512 workgroups, or no workspace is needed), the
+ * split-context partition pass, which takes its work in that order so the
+ * launch does not end on a few long partitions, then the log-sum-exp reduce
+ * (skipped per sequence when one partition covers it). Results do not depend
+ * on the order.
  * ------------------------------------------------------------------------- */
 int hpkv_paged_attention_decode(int dtype, int index_type, const void* q, const void* k_cache,
                                 const void* v_cache, const void* block_table,
@@ -242,13 +239,12 @@ int hpkv_paged_attention_decode(int dtype, int index_type, const void* q, const 
                                 uint32_t max_context_len, void* workspace, size_t workspace_bytes,
                                 void* out, void* stream);
 
-/* The partition pass alone, and a separate reduce. The partition pass is all
- * of hpkv_paged_attention_decode's work (ordering kernel, then partition
- * kernel with the merge); it also leaves every multi-partition sequence's
- * partials in the workspace. The reduce merges those partials into `out` again
- * with the same arithmetic, so it reproduces the same bits; it exists to time
- * and test the merge on its own. Both take the arguments of
- * hpkv_paged_attention_decode (the reduce only those it declares). */
+/* The two passes of hpkv_paged_attention_decode, separately: the partition
+ * pass (the ordering kernel, then the partition kernel, which writes `out` for
+ * sequences covered by one partition and partials for the rest) and the
+ * reduce (merges the partials into `out`). Calling them in this
+ * order on one stream with the same arguments is equivalent to
+ * hpkv_paged_attention_decode. Used to time the kernels one by one. */
 int hpkv_paged_attention_decode_partitions(int dtype, int index_type, const void* q,
                                            const void* k_cache, const void* v_cache,
                                            const void* block_table, uint64_t block_table_len,

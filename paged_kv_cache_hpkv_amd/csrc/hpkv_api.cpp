@@ -106,23 +106,21 @@ DecodePlan plan_decode(int dtype, bool quant, uint32_t num_seqs, uint32_t num_q_
 }
 
 struct WorkspaceLayout {
-  size_t ml_offset, o_offset, order_offset, counters_offset, bytes;
+  size_t ml_offset, o_offset, order_offset, bytes;
 };
 
 WorkspaceLayout workspace_layout(uint32_t num_seqs, uint32_t num_q_heads, uint32_t head_dim,
                                  uint32_t max_context_len, uint32_t part_tokens) {
   const uint64_t mp = max_parts_for(max_context_len, part_tokens);
-  WorkspaceLayout w{0, 0, 0, 0, 0};
+  WorkspaceLayout w{0, 0, 0, 0};
   if (mp <= 1) return w;  // every sequence fits one partition: no partials
-  const auto pad = [](uint64_t b) { return (b + 255) & ~uint64_t(255); };
   const uint64_t rows = uint64_t(num_seqs) * num_q_heads * mp;
+  const uint64_t ml_bytes = (rows * sizeof(float2) + 255) & ~uint64_t(255);
+  const uint64_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~uint64_t(255);
   w.ml_offset = 0;
-  w.o_offset = pad(rows * sizeof(float2));
-  w.order_offset = w.o_offset + pad(rows * head_dim * sizeof(float));
-  // one u32 per (sequence, partition), then one arrival counter per (sequence,
-  // head tile): at most one per (sequence, query head)
-  w.counters_offset = w.order_offset + pad(uint64_t(num_seqs) * mp * sizeof(uint32_t));
-  w.bytes = w.counters_offset + uint64_t(num_seqs) * num_q_heads * sizeof(uint32_t);
+  w.o_offset = ml_bytes;
+  w.order_offset = ml_bytes + o_bytes;  // then one u32 per (sequence, partition)
+  w.bytes = w.order_offset + uint64_t(num_seqs) * mp * sizeof(uint32_t);
   return w;
 }
 
@@ -204,13 +202,23 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
   a->order = w.bytes > 0 && nwg > kOrderMinWorkgroups
                  ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + w.order_offset)
                  : nullptr;
-  // sequences longer than one partition are merged by the partition pass itself
-  a->counters = w.bytes > 0
-                    ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + w.counters_offset)
-                    : nullptr;
-  a->num_counters = w.bytes > 0 ? uint32_t(uint64_t(num_seqs) * head_tiles) : 0u;
   *num_workgroups = nwg;
   return 1;  // ready to launch
+}
+
+ReduceKernelArgs reduce_args(const DecodeKernelArgs& a, uint32_t head_dim) {
+  ReduceKernelArgs r;
+  r.context_lens = a.context_lens;
+  r.ws_o = a.ws_o;
+  r.ws_ml = a.ws_ml;
+  r.out = a.out;
+  r.num_seqs = a.num_seqs;
+  r.num_q_heads = a.num_q_heads;
+  r.head_dim = head_dim;
+  r.max_parts = a.max_parts;
+  r.part_tokens = a.part_tokens;
+  r.max_context_len = a.max_context_len;
+  return r;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? HPKV_OK : HPKV_ERR_HIP; }
@@ -412,7 +420,10 @@ int hpkv_paged_attention_decode(int dtype, int index_type, const void* q, const 
                                 max_context_len, workspace, workspace_bytes, out, &a, &nwg);
   if (st <= 0) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(hpkv::launch_decode_partitions(dtype, head_dim, a, nwg, s));
+  hipError_t e = hpkv::launch_decode_partitions(dtype, head_dim, a, nwg, s);
+  if (e != hipSuccess) return HPKV_ERR_HIP;
+  if (a.max_parts > 1) e = hpkv::launch_decode_reduce(dtype, reduce_args(a, head_dim), s);
+  return hip_status(e);
 }
 
 int hpkv_paged_attention_decode_step(int dtype, int index_type, const void* q,
@@ -439,7 +450,10 @@ int hpkv_paged_attention_decode_step(int dtype, int index_type, const void* q,
   a.new_v = new_value;
   a.slots_out = slots_out;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(hpkv::launch_decode_partitions(dtype, head_dim, a, nwg, s));
+  hipError_t e = hpkv::launch_decode_partitions(dtype, head_dim, a, nwg, s);
+  if (e != hipSuccess) return HPKV_ERR_HIP;
+  if (a.max_parts > 1) e = hpkv::launch_decode_reduce(dtype, reduce_args(a, head_dim), s);
+  return hip_status(e);
 }
 
 int hpkv_paged_attention_prefill(int dtype, int index_type, const void* q, const void* k_cache,
@@ -557,7 +571,10 @@ int hpkv_paged_attention_decode_quant(int dtype, int kv_type, int index_type, co
   a.v_scale = v_scale;
   a.v_zero = v_zero;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(hpkv::launch_decode_partitions_quant(dtype, kv_type, head_dim, a, nwg, s));
+  hipError_t e = hpkv::launch_decode_partitions_quant(dtype, kv_type, head_dim, a, nwg, s);
+  if (e != hipSuccess) return HPKV_ERR_HIP;
+  if (a.max_parts > 1) e = hpkv::launch_decode_reduce(dtype, reduce_args(a, head_dim), s);
+  return hip_status(e);
 }
 
 }  // extern "C"

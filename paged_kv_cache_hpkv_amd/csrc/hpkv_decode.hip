@@ -207,8 +207,6 @@ __device__ inline uint32_t order_class(const DecodeKernelArgs& a, const int32_t*
 
 __global__ __launch_bounds__(kOrderWaves * kWave) void decode_order_kernel(
     const DecodeKernelArgs a) {
-  for (uint32_t i = threadIdx.x; i < a.num_counters; i += kOrderWaves * kWave) a.counters[i] = 0;
-  if (a.order == nullptr) return;
   __shared__ uint32_t s_cnt[kOrderClasses][kOrderWaves];
   __shared__ int32_t s_len[kOrderLdsSeqs];
   const uint32_t lane = threadIdx.x % kWave;
@@ -278,112 +276,9 @@ __global__ __launch_bounds__(kOrderWaves * kWave) void decode_order_kernel(
 }
 
 hipError_t launch_order(const DecodeKernelArgs& a, hipStream_t stream) {
-  if (a.order == nullptr && a.counters == nullptr) return hipSuccess;
+  if (a.order == nullptr) return hipSuccess;
   hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderWaves * kWave), 0, stream, a);
   return hipGetLastError();
-}
-
-// Merges the partitions of one (sequence, query head) row `sh` with the
-// log-sum-exp rule, normalises and rounds to dtype; run by every lane of one
-// wave. Lane j reads partition j's (max, sum) so the partials are fetched in
-// parallel; the weights are then shared through the wave's lanes. The
-// reduce kernel and the in-kernel merge below share this code, so both give
-// the same bits.
-// Partials written in one launch and read by another workgroup of the same
-// launch go through agent-scope atomic accesses: stores that write through this
-// XCD's L2 and loads that do not trust it, so no cache-wide write-back or
-// invalidation is needed. Across launches plain accesses suffice.
-__device__ inline void store_partial(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void store_partial(float2* p, float2 v) {
-  uint64_t b;
-  __builtin_memcpy(&b, &v, 8);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), b, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-template <bool COH>
-__device__ inline float load_partial(const float* p) {
-  if constexpr (COH)
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    return *p;
-}
-template <bool COH>
-__device__ inline float2 load_partial(const float2* p) {
-  if constexpr (COH) {
-    const uint64_t b = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float2*>(p)),
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    float2 v;
-    __builtin_memcpy(&v, &b, 8);
-    return v;
-  } else {
-    return *p;
-  }
-}
-
-template <int DT, bool COH = false>
-__device__ inline void merge_row(const float2* ws_ml, const float* ws_o, void* out, uint64_t sh,
-                                 uint32_t nparts, uint32_t max_parts, uint32_t head_dim) {
-  const uint32_t lane = threadIdx.x % kWave;
-  const float2* ml = ws_ml + sh * max_parts;
-  const float* o = ws_o + sh * max_parts * head_dim;
-  // global max over partitions: lane j holds partition j, j + 64, ...
-  float mx = -INFINITY;
-  for (uint32_t j = lane; j < nparts; j += kWave) mx = fmaxf(mx, load_partial<COH>(ml + j).x);
-#pragma unroll
-  for (int sft = 32; sft >= 1; sft >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sft));
-  // weight of partition `lane` (the first 64 partitions), and the total weight
-  float wl = 0.0f, L = 0.0f;
-  for (uint32_t j = lane; j < nparts; j += kWave) {
-    const float2 v = load_partial<COH>(ml + j);
-    const float f = __builtin_amdgcn_exp2f(v.x - mx);
-    if (j == lane) wl = f;
-    L = fmaf(v.y, f, L);
-  }
-#pragma unroll
-  for (int sft = 32; sft >= 1; sft >>= 1) L += __shfl_xor(L, sft);
-  // weighted sum of the partial vectors, partitions in order; every lane runs
-  // every iteration (the weights are read from lane j with v_readlane)
-  for (uint32_t e0 = 0; e0 < head_dim; e0 += kWave) {
-    const uint32_t e = e0 + lane;
-    const bool active = e < head_dim;
-    float O = 0.0f;
-#pragma unroll 8
-    for (uint32_t j = 0; j < nparts; ++j) {
-      const float f = j < uint32_t(kWave)
-                          ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), int(j)))
-                          : __builtin_amdgcn_exp2f(load_partial<COH>(ml + j).x - mx);
-      const float v = active ? load_partial<COH>(o + uint64_t(j) * head_dim + e) : 0.0f;
-      O = fmaf(v, f, O);
-    }
-    if (active) store_out<DT>(out, sh * head_dim + e, O / L);
-  }
-}
-
-// Split-context merge inside the partition pass. A workgroup that has written
-// the partials of rows row0 .. row0+NR-1 for one of the sequence's nparts
-// partitions (store_partial) waits until those stores have completed, then
-// counts itself in counters[row0 / NR] (zeroed by the ordering pass); the last
-// of the nparts merges the rows into `out`, one wave per row, reading the
-// partials with agent-coherent loads. Completed write-through stores before
-// the count and coherent loads after it are what a release/acquire pair at
-// agent scope would provide for these locations; the writers may sit on other
-// XCDs.
-template <int DT, int D, int NR, int NW>
-__device__ inline void arrive_and_merge(const DecodeKernelArgs& a, uint64_t row0,
-                                        uint32_t nparts) {
-  __shared__ uint32_t s_last;
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
-  __syncthreads();                // ... and every other thread's
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(a.counters + row0 / NR, 1u, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) + 1u == nparts ? 1u : 0u;
-  __syncthreads();
-  if (s_last == 0) return;
-  const uint32_t wave = threadIdx.x / kWave;
-  for (uint32_t r = wave; r < uint32_t(NR); r += NW)
-    merge_row<DT, true>(a.ws_ml, a.ws_o, a.out, row0 + r, nparts, a.max_parts, D);
 }
 
 // Checks the item's sequence length and table slice, and resolves each token
@@ -469,11 +364,9 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
     } else {
       for (uint32_t i = tid; i < NH * D; i += NTH) {
         const uint64_t r = (w.out_row0 + i / D) * a.max_parts + w.part;
-        store_partial(a.ws_o + r * D + i % D, NAN);
-        if (i % D == 0) store_partial(a.ws_ml + r, make_float2(NAN, NAN));
+        a.ws_o[r * D + i % D] = NAN;
+        if (i % D == 0) a.ws_ml[r] = make_float2(NAN, NAN);
       }
-      if (a.counters != nullptr)
-        arrive_and_merge<DT, D, NH, (NTH + kWave - 1) / kWave>(a, w.out_row0, w.nparts);
     }
     if (slot_writer && last_part) a.slots_out[w.s] = -1;
     return false;
@@ -537,12 +430,10 @@ __device__ inline void finish_partition(const DecodeKernelArgs& a, const Partiti
       store_out<DT>(a.out, row * D + e, L > 0.0f ? O / L : 0.0f);
     } else {
       const uint64_t r = row * a.max_parts + w.part;
-      store_partial(a.ws_o + r * D + e, O);
-      if (e == 0) store_partial(a.ws_ml + r, make_float2(mx, L));
+      a.ws_o[r * D + e] = O;
+      if (e == 0) a.ws_ml[r] = make_float2(mx, L);
     }
   }
-  if (w.nparts > 1 && a.counters != nullptr)
-    arrive_and_merge<DT, D, HPW * GT, NW>(a, w.out_row0, w.nparts);
 }
 
 // HPW adjacent KV heads per workgroup (whole GQA groups, GT == group): a token's
@@ -1449,11 +1340,12 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
 }
 
 // One wave per (sequence, query head) with more than one partition: merges the
-// partitions (merge_row) into `out`. The partition pass does the same merge in
-// the last workgroup of each head tile, so this kernel only serves the
-// separate reduce entry point.
+// partitions with the log-sum-exp rule, normalises and rounds to dtype. Lane j
+// reads partition j's (max, sum) so the partials are fetched in parallel; the
+// weights are then shared through the wave's lanes.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const ReduceKernelArgs a) {
+  const uint32_t lane = threadIdx.x % kWave;
   const uint64_t sh = uint64_t(blockIdx.x) * kWaves + threadIdx.x / kWave;
   if (sh >= uint64_t(a.num_seqs) * a.num_q_heads) return;
   const uint32_t s = uint32_t(sh / a.num_q_heads);
@@ -1461,7 +1353,39 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const ReduceKer
   if (length_is_bad(n, a.max_context_len)) return;
   const uint32_t nparts = num_parts(n, a.part_tokens);
   if (nparts <= 1) return;
-  merge_row<DT>(a.ws_ml, a.ws_o, a.out, sh, nparts, a.max_parts, a.head_dim);
+  const float2* ml = a.ws_ml + sh * a.max_parts;
+  const float* o = a.ws_o + sh * a.max_parts * a.head_dim;
+  // global max over partitions: lane j holds partition j, j + 64, ...
+  float mx = -INFINITY;
+  for (uint32_t j = lane; j < nparts; j += kWave) mx = fmaxf(mx, ml[j].x);
+#pragma unroll
+  for (int sft = 32; sft >= 1; sft >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sft));
+  // weight of partition `lane` (the first 64 partitions), and the total weight
+  float wl = 0.0f, L = 0.0f;
+  for (uint32_t j = lane; j < nparts; j += kWave) {
+    const float2 v = ml[j];
+    const float f = __builtin_amdgcn_exp2f(v.x - mx);
+    if (j == lane) wl = f;
+    L = fmaf(v.y, f, L);
+  }
+#pragma unroll
+  for (int sft = 32; sft >= 1; sft >>= 1) L += __shfl_xor(L, sft);
+  // weighted sum of the partial vectors, partitions in order; every lane runs
+  // every iteration (the weights are read from lane j with v_readlane)
+  for (uint32_t e0 = 0; e0 < a.head_dim; e0 += kWave) {
+    const uint32_t e = e0 + lane;
+    const bool active = e < a.head_dim;
+    float O = 0.0f;
+#pragma unroll 8
+    for (uint32_t j = 0; j < nparts; ++j) {
+      const float f = j < uint32_t(kWave)
+                          ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), int(j)))
+                          : __builtin_amdgcn_exp2f(ml[j].x - mx);
+      const float v = active ? o[uint64_t(j) * a.head_dim + e] : 0.0f;
+      O = fmaf(v, f, O);
+    }
+    if (active) store_out<DT>(a.out, sh * a.head_dim + e, O / L);
+  }
 }
 
 // Launch shapes measured on MI355X (bf16, d=128): for one query head per KV

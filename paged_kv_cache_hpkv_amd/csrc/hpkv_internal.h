@@ -82,11 +82,6 @@ struct DecodeKernelArgs {
   // the ordering pass ahead of the partition pass. Null: plain partition-major
   // order.
   uint32_t* order;
-  // Split-context merge in the partition pass: one arrival counter per
-  // (sequence, head tile), zeroed by the ordering pass; null when no sequence
-  // can have more than one partition.
-  uint32_t* counters;
-  uint32_t num_counters;
 };
 
 struct ReduceKernelArgs {

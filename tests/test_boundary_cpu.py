@@ -236,9 +236,8 @@ def test_reduce_argument_errors():
 
 def test_workspace_size_accounting():
     """The workspace is counted with the smaller, 512-token partition, so it covers
-    every shape's plan: the (max, sum) pairs, the partial vectors and one u32 per
-    (sequence, partition) for the dispatch order, each padded to 256 bytes, then
-    one u32 arrival counter per (sequence, query head)."""
+    every shape's plan: the (max, sum) pairs and the partial vectors, each padded
+    to 256 bytes, then one u32 per (sequence, partition) for the dispatch order."""
     P = hpkv.lib.hpkv_paged_attention_decode_partition_tokens(hpkv.BF16, 1, 32, 32, 128, 16,
                                                               4096)
     assert P == 512
@@ -247,10 +246,9 @@ def test_workspace_size_accounting():
     parts = -(-4096 // P)
     rows = 64 * 32 * parts
     pad = lambda b: -(-b // 256) * 256
-    assert ws(hpkv.BF16, 64, 32, 128, 16, 4096) == \
-        pad(rows * 8) + pad(rows * 128 * 4) + pad(64 * parts * 4) + 64 * 32 * 4
+    assert ws(hpkv.BF16, 64, 32, 128, 16, 4096) == pad(rows * 8) + pad(rows * 128 * 4) + 64 * parts * 4
     rows = 3 * 5 * 2  # ragged: 3 sequences, 5 query heads, d = 8, two partitions
-    assert ws(hpkv.F32, 3, 5, 8, 4, 513) == pad(rows * 8) + pad(rows * 8 * 4) + pad(3 * 2 * 4) + 3 * 5 * 4
+    assert ws(hpkv.F32, 3, 5, 8, 4, 513) == pad(rows * 8) + pad(rows * 8 * 4) + 3 * 2 * 4
     assert ws(9, 64, 32, 128, 16, 4096) == 0
 
 

@@ -203,11 +203,10 @@ def test_decode_dispatch_order_many_seqs():
 
 
 @pytest.mark.parametrize("hq,hkv", [(32, 8), (32, 32)])
-def test_merge_with_malformed_page_in_a_middle_partition(hq, hkv):
-    """The partition pass merges each sequence's partitions in whichever workgroup
-    finishes last; a partition that finds a page id past the pool still counts
-    itself, so its sequence gets NaN rows and every other sequence the bits of a
-    clean run."""
+def test_malformed_page_in_a_middle_partition(hq, hkv):
+    """A partition that finds a page id past the pool writes NaN partials; the
+    reduce turns them into NaN rows for that sequence alone, and every other
+    sequence gets the bits of a clean run."""
     ctx = [5000, 3000, 4096, 700, 2049, 5000, 1]
     w = _shape("merge-bad", ctx, hq, hkv, seed=23)
     t = workloads.make_tensors(w, DEV)
