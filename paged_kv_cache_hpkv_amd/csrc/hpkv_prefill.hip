@@ -76,15 +76,21 @@ __device__ inline uint2 lds_read_tr16(const char* p) {
   return r;
 }
 
+// Maximum of two scores as IEEE maximum (a NaN operand gives NaN): gfx950's
+// v_maximum3_f32, which needs none of the quieting instructions an fmaxf of
+// matrix-core results costs. The row max only shifts the exponent; a NaN score
+// makes its row NaN under either maximum.
+__device__ inline float smax(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+
 // Max over the four lanes l, l^16, l^32, l^48 that hold one row of a score tile
 // (v_permlane32_swap / v_permlane16_swap exchange whole 32- and 16-lane halves).
 __device__ inline float row_max4(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = smax(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return smax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Two fp32 weights rounded to nearest even in the 16-bit input type, packed low-first.
@@ -281,8 +287,8 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
           if (int32_t(tb + 16 * (e / 4) + 4 * q4 + (e % 4)) > pos[jt]) sv[e] = -INFINITY;
         }
       }
-      float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      float mt = smax(smax(smax(sv[0], sv[1]), smax(sv[2], sv[3])),
+                      smax(smax(sv[4], sv[5]), smax(sv[6], sv[7])));
       mt = row_max4(mt);
       const bool need = mt > mthr[jt];
       if (__any(need)) {
