@@ -850,6 +850,20 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
 // The next tile's loads are issued before the current tile is computed.
 // ---------------------------------------------------------------------------
 
+// Max over the four lanes l, l^16, l^32, l^48 that hold one column of a
+// 16x16 MFMA result (v_permlane32_swap / v_permlane16_swap exchange whole 32-
+// and 16-lane halves, without the LDS round trip of a shuffle), as IEEE
+// maximum: gfx950's v_maximum, which needs no quieting instructions. A NaN
+// score makes its head's result NaN under either maximum.
+__device__ inline float col_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // ds_read_b64_tr_b16 (gfx950 transposing LDS read): within each group of 16
 // lanes, lanes 4r..4r+3 fetch the 16 elements of row r of a 4x16 block (8 bytes
 // each) and lane i receives column i of the four rows. Returns this lane's four
@@ -974,8 +988,7 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
       float mt = z[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) mt = fmaxf(mt, z[j]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = col_max4(mt);
       const float mn = fmaxf(m, mt);
       const float mu = mn == -INFINITY ? 0.0f : mn;
       const float corr = __builtin_amdgcn_exp2f(m - mu);
@@ -1255,8 +1268,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
       }
       float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                        fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = col_max4(mt);
       const bool need = mt > mthr;
       if (__any(need)) {
         const float mcn = need ? mt * c : mc;
