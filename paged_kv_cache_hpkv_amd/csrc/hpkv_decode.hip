@@ -640,6 +640,80 @@ __device__ inline void codes16(const u32x4 v, float* f) {
   }
 }
 
+// Two exact code values (fp32) as a packed 16-bit pair of the q type.
+template <int DT>
+__device__ inline uint32_t pack_exact16(float x, float y) {
+  if constexpr (DT == kBF16) {  // at most 8 significant bits: the upper halves are exact
+    return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
+  } else {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(x, y);  // exact: no rounding happens
+    uint32_t r;
+    __builtin_memcpy(&r, &h, 4);
+    return r;
+  }
+}
+
+// 16 codes (one 16-byte chunk) as 16 exact 16-bit values: `lo` holds elements
+// 0..7, `hi` elements 8..15.
+template <int DT, int QT>
+__device__ inline void codes16_to_bits16(const u32x4 c, u32x4& lo, u32x4& hi) {
+  if constexpr (QT == kFP8) {  // packed scaled conversion with scale 1: exact
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    uint32_t r[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == kBF16) {
+        const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+        const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+        __builtin_memcpy(&r[2 * i], &a, 4);
+        __builtin_memcpy(&r[2 * i + 1], &b, 4);
+      } else {
+        const auto a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
+        const auto b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
+        __builtin_memcpy(&r[2 * i], &a, 4);
+        __builtin_memcpy(&r[2 * i + 1], &b, 4);
+      }
+    }
+    lo = u32x4{r[0], r[1], r[2], r[3]};
+    hi = u32x4{r[4], r[5], r[6], r[7]};
+    return;
+  }
+  float f[16];
+  codes16<QT>(c, f);
+  lo = u32x4{pack_exact16<DT>(f[0], f[1]), pack_exact16<DT>(f[2], f[3]),
+             pack_exact16<DT>(f[4], f[5]), pack_exact16<DT>(f[6], f[7])};
+  hi = u32x4{pack_exact16<DT>(f[8], f[9]), pack_exact16<DT>(f[10], f[11]),
+             pack_exact16<DT>(f[12], f[13]), pack_exact16<DT>(f[14], f[15])};
+}
+
+// Eight codes (two words) as exact 16-bit values of the q type: one operand.
+template <int DT, int QT>
+__device__ inline u32x4 codes8_to_bits16(const uint2 c) {
+  const uint32_t w[2] = {c.x, c.y};
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if constexpr (QT == kFP8) {  // packed scaled conversion with scale 1: exact
+      if constexpr (DT == kBF16) {
+        const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+        const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+        __builtin_memcpy(&r[2 * i], &a, 4);
+        __builtin_memcpy(&r[2 * i + 1], &b, 4);
+      } else {
+        const auto a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
+        const auto b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
+        __builtin_memcpy(&r[2 * i], &a, 4);
+        __builtin_memcpy(&r[2 * i + 1], &b, 4);
+      }
+    } else {  // int8 as code + 128 (sign bit flipped): 0..255, exact in fp32 and 16 bits
+      const uint32_t u = w[i] ^ 0x80808080u;
+      r[2 * i] = pack_exact16<DT>(float(u & 0xffu), float((u >> 8) & 0xffu));
+      r[2 * i + 1] = pack_exact16<DT>(float((u >> 16) & 0xffu), float(u >> 24));
+    }
+  }
+  return u32x4{r[0], r[1], r[2], r[3]};
+}
+
 // HPW adjacent KV heads per workgroup (whole GQA groups, GT == group): a token's
 // codes of those heads are HPW*D contiguous bytes, read as one row by HPW*D/16
 // lanes; each aligned group of D/16 lanes holds one head (lane head hw) and keeps
@@ -690,22 +764,41 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
   const uint32_t hw = (lane % LPR) / LPH;  // the lane's KV head within the workgroup's
   const uint32_t c = lane % LPH;           // the lane's chunk of that head's row
 
-  // q of the lane's 16 elements of each head, and sum(q) over the head
-  float qf[GT][EPL], qsum[GT];
+  // q of the lane's 16 elements of each head, and sum(q) over the head. With a
+  // 16-bit q and fp8 codes the K products run as v_dot2 on the codes' exact
+  // 16-bit values (one packed conversion per two codes, two products per
+  // instruction, fp32 accumulation), so q stays packed (qw); otherwise one FMA
+  // per element on fp32 values (qf): int8 codes take three instructions per
+  // pair to reach 16 bits, more than the products they would save.
+  constexpr bool DOT2 = DT != kF32 && QT == kFP8;
+  float qf[DOT2 ? 1 : GT][EPL], qsum[GT];
+  uint32_t qw[DOT2 ? GT : 1][EPL / 2];
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
     const char* qp =
         static_cast<const char*>(a.q) + ((out_row0 + hw * GT + hh) * D + c * EPL) * EQ;
-#pragma unroll
-    for (int h2 = 0; h2 < EPL * EQ / 16; ++h2) {
-      float t[16 / EQ];
-      widen16<DT>(*reinterpret_cast<const u32x4*>(qp + 16 * h2), t);
-#pragma unroll
-      for (int e = 0; e < 16 / EQ; ++e) qf[hh][h2 * (16 / EQ) + e] = t[e];
-    }
     float sq = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) sq += qf[hh][e];
+    for (int h2 = 0; h2 < EPL * EQ / 16; ++h2) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 16 * h2);
+      float t[16 / EQ];
+      widen16<DT>(raw, t);
+#pragma unroll
+      for (int e = 0; e < 16 / EQ; ++e) {
+        if constexpr (DOT2) {
+          sq += t[e];
+        } else {
+          qf[hh][h2 * (16 / EQ) + e] = t[e];
+          sq += t[e];
+        }
+      }
+      if constexpr (DOT2) {
+        qw[hh][4 * h2] = raw.x;
+        qw[hh][4 * h2 + 1] = raw.y;
+        qw[hh][4 * h2 + 2] = raw.z;
+        qw[hh][4 * h2 + 3] = raw.w;
+      }
+    }
     qsum[hh] = row_sum<LPH>(sq);
   }
 
@@ -739,13 +832,33 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
 #pragma unroll
     for (int k = 0; k < NLOAD; ++k) {
       const bool valid = tb + k * RPL + row < cnt;
-      float kf[EPL];
-      codes16<QT>(kr[k], kf);
+      float kf[DOT2 ? 1 : EPL];
+      uint32_t kw[DOT2 ? EPL / 2 : 1];
+      if constexpr (DOT2) {
+        const u32x4 lo = codes8_to_bits16<DT, QT>(uint2{kr[k].x, kr[k].y});
+        const u32x4 hi = codes8_to_bits16<DT, QT>(uint2{kr[k].z, kr[k].w});
+        kw[0] = lo.x; kw[1] = lo.y; kw[2] = lo.z; kw[3] = lo.w;
+        kw[4] = hi.x; kw[5] = hi.y; kw[6] = hi.z; kw[7] = hi.w;
+      } else {
+        codes16<QT>(kr[k], kf);
+      }
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) {
         float d0 = 0.0f;
+        if constexpr (DOT2) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) d0 = fmaf(qf[hh][e], kf[e], d0);
+          for (int i = 0; i < EPL / 2; ++i) {
+            if constexpr (DT == kBF16)
+              d0 = __builtin_amdgcn_fdot2_f32_bf16(as_pair<bf16x2>(kw[i]),
+                                                   as_pair<bf16x2>(qw[hh][i]), d0, false);
+            else
+              d0 = __builtin_amdgcn_fdot2(as_pair<f16x2>(kw[i]), as_pair<f16x2>(qw[hh][i]), d0,
+                                          false);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) d0 = fmaf(qf[hh][e], kf[e], d0);
+        }
         const float dot = row_sum<LPH>(d0);
         const float z = fac[k].x * fmaf(-fac[k].y, qsum[hh], dot) * a.scale_log2;
         sc[hh][k] = valid ? z : -INFINITY;
@@ -1064,80 +1177,6 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
 // fetch row r of a 4x16 block; lane i receives column i), from rows padded by
 // 32 bytes so those 8-byte reads fall on distinct banks.
 // ---------------------------------------------------------------------------
-
-// Two exact code values (fp32) as a packed 16-bit pair of the q type.
-template <int DT>
-__device__ inline uint32_t pack_exact16(float x, float y) {
-  if constexpr (DT == kBF16) {  // at most 8 significant bits: the upper halves are exact
-    return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
-  } else {
-    const auto h = __builtin_amdgcn_cvt_pkrtz(x, y);  // exact: no rounding happens
-    uint32_t r;
-    __builtin_memcpy(&r, &h, 4);
-    return r;
-  }
-}
-
-// 16 codes (one 16-byte chunk) as 16 exact 16-bit values: `lo` holds elements
-// 0..7, `hi` elements 8..15.
-template <int DT, int QT>
-__device__ inline void codes16_to_bits16(const u32x4 c, u32x4& lo, u32x4& hi) {
-  if constexpr (QT == kFP8) {  // packed scaled conversion with scale 1: exact
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    uint32_t r[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (DT == kBF16) {
-        const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
-        const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
-        __builtin_memcpy(&r[2 * i], &a, 4);
-        __builtin_memcpy(&r[2 * i + 1], &b, 4);
-      } else {
-        const auto a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
-        const auto b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
-        __builtin_memcpy(&r[2 * i], &a, 4);
-        __builtin_memcpy(&r[2 * i + 1], &b, 4);
-      }
-    }
-    lo = u32x4{r[0], r[1], r[2], r[3]};
-    hi = u32x4{r[4], r[5], r[6], r[7]};
-    return;
-  }
-  float f[16];
-  codes16<QT>(c, f);
-  lo = u32x4{pack_exact16<DT>(f[0], f[1]), pack_exact16<DT>(f[2], f[3]),
-             pack_exact16<DT>(f[4], f[5]), pack_exact16<DT>(f[6], f[7])};
-  hi = u32x4{pack_exact16<DT>(f[8], f[9]), pack_exact16<DT>(f[10], f[11]),
-             pack_exact16<DT>(f[12], f[13]), pack_exact16<DT>(f[14], f[15])};
-}
-
-// Eight codes (two words) as exact 16-bit values of the q type: one operand.
-template <int DT, int QT>
-__device__ inline u32x4 codes8_to_bits16(const uint2 c) {
-  const uint32_t w[2] = {c.x, c.y};
-  uint32_t r[4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if constexpr (QT == kFP8) {  // packed scaled conversion with scale 1: exact
-      if constexpr (DT == kBF16) {
-        const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
-        const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
-        __builtin_memcpy(&r[2 * i], &a, 4);
-        __builtin_memcpy(&r[2 * i + 1], &b, 4);
-      } else {
-        const auto a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
-        const auto b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
-        __builtin_memcpy(&r[2 * i], &a, 4);
-        __builtin_memcpy(&r[2 * i + 1], &b, 4);
-      }
-    } else {  // int8 as code + 128 (sign bit flipped): 0..255, exact in fp32 and 16 bits
-      const uint32_t u = w[i] ^ 0x80808080u;
-      r[2 * i] = pack_exact16<DT>(float(u & 0xffu), float((u >> 8) & 0xffu));
-      r[2 * i + 1] = pack_exact16<DT>(float((u >> 16) & 0xffu), float(u >> 24));
-    }
-  }
-  return u32x4{r[0], r[1], r[2], r[3]};
-}
 
 template <int DT, int QT, int D, int GT, class TU>
 __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_quant_kernel(
