@@ -15,7 +15,9 @@
 //    its KV once. The host picks the tile and the partition size per call.
 //  * Kernels: the VALU kernel below (one query head per KV head, fp32, groups
 //    not divisible by 4), the matrix-core kernel (16-bit GQA groups of 4+),
-//    and both for quantized pools; the reduce kernel merges the partitions.
+//    and both for quantized pools; ahead of them a one-workgroup ordering
+//    pass lists the partitions longest first, and after them the reduce
+//    kernel merges the partitions.
 //  * The workgroup first resolves every token of its partition to a pool row
 //    through the block table and keeps the row offsets in LDS; the token
 //    loop then needs no division and no table reads.
@@ -133,13 +135,13 @@ struct WorkItem {
   uint32_t s, part, g, h0;
 };
 
-// Grid order: head tile fastest, then sequence, then partition. A head tile
-// is GT query heads of one KV head, or the whole groups of kv_per_wg adjacent
-// KV heads. Every
-// sequence has a partition 0, so the first num_seqs*head_tiles workgroups all
-// carry work; the higher partitions, empty for short sequences, are
-// dispatched last where their early exit overlaps the tail of the launch.
-// Tile ht serves query heads [h0, h0 + GT) of KV head g.
+// Grid order: head tile fastest, then the (sequence, partition) pair. A head
+// tile is GT query heads of one KV head, or the whole groups of kv_per_wg
+// adjacent KV heads. The pairs are taken from the ordering pass's list
+// (longest partitions first, see below) when it ran, else in partition-major
+// order (every sequence has a partition 0, so the first num_seqs*head_tiles
+// workgroups all carry work). Tile ht serves query heads [h0, h0 + GT) of KV
+// head g.
 // With fewer head tiles than the 8 XCDs (T = head_tiles dividing 8), workgroups
 // dispatched round-robin over the XCDs would alternate consecutive sequences
 // between the R = 8/T XCDs that serve one head tile. CHUNKED remaps the block
