@@ -4,7 +4,9 @@ Each case draws a batch size, head counts, head size, page size, element and
 index type and a length mix from one seed, then runs the full step (slot
 mapping, store, decode) against the oracle with NaN-poisoned unused pool rows;
 the quantized cases run the int8 / fp8 decode against the quantized oracle,
-with NaN factors on the pages no sequence references.
+with NaN factors on the pages no sequence references; the prefill cases run
+chunked prefill (slot mapping, store, causal attention per chunk) over groups
+that alias a prefix, with chunk cuts inside pages.
 The draws cover the decode's launch plans: one, two or four KV heads per
 workgroup, 512- or 1024-token partitions, grids above and below the size at
 which partitions are dispatched longest first, ragged tails and pages that do
@@ -85,3 +87,28 @@ def test_random_shape_quant_decode(seed):
         host_threads())
     max_err, ratio, finite = decode_errors(w.dtype, host_bits(out), ref)
     assert finite and ratio <= 1.0, max_err
+
+
+PSEEDS = list(range(301, 313))
+
+
+def _draw_prefill(seed):
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2, 4]))
+    group = int(rng.choice([1, 2, 3, 4, 8]))
+    d = int(rng.choice([32, 64, 128, 256]))
+    bs = int(rng.choice([4, 12, 16, 64]))
+    prefix_pages = int(rng.integers(0, 6))
+    return workloads.chunked_prefill(
+        f"psweep{seed}", str(rng.choice(["bf16", "f16"])), str(rng.choice(["u32", "u64"])), seed,
+        groups=int(rng.integers(1, 4)), group_size=int(rng.integers(1, 4)),
+        prefix_tokens=prefix_pages * bs, n_chunks=int(rng.integers(1, 4)),
+        num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=d, bs=bs,
+        tail_lo=int(rng.integers(1, 50)), tail_hi=int(rng.integers(50, 500)))
+
+
+@pytest.mark.parametrize("seed", PSEEDS)
+def test_random_shape_prefill(seed):
+    from test_gpu_prefill import _run
+    w = _draw_prefill(seed)
+    _run(w)
