@@ -490,7 +490,7 @@ def main_prefill(args, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has "
               "no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
