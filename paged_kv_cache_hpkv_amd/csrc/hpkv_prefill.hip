@@ -21,9 +21,10 @@
 //    rows as JT column blocks of the transposed score tile.
 //  * Key loop over 32-key tiles from token 0 to the block's last position.
 //    Loading lanes resolve their key's pool row through the block table one
-//    tile ahead of use, fetch K and V rows with 16-byte loads one tile ahead
-//    of the product, and write them into a double-buffered LDS tile (one
-//    barrier per tile).
+//    tile ahead of use and fetch K and V rows one tile ahead of the product
+//    into a double-buffered LDS tile (one barrier per tile): at head_dim 128
+//    with direct-to-LDS loads into XOR-swizzled rows, otherwise with 16-byte
+//    loads staged through registers into padded rows.
 //  * S^T = K Q^T with v_mfma_f32_16x16x32 (A = K rows from LDS, B = q held in
 //    registers for the whole loop; lane layout A[l%16][8(l/16)+e],
 //    B[8(l/16)+e][l%16], D[4(l/16)+r][l%16]). Lane l ends with keys
@@ -121,14 +122,24 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
   constexpr int RPP = LOADERS / CPR;                    // tile rows per load pass
   constexpr int NP = kKeyTile / RPP;                    // load passes per tile
   static_assert(kKeyTile % RPP == 0 && LOADERS % CPR == 0, "load mapping");
-  constexpr int KROW = D * 2 + 16;  // LDS bytes per K row: 16-byte lane reads hit distinct banks
-  constexpr int VROW = D * 2 + 32;  // LDS bytes per V row: transposed 8-byte reads likewise
+  // head_dim 128: K/V tiles arrive by direct-to-LDS loads into unpadded rows whose 16-byte
+  // chunks are XOR-swizzled by row (see dma_kv); other head sizes stage the tiles through
+  // registers into padded rows (16-byte K reads and transposed 8-byte V reads on distinct
+  // banks either way).
+  constexpr bool DL = D == 128;
+  constexpr int KROW = DL ? D * 2 : D * 2 + 16;  // LDS bytes per K row
+  constexpr int VROW = DL ? D * 2 : D * 2 + 32;  // LDS bytes per V row
   constexpr int KS = D / 32;        // k-steps of the score product
   constexpr int NB = D / 16;        // 16-column blocks of O^T
   constexpr int ROWS = NW * 16 * JT;
 
-  __shared__ __attribute__((aligned(16))) char s_k[2][kKeyTile * KROW];
-  __shared__ __attribute__((aligned(16))) char s_v[2][kKeyTile * VROW];
+  // the two buffers of the double-buffered tile are separate LDS objects, so the compiler
+  // can tell a direct-to-LDS load into one from a read of the other and need not wait for
+  // the load before the read
+  __shared__ __attribute__((aligned(16))) char s_k0[kKeyTile * KROW];
+  __shared__ __attribute__((aligned(16))) char s_k1[kKeyTile * KROW];
+  __shared__ __attribute__((aligned(16))) char s_v0[kKeyTile * VROW];
+  __shared__ __attribute__((aligned(16))) char s_v1[kKeyTile * VROW];
   __shared__ uint32_t s_rows[kSegKeys];  // pool row of each key of the current segment
 
   const uint32_t tid = threadIdx.x;
@@ -252,15 +263,42 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const uint32_t r = p * RPP + lr;
-      *reinterpret_cast<u32x4*>(&s_k[b][r * KROW + lc * 16]) = kr[p];
-      *reinterpret_cast<u32x4*>(&s_v[b][r * VROW + lc * 16]) = vr[p];
+      *reinterpret_cast<u32x4*>(&(b ? s_k1 : s_k0)[r * KROW + lc * 16]) = kr[p];
+      *reinterpret_cast<u32x4*>(&(b ? s_v1 : s_v0)[r * VROW + lc * 16]) = vr[p];
+    }
+  };
+  // Direct-to-LDS tile load (head_dim 128): 16 lanes per 256-byte row, so one wave's
+  // global_load_lds_dwordx4 covers 4 whole rows, and lane i's 16 bytes land at the wave's
+  // LDS base + 16 i (the wave's rows are contiguous, unpadded). Lane (lr, lc) fetches
+  // logical chunk lc ^ (lr & 15) of its row, so LDS chunk lc of tile row r holds logical
+  // chunk lc ^ (r & 15): the 16 rows a K operand read touches at one logical chunk, and
+  // the four rows of a transposed V read, fall on distinct banks.
+  const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint64_t dl_head = uint64_t(g) * D_ * 2 + uint64_t((lc ^ (lr & 15u)) * 16u);
+  const char* kdl = static_cast<const char*>(a.k_cache) + dl_head;
+  const char* vdl = static_cast<const char*>(a.v_cache) + dl_head;
+  auto dma_kv = [&](uint32_t tl, auto buf_tag) {
+    constexpr int b = decltype(buf_tag)::value;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint64_t off = uint64_t(s_rows[tl + p * RPP + lr]) * row_stride;
+      const uint32_t r0 = p * RPP + 4 * wave_u;  // first of the wave's four rows
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void*)(kdl + off),
+          (__attribute__((address_space(3))) void*)(&(b ? s_k1 : s_k0)[r0 * KROW]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void*)(vdl + off),
+          (__attribute__((address_space(3))) void*)(&(b ? s_v1 : s_v0)[r0 * VROW]), 16, 0, 0);
     }
   };
 
   // One 32-key tile: scores, online softmax, P.V. MASK: some key of the tile lies past
   // the position of some row of this wave (the diagonal tiles); the others skip the mask.
-  auto tile = [&](auto mask_tag, int b, uint32_t tb) {
+  // buf: the LDS buffer, a compile-time constant on the direct-to-LDS path (each buffer a
+  // distinct object in the code), a runtime index otherwise
+  auto tile = [&](auto mask_tag, auto buf, uint32_t tb) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    const int b = int(buf);
     // scores: keys tb + 16u + 4*q4 + r of row `col` of each column block
     f32x4 sacc[2][JT];
 #pragma unroll
@@ -270,7 +308,8 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const u32x4 kop = *reinterpret_cast<const u32x4*>(
-            &s_k[b][(16 * u + col) * KROW + (32 * ks + 8 * q4) * 2]);
+            DL ? &(b ? s_k1 : s_k0)[(16 * u + col) * KROW + (((4 * ks + q4) ^ col) * 16)]
+               : &(b ? s_k1 : s_k0)[(16 * u + col) * KROW + (32 * ks + 8 * q4) * 2]);
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
           sacc[u][jt] = mfma_16x16x32<DT>(kop, qop[jt][ks], sacc[u][jt]);
@@ -310,11 +349,14 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
     }
     // O^T += V^T P^T; lane (q4, col) fetches row 4*q4 + col/4 (and 16 + that) of the
     // tile, columns 16*nb + 4*(col%4) .. +3, and receives column 16*nb + col.
-    const char* vrow0 = &s_v[b][(4 * q4 + col / 4) * VROW + 8 * (col % 4)];
+    const uint32_t vr_row = 4 * q4 + col / 4;
+    const char* vrow0 = &(b ? s_v1 : s_v0)[vr_row * VROW + 8 * (col % 4)];
+    const char* vrowd = &(b ? s_v1 : s_v0)[vr_row * VROW + 8 * ((col % 4) & 1)];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const uint2 lo = lds_read_tr16(vrow0 + 32 * nb);
-      const uint2 hi = lds_read_tr16(vrow0 + 16 * VROW + 32 * nb);
+      const uint32_t vch = (2 * nb + (col % 4) / 2) ^ (vr_row & 15);
+      const uint2 lo = lds_read_tr16(DL ? vrowd + 16 * vch : vrow0 + 32 * nb);
+      const uint2 hi = lds_read_tr16(DL ? vrowd + 16 * VROW + 16 * vch : vrow0 + 16 * VROW + 32 * nb);
       const u32x4 vop = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) acc[jt][nb] = mfma_16x16x32<DT>(vop, pop[jt], acc[jt][nb]);
@@ -340,25 +382,52 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
       s_rows[k] = uint32_t(ph * a.page_size + (key - pg * a.page_size));
     }
     __syncthreads();
-    if (loader) {
-      load_kv(0);
-      store_lds(0);
-    }
-    __syncthreads();
-    for (uint32_t it = 0; it < seg_tiles; ++it) {
-      const uint32_t tb = seg0 + it * kKeyTile;
-      const int b = it & 1;
-      const bool has_next = it + 1 < seg_tiles;
-      if (loader && has_next) load_kv((it + 1) * kKeyTile);
-      if (wave_active) {
-        if (int32_t(tb + kKeyTile - 1) <= min_pos) {
-          tile(std::false_type{}, b, tb);
-        } else {
-          tile(std::true_type{}, b, tb);
-        }
-      }
-      if (loader && has_next) store_lds(b ^ 1);
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    if constexpr (DL) {
+      // tile it + 1 streams into the other buffer while tile it is computed; each thread
+      // waits for its own loads before the barrier that hands the buffer over
+      dma_kv(0, B0{});
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      auto step = [&](uint32_t it, auto cur, auto nxt) {
+        const uint32_t tb = seg0 + it * kKeyTile;
+        if (it + 1 < seg_tiles) dma_kv((it + 1) * kKeyTile, nxt);
+        if (wave_active) {
+          if (int32_t(tb + kKeyTile - 1) <= min_pos) {
+            tile(std::false_type{}, cur, tb);
+          } else {
+            tile(std::true_type{}, cur, tb);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      };
+      for (uint32_t it = 0; it < seg_tiles; it += 2) {
+        step(it, B0{}, B1{});
+        if (it + 1 < seg_tiles) step(it + 1, B1{}, B0{});
+      }
+    } else {
+      if (loader) {
+        load_kv(0);
+        store_lds(0);
+      }
+      __syncthreads();
+      for (uint32_t it = 0; it < seg_tiles; ++it) {
+        const uint32_t tb = seg0 + it * kKeyTile;
+        const int b = it & 1;
+        const bool has_next = it + 1 < seg_tiles;
+        if (loader && has_next) load_kv((it + 1) * kKeyTile);
+        if (wave_active) {
+          if (int32_t(tb + kKeyTile - 1) <= min_pos) {
+            tile(std::false_type{}, b, tb);
+          } else {
+            tile(std::true_type{}, b, tb);
+          }
+        }
+        if (loader && has_next) store_lds(b ^ 1);
+        __syncthreads();
+      }
     }
   }
 
