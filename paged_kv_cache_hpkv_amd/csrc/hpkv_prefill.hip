@@ -269,14 +269,15 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
   };
   // Direct-to-LDS tile load (head_dim 128): 16 lanes per 256-byte row, so one wave's
   // global_load_lds_dwordx4 covers 4 whole rows, and lane i's 16 bytes land at the wave's
-  // LDS base + 16 i (the wave's rows are contiguous, unpadded). Lane (lr, lc) fetches
-  // logical chunk lc ^ (lr & 15) of its row, so LDS chunk lc of tile row r holds logical
-  // chunk lc ^ (r & 15): the 16 rows a K operand read touches at one logical chunk, and
-  // the four rows of a transposed V read, fall on distinct banks.
+  // LDS base + 16 i (the wave's rows are contiguous, unpadded). Lane (lr, lc) fetches the
+  // logical chunk that belongs at LDS chunk lc of its row: for K, LDS chunk c of tile row
+  // r holds logical chunk c ^ (r & 15), so the 16 rows of a K operand read at one logical
+  // chunk sit on distinct banks; for V, c ^ 2 (r & 7), which permutes whole 32-byte pairs,
+  // so the four rows of a transposed V read (two 8-byte pieces of one pair each) do.
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const uint64_t dl_head = uint64_t(g) * D_ * 2 + uint64_t((lc ^ (lr & 15u)) * 16u);
-  const char* kdl = static_cast<const char*>(a.k_cache) + dl_head;
-  const char* vdl = static_cast<const char*>(a.v_cache) + dl_head;
+  const uint64_t dl_head = uint64_t(g) * D_ * 2;
+  const char* kdl = static_cast<const char*>(a.k_cache) + dl_head + (lc ^ (lr & 15u)) * 16u;
+  const char* vdl = static_cast<const char*>(a.v_cache) + dl_head + (lc ^ (2u * (lr & 7u))) * 16u;
   auto dma_kv = [&](uint32_t tl, auto buf_tag) {
     constexpr int b = decltype(buf_tag)::value;
 #pragma unroll
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
     const char* vrowd = &(b ? s_v1 : s_v0)[vr_row * VROW + 8 * ((col % 4) & 1)];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const uint32_t vch = (2 * nb + (col % 4) / 2) ^ (vr_row & 15);
+      const uint32_t vch = (2 * nb + (col % 4) / 2) ^ (2 * (vr_row & 7));
       const uint2 lo = lds_read_tr16(DL ? vrowd + 16 * vch : vrow0 + 32 * nb);
       const uint2 hi = lds_read_tr16(DL ? vrowd + 16 * VROW + 16 * vch : vrow0 + 16 * VROW + 32 * nb);
       const u32x4 vop = u32x4{lo.x, lo.y, hi.x, hi.y};
