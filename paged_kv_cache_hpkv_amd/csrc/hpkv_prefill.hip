@@ -449,17 +449,19 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
 }
 
 // Launch shape per head size: 16-row column blocks per wave (JT), waves per
-// workgroup (NW) and workgroups per CU (MINB). Every operand byte read from LDS
-// feeds JT matrix-core products, and the LDS read rate (not the matrix cores)
-// bounds a one-block wave, so two blocks per wave is the best balance where the
-// registers allow it; at head_dim 256 the accumulators of two blocks do not fit
-// two waves per SIMD, so it keeps one block per wave and eight waves per
-// workgroup. Every shape covers 128 rows per workgroup. The chain scores ->
+// workgroup (NW) and the launch bound's minimum workgroups per CU (MINB).
+// Every operand byte read from LDS feeds JT matrix-core products, and the LDS
+// read rate (not the matrix cores) bounds a one-block wave, so two blocks per
+// wave is the best balance where the registers allow it; at head_dim 256 the
+// accumulators of two blocks do not fit two waves per SIMD, so it keeps one
+// block per wave and eight waves per workgroup. Every shape covers 128 rows
+// per workgroup. The chain scores ->
 // softmax -> P.V of one wave is latency-bound, so more waves per SIMD pay: at
 // head_dim 128 three workgroups per CU cap the registers at 168, which costs
 // four spilled registers stored before the tile loop and reloaded after it
-// (three waves per SIMD; LDS 3 x 49 KB). head_dim 32 and 64 reach four waves
-// per SIMD at two workgroups per CU by their registers alone.
+// (three waves per SIMD; LDS 3 x 49 KB). head_dim 32 and 64 need no tighter
+// bound: their registers (at most 128) and LDS (at most 36 KB) already let
+// four workgroups share a CU, four waves per SIMD.
 template <int DT, int D>
 struct PrefillShape {
   static constexpr int JT = D >= 256 ? 1 : 2;
