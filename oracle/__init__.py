@@ -42,8 +42,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIB):
-        _build.build()
+    _build.ensure_built()
     lib = ctypes.CDLL(_build.LIB)
     vp, u64, i64, i32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int
     lib.orc_validate_index_buffers.argtypes = [i32, u64, u64, vp, vp, u64, vp, u64]

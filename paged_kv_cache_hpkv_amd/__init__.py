@@ -4,8 +4,9 @@ Argument marshalling only: every function below forwards to the C entry point
 of the same name declared in include/hpkv.h, passing tensor data pointers,
 sizes read from tensor shapes and the current HIP stream. All computation runs
 in the library's HIP kernels; there is no CPU fallback. Importing works
-without a GPU (the library loads; host-only helpers run), but the library must
-have been built: a missing libhpkv.so raises at import.
+without a GPU (the library loads; host-only helpers run). A libhpkv.so that is
+missing, or older than its sources, is first built with hipcc by build.py (a
+build, not a fallback); if that build fails, the import raises.
 
 Device tensors are torch tensors on a ROCm device. Index tensors
 (block_table, seq_ptr) may be 32- or 64-bit (signed or unsigned); their width
@@ -54,9 +55,11 @@ class HpkvError(RuntimeError):
 
 
 def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python paged_kv_cache_hpkv_amd/build.py` (there is no fallback path)")
+    from . import build as _build  # the build script; it imports nothing from the package
+    try:
+        _build.ensure_built()
+    except Exception as e:  # no library means no path at all: fail loudly
+        raise ImportError(f"{LIB_PATH} could not be built ({e}); there is no fallback path") from e
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, u32, u64, f32 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint64,
                               ctypes.c_float)

@@ -46,7 +46,32 @@
 
 #include "hpkv_device.h"
 
+// The build compiles this file once per part so that its kernel instantiations
+// compile in parallel: part 0 holds the ordering and reduce kernels and the
+// host-side launch plan, parts 1-3 the fp32, fp16 and bf16 decode kernels and
+// parts 4-6 the quantized-pool kernels for fp32, fp16 and bf16 queries. Compiled without HPKV_DECODE_PART, one
+// object holds every part.
+#ifdef HPKV_DECODE_PART
+#define HPKV_DECODE_HAS(p) (HPKV_DECODE_PART == (p))
+#else
+#define HPKV_DECODE_HAS(p) 1
+#endif
+
 namespace hpkv {
+
+hipError_t launch_decode_f32(uint32_t head_dim, const DecodeKernelArgs& a, uint64_t nwg,
+                             hipStream_t stream);
+hipError_t launch_decode_f16(uint32_t head_dim, const DecodeKernelArgs& a, uint64_t nwg,
+                             hipStream_t stream);
+hipError_t launch_decode_bf16(uint32_t head_dim, const DecodeKernelArgs& a, uint64_t nwg,
+                              hipStream_t stream);
+hipError_t launch_decode_quant_f32(int kv_type, uint32_t head_dim, const DecodeKernelArgs& a,
+                                   uint64_t nwg, hipStream_t stream);
+hipError_t launch_decode_quant_f16(int kv_type, uint32_t head_dim, const DecodeKernelArgs& a,
+                                   uint64_t nwg, hipStream_t stream);
+hipError_t launch_decode_quant_bf16(int kv_type, uint32_t head_dim, const DecodeKernelArgs& a,
+                                    uint64_t nwg, hipStream_t stream);
+
 namespace {
 
 constexpr int kWave = 64;
@@ -207,6 +232,7 @@ __device__ inline uint32_t order_class(const DecodeKernelArgs& a, const int32_t*
   return (a.part_tokens - len) * 16u / a.part_tokens;  // 0 (full) .. 15
 }
 
+#if HPKV_DECODE_HAS(0)
 __global__ __launch_bounds__(kOrderWaves * kWave) void decode_order_kernel(
     const DecodeKernelArgs a) {
   __shared__ uint32_t s_cnt[kOrderClasses][kOrderWaves];
@@ -282,6 +308,7 @@ hipError_t launch_order(const DecodeKernelArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderWaves * kWave), 0, stream, a);
   return hipGetLastError();
 }
+#endif  // HPKV_DECODE_HAS(0)
 
 // Checks the item's sequence length and table slice, and resolves each token
 // of the partition to the element offset of head g's row in the pool (s_row);
@@ -1483,7 +1510,7 @@ hipError_t launch_pd(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream
 // Matrix-core path: 16-bit inputs, head_dim a multiple of 32 up to 128, and
 // at least 4 query heads per KV head (below that the VALU kernel already
 // streams at the bandwidth ceiling).
-bool mfma_eligible(int dtype, uint32_t head_dim, uint32_t group) {
+inline bool mfma_eligible(int dtype, uint32_t head_dim, uint32_t group) {
   return dtype != kF32 && (head_dim == 32 || head_dim == 64 || head_dim == 128) &&
          group % 4 == 0;
 }
@@ -1577,7 +1604,7 @@ hipError_t launch_quant_mfma(const DecodeKernelArgs& a, uint64_t nwg, hipStream_
   return hipGetLastError();
 }
 
-bool mfma_quant_eligible(int dtype, uint32_t head_dim, uint32_t group) {
+inline bool mfma_quant_eligible(int dtype, uint32_t head_dim, uint32_t group) {
   return dtype != kF32 && (head_dim == 32 || head_dim == 64 || head_dim == 128) &&
          group % 4 == 0;
 }
@@ -1627,6 +1654,49 @@ hipError_t launch_quant_kv(int kv_type, uint32_t head_dim, const DecodeKernelArg
 
 }  // namespace
 
+#if HPKV_DECODE_HAS(1)
+hipError_t launch_decode_f32(uint32_t head_dim, const DecodeKernelArgs& a, uint64_t nwg,
+                             hipStream_t stream) {
+  return launch_dt<kF32>(head_dim, a, nwg, stream);
+}
+#endif
+
+#if HPKV_DECODE_HAS(2)
+hipError_t launch_decode_f16(uint32_t head_dim, const DecodeKernelArgs& a, uint64_t nwg,
+                             hipStream_t stream) {
+  return launch_dt<kF16>(head_dim, a, nwg, stream);
+}
+#endif
+
+#if HPKV_DECODE_HAS(3)
+hipError_t launch_decode_bf16(uint32_t head_dim, const DecodeKernelArgs& a, uint64_t nwg,
+                              hipStream_t stream) {
+  return launch_dt<kBF16>(head_dim, a, nwg, stream);
+}
+#endif
+
+#if HPKV_DECODE_HAS(4)
+hipError_t launch_decode_quant_f32(int kv_type, uint32_t head_dim, const DecodeKernelArgs& a,
+                                   uint64_t nwg, hipStream_t stream) {
+  return launch_quant_kv<kF32>(kv_type, head_dim, a, nwg, stream);
+}
+#endif
+
+#if HPKV_DECODE_HAS(5)
+hipError_t launch_decode_quant_f16(int kv_type, uint32_t head_dim, const DecodeKernelArgs& a,
+                                   uint64_t nwg, hipStream_t stream) {
+  return launch_quant_kv<kF16>(kv_type, head_dim, a, nwg, stream);
+}
+#endif
+
+#if HPKV_DECODE_HAS(6)
+hipError_t launch_decode_quant_bf16(int kv_type, uint32_t head_dim, const DecodeKernelArgs& a,
+                                    uint64_t nwg, hipStream_t stream) {
+  return launch_quant_kv<kBF16>(kv_type, head_dim, a, nwg, stream);
+}
+#endif
+
+#if HPKV_DECODE_HAS(0)
 uint32_t heads_per_workgroup_quant(int dtype, uint32_t head_dim, uint32_t group) {
   if (mfma_quant_eligible(dtype, head_dim, group))
     return group % 16 == 0 ? 16 : group % 8 == 0 ? 8 : 4;
@@ -1641,9 +1711,9 @@ hipError_t launch_decode_partitions_quant(int dtype, int kv_type, uint32_t head_
   const hipError_t e = launch_order(a, stream);
   if (e != hipSuccess) return e;
   switch (dtype) {
-    case kF32: return launch_quant_kv<kF32>(kv_type, head_dim, a, num_workgroups, stream);
-    case kF16: return launch_quant_kv<kF16>(kv_type, head_dim, a, num_workgroups, stream);
-    case kBF16: return launch_quant_kv<kBF16>(kv_type, head_dim, a, num_workgroups, stream);
+    case kF32: return launch_decode_quant_f32(kv_type, head_dim, a, num_workgroups, stream);
+    case kF16: return launch_decode_quant_f16(kv_type, head_dim, a, num_workgroups, stream);
+    case kBF16: return launch_decode_quant_bf16(kv_type, head_dim, a, num_workgroups, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1682,9 +1752,9 @@ hipError_t launch_decode_partitions(int dtype, uint32_t head_dim, const DecodeKe
   const hipError_t e = launch_order(a, stream);
   if (e != hipSuccess) return e;
   switch (dtype) {
-    case kF32: return launch_dt<kF32>(head_dim, a, num_workgroups, stream);
-    case kF16: return launch_dt<kF16>(head_dim, a, num_workgroups, stream);
-    case kBF16: return launch_dt<kBF16>(head_dim, a, num_workgroups, stream);
+    case kF32: return launch_decode_f32(head_dim, a, num_workgroups, stream);
+    case kF16: return launch_decode_f16(head_dim, a, num_workgroups, stream);
+    case kBF16: return launch_decode_bf16(head_dim, a, num_workgroups, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1707,5 +1777,7 @@ hipError_t launch_decode_reduce(int dtype, const ReduceKernelArgs& a, hipStream_
   }
   return hipGetLastError();
 }
+
+#endif  // HPKV_DECODE_HAS(0)
 
 }  // namespace hpkv

@@ -126,6 +126,66 @@ def check_step(w: workloads.Workload, device="cuda", seed_poison=True, verbose=T
                 oracle_out64=o_out64, tensors=t)
 
 
+def decode_step_workload(w: workloads.Workload, empty_seq=None) -> workloads.Workload:
+    """Copy of `w` whose store step is the decode step's: one new token per sequence at
+    position ctx-1, none for an empty sequence; `empty_seq` (an index) is set to ctx 0."""
+    w2 = workloads.Workload(**{**w.__dict__})
+    w2.context_lens = w.context_lens.copy()
+    if empty_seq is not None and w2.num_seqs > empty_seq:
+        w2.context_lens[empty_seq] = 0
+    w2.chunks = workloads._decode_step_chunks(w2.context_lens)
+    w2.drop_mask = None
+    return w2
+
+
+def gpu_fused_step(w: workloads.Workload, t: workloads.Tensors):
+    """hpkv_paged_attention_decode_step on the decode-step workload `w` (one new row per
+    non-empty sequence in t.new_keys[0]); returns (slots [B], out)."""
+    dev = t.q.device
+    B = w.num_seqs
+    nk = torch.zeros(B, w.num_kv_heads, w.head_dim, dtype=t.q.dtype, device=dev)
+    nv = torch.zeros_like(nk)
+    has = torch.from_numpy(w.context_lens > 0).to(dev)
+    nk[has] = t.new_keys[0]
+    nv[has] = t.new_values[0]
+    out = torch.empty_like(t.q)
+    slots = torch.full((B,), 7, dtype=torch.int64, device=dev)
+    ws = hpkv.alloc_workspace(t.q, t.k_cache, w.max_context_len)
+    hpkv.hpkv_paged_attention_decode_step(
+        t.q, nk, nv, t.k_cache, t.v_cache, torch.from_numpy(w.block_table).to(dev),
+        torch.from_numpy(w.seq_ptr).to(dev), torch.from_numpy(w.context_lens).to(dev), w.scale,
+        w.max_context_len, ws, out, slots_out=slots)
+    torch.cuda.synchronize(dev)
+    return slots.cpu().numpy(), out
+
+
+def check_fused_step(w: workloads.Workload, device="cuda", empty_seq=1, verbose=True):
+    """The fused store-and-decode entry point against the oracle's slot mapping (position
+    ctx-1), store and decode on the same inputs: slots and both pools bit-exact, output within
+    tolerance; an empty sequence gets slot -1 and zeros."""
+    w = decode_step_workload(w, empty_seq)
+    if verbose:
+        print(f"[parity fused] {w.name} {w.dtype} {w.index} B={w.num_seqs} Hq={w.num_q_heads} "
+              f"Hkv={w.num_kv_heads} d={w.head_dim} bs={w.page_size}", flush=True)
+    t = workloads.make_tensors(w, device)
+    poison_unused(w, t)
+    h = host_inputs(t)
+    g_slots, g_out = gpu_fused_step(w, t)
+    o_slots, _, o_out64 = oracle_step(w, h)
+    want = np.full(w.num_seqs, -1, dtype=np.int64)
+    want[w.context_lens > 0] = o_slots[0]
+    np.testing.assert_array_equal(g_slots, want)
+    for name in ("k_cache", "v_cache"):
+        assert host_bits(getattr(t, name)).tobytes() == h[name].tobytes(), \
+            f"{name} differs after the fused store"
+    max_err, worst_ratio, finite = decode_errors(w.dtype, host_bits(g_out), o_out64)
+    assert finite, "non-finite fused decode output"
+    assert worst_ratio <= 1.0, f"fused decode error {max_err} above tolerance"
+    if empty_seq is not None and w.num_seqs > empty_seq:
+        assert not host_bits(g_out)[empty_seq].any(), "empty sequence must decode to zeros"
+    return dict(max_err=max_err, worst_ratio=worst_ratio)
+
+
 # ------------------------------------------------------------ chunked prefill
 
 def max_chunk_len(cu) -> int:

@@ -12,13 +12,13 @@ xxhash package.
 """
 import numpy as np
 import pytest
-import xxhash
 
 import oracle
 import paged_kv_cache_hpkv_amd as hpkv
 
 
 def test_xxh64_matches_xxhash_package():
+    xxhash = pytest.importorskip("xxhash")
     rng = np.random.default_rng(0)
     for n in list(range(0, 70)) + [127, 128, 1000]:
         data = rng.integers(0, 256, n, dtype=np.uint8).tobytes()

@@ -13,8 +13,8 @@ import torch
 import oracle
 import paged_kv_cache_hpkv_amd as hpkv
 import workloads
-from paths import check_step, decode_errors, gpu_step, host_bits, host_inputs, oracle_step, \
-    poison_unused
+from paths import (check_fused_step, check_step, decode_errors, gpu_step, host_bits, host_inputs,
+                   oracle_step, poison_unused)
 
 pytestmark = pytest.mark.gpu
 
@@ -291,3 +291,18 @@ def test_fused_decode_step_equals_separate_calls(make):
     want = np.full(B, -1, dtype=np.int64)
     want[w.context_lens > 0] = slots_sep[0]
     np.testing.assert_array_equal(slots.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("make", [lambda: workloads.llama7b(batch=12),
+                                  lambda: workloads.gqa(batch=40, dtype="f16"),
+                                  lambda: workloads.qwen3(batch=10),
+                                  lambda: workloads.tiny(bs=16, dtype="f32"),
+                                  lambda: workloads.tiny(bs=4, dtype="bf16", index="u64"),
+                                  lambda: workloads.prefix(groups=2, group_size=4)])
+def test_fused_decode_step_matches_oracle(make):
+    """hpkv_paged_attention_decode_step against the oracle directly: the new row lands at
+    position ctx-1 ("Paged KV Cache · AI infra interview lesson", Common Pitfalls and Walk the
+    Shapes First), slots and pools bit-exact, output within tolerance, an empty sequence
+    decodes to zeros with slot -1."""
+    r = check_fused_step(make(), device="cuda")
+    print(f"fused max err {r['max_err']:.2e}")
