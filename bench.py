@@ -140,7 +140,7 @@ class Step:
                 slots_out=self.chunks[0][2])
             return
         for c, (start, cu, slots) in enumerate(self.chunks):
-            h.hpkv_slot_mapping(self.bt, self.sp, w.page_size, start, cu, slots)
+            h.hpkv_slot_mapping(self.bt, self.sp, w.page_size, w.num_pages, start, cu, slots)
             if self.drop is not None and c == 0:
                 slots.masked_fill_(self.drop, -1)
             h.hpkv_store_kvcache(t.new_keys[c], t.new_values[c], t.k_cache, t.v_cache, slots)
@@ -229,7 +229,7 @@ class QuantStep:
     def __call__(self):
         h, w, t, q = self.hpkv, self.w, self.t, self.qt
         for c, (start, cu, slots) in enumerate(self.chunks):
-            h.hpkv_slot_mapping(self.bt, self.sp, w.page_size, start, cu, slots)
+            h.hpkv_slot_mapping(self.bt, self.sp, w.page_size, w.num_pages, start, cu, slots)
             if self.drop is not None and c == 0:
                 slots.masked_fill_(self.drop, -1)
             h.hpkv_store_kvcache_quant(self.kv, t.new_keys[c], t.new_values[c], q.k_codes,
@@ -369,7 +369,7 @@ class PrefillStep:
     def __call__(self):
         h, w, t = self.hpkv, self.w, self.t
         for c, (start, cu, slots, _) in enumerate(self.chunks):
-            h.hpkv_slot_mapping(self.bt, self.sp, w.page_size, start, cu, slots)
+            h.hpkv_slot_mapping(self.bt, self.sp, w.page_size, w.num_pages, start, cu, slots)
             h.hpkv_store_kvcache(t.new_keys[c], t.new_values[c], t.k_cache, t.v_cache, slots)
             self.attention(c)
 

@@ -126,8 +126,11 @@ int hpkv_validate_shape(uint32_t rank, const uint64_t* dims);
  * position p = start_pos[s] + (i - cu_new[s]) and gets
  *   slots[i] = block_table[seq_ptr[s] + p/page_size] * page_size + p%page_size.
  * A chunk may start part-way into a page (prefix hit, second half of a
- * chunked prefill). A position whose page is not in the sequence's slice, or
- * whose block_table index is >= block_table_len, gets -1 (the skip value).
+ * chunked prefill). A position whose page is not in the sequence's slice,
+ * whose block_table index is >= block_table_len, or whose page id is
+ * >= num_pages (outside the pool: the storage invariant of "Block-Paged KV
+ * Cache", section "Validating index buffers", does not hold there) gets -1,
+ * the skip value, so a store never writes outside the pool.
  *   block_table  device, block_table_len entries of index_type
  *   seq_ptr      device, num_seqs + 1 entries of index_type
  *   start_pos    device int32 [num_seqs]
@@ -138,7 +141,7 @@ int hpkv_validate_shape(uint32_t rank, const uint64_t* dims);
  * ------------------------------------------------------------------------- */
 int hpkv_slot_mapping(int index_type, const void* block_table, uint64_t block_table_len,
                       const void* seq_ptr, uint32_t num_seqs, uint32_t page_size,
-                      const int32_t* start_pos, const int64_t* cu_new, uint64_t num_new,
+                      uint64_t num_pages, const int32_t* start_pos, const int64_t* cu_new, uint64_t num_new,
                       int64_t* slots, void* stream);
 
 /* ---------------------------------------------------------------------------
@@ -205,7 +208,15 @@ uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_se
  * the context in the last page are never loaded, so their contents, NaN
  * included, do not matter). n == 0 gives zeros.
  * Arithmetic: fp32 dot products and online softmax, fp32 accumulation, one
- * rounding (nearest-even) to dtype at the end.
+ * rounding (nearest-even) to dtype at the end; with one exception. For f16
+ * and bf16 with head_dim in {32, 64, 128} and num_q_heads / num_kv_heads a
+ * multiple of 4, the scores and P.V run on the matrix cores: there each
+ * softmax weight exp(z_t - running max) is rounded (nearest-even) to dtype
+ * before it multiplies V, and the softmax denominator sums those rounded
+ * weights, so the output is a convex combination of V rows with weights
+ * accurate to dtype's precision (about 2^-9 relative for bf16). Everything
+ * else (dot products, maxima, sums, the accumulator, the split merge) stays
+ * fp32.
  *   q, out            device [num_seqs, num_q_heads, head_dim] of dtype
  *   k_cache, v_cache  device pools of dtype
  *   block_table, seq_ptr  device, as above
@@ -380,9 +391,14 @@ int hpkv_store_kvcache_quant(int dtype, int kv_type, const void* key, const void
  *
  * hpkv_paged_attention_decode over quantized pools: every K/V element is
  * taken as scale * (value(code) - zero) of its page slot and KV head. q and
- * out keep dtype (f32, f16 or bf16); arithmetic is fp32 throughout (the page
+ * out keep dtype (f32, f16 or bf16); arithmetic is fp32 (the page
  * scale multiplies each score, the V scale each weight, and the zero points
- * enter as one correction per row). The workspace, its size function
+ * enter as one correction per row), except that on the matrix-core path
+ * (f16/bf16 q, head_dim in {32, 64, 128}, num_q_heads / num_kv_heads a
+ * multiple of 4) each weight times its V scale is rounded (nearest-even) to
+ * dtype before it multiplies the V codes, and the V zero-point correction
+ * uses those rounded products; the denominator sums the unrounded fp32
+ * weights. The workspace, its size function
  * (hpkv_paged_attention_decode_workspace_size with the same dtype), the
  * tail masking, the malformed-input NaN results and the argument errors are
  * those of hpkv_paged_attention_decode. Requirements: head_dim in

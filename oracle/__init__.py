@@ -50,9 +50,7 @@ def _load():
     lib.orc_element_offset.argtypes = [i32, u64, u64, u64, u64, u64, u64, u64, u64, vp, u64,
                                        vp, u64, vp]
     lib.orc_element_offset.restype = i32
-    lib.orc_compute_slot_mapping.argtypes = [vp, i64, i64, i64, i64, vp, i64]
-    lib.orc_compute_slot_mapping.restype = i64
-    lib.orc_slot_mapping.argtypes = [i32, vp, u64, vp, u64, u64, vp, vp, vp]
+    lib.orc_slot_mapping.argtypes = [i32, vp, u64, vp, u64, u64, u64, vp, vp, vp]
     lib.orc_slot_mapping.restype = i32
     lib.orc_store_kvcache.argtypes = [u64, vp, vp, vp, vp, vp, u64, u64, u64, u64, u64]
     lib.orc_store_kvcache.restype = i64
@@ -126,26 +124,16 @@ def element_offset(s, t, h, d, page_size, num_pages, num_heads, head_dim, block_
     return st, int(out[0])
 
 
-def compute_slot_mapping(block_table, start, end, block_size):
-    """Per-block range emission for one sequence (list of slots)."""
-    bt = np.ascontiguousarray(block_table, dtype=np.int64)
-    cap = max(0, end - start)
-    out = np.zeros(max(cap, 1), dtype=np.int64)
-    n = _load().orc_compute_slot_mapping(_ptr(bt), len(bt), start, end, block_size, _ptr(out), cap)
-    if n < 0:
-        raise ValueError("compute_slot_mapping: bad arguments or block table too short")
-    return out[:n].tolist()
-
-
-def slot_mapping(block_table, seq_ptr, page_size, start_pos, cu_new):
-    """Per-token slots over a CSR table (int64, -1 where no page)."""
+def slot_mapping(block_table, seq_ptr, page_size, num_pages, start_pos, cu_new):
+    """Per-token slots over a CSR table (int64, -1 where no page or a page id >= num_pages)."""
     seq_ptr = np.ascontiguousarray(seq_ptr)
     block_table = np.ascontiguousarray(block_table, dtype=seq_ptr.dtype)
     start_pos = np.ascontiguousarray(start_pos, dtype=np.int32)
     cu_new = np.ascontiguousarray(cu_new, dtype=np.int64)
     slots = np.zeros(max(int(cu_new[-1]), 1), dtype=np.int64)
     st = _load().orc_slot_mapping(_index_bytes(seq_ptr), _ptr(block_table), len(block_table),
-                                  _ptr(seq_ptr), len(seq_ptr) - 1, page_size, _ptr(start_pos),
+                                  _ptr(seq_ptr), len(seq_ptr) - 1, page_size, num_pages,
+                                  _ptr(start_pos),
                                   _ptr(cu_new), _ptr(slots))
     if st != OK:
         raise ValueError(f"slot_mapping: oracle status {st}")

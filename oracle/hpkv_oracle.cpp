@@ -385,40 +385,15 @@ int orc_element_offset(int index_bytes, uint64_t s, uint64_t t, uint64_t h, uint
                         block_table, block_table_len, seq_ptr, num_seqs, flat);
 }
 
-// [INT] "Step 1": the per-block range emission for one sequence with a plain
-// list of page ids. Positions [start, end) are covered block by block; only
-// the first block may begin part-way in (start % bs) and only the last may end
-// early (end - i*bs). start >= end yields nothing. Returns the number of slots
-// written to out (at most out_cap), or -1 on bad arguments or a missing page.
-int64_t orc_compute_slot_mapping(const int64_t* block_table, int64_t block_table_len,
-                                 int64_t start, int64_t end, int64_t block_size, int64_t* out,
-                                 int64_t out_cap) {
-  if (block_size <= 0 || start < 0) return -1;
-  if (start >= end) return 0;
-  const int64_t start_block = start / block_size;
-  const int64_t end_block = (end + block_size - 1) / block_size;
-  if (end_block > block_table_len) return -1;
-  int64_t count = 0;
-  for (int64_t i = start_block; i < end_block; ++i) {
-    const int64_t base = block_table[i] * block_size;
-    const int64_t lo = (i == start_block) ? start % block_size : 0;
-    const int64_t hi = (i == end_block - 1) ? end - i * block_size : block_size;
-    for (int64_t slot = base + lo; slot < base + hi; ++slot) {
-      if (count >= out_cap) return -1;
-      out[count++] = slot;
-    }
-  }
-  return count;
-}
-
 // [INT] "Walk the Shapes First" / "Step 1" per-token rule over the CSR table:
 // new-token row i of sequence s (cu_new[s] <= i < cu_new[s+1]) sits at position
 // p = start_pos[s] + (i - cu_new[s]), and its slot is
 // block_table[seq_ptr[s] + p/bs]*bs + p%bs. A position whose page is not in the
-// sequence's slice gets -1 (reading: no slot).
+// sequence's slice, or whose page id is not below num_pages, gets -1 (reading:
+// no slot; [HUR] "Validating index buffers" requires every id < num_pages).
 int orc_slot_mapping(int index_bytes, const void* block_table, uint64_t block_table_len,
                      const void* seq_ptr, uint64_t num_seqs, uint64_t page_size,
-                     const int32_t* start_pos, const int64_t* cu_new, int64_t* slots) {
+                     uint64_t num_pages, const int32_t* start_pos, const int64_t* cu_new, int64_t* slots) {
   if (page_size == 0 || seq_ptr == nullptr || start_pos == nullptr || cu_new == nullptr)
     return ORC_BAD_ARG;
   for (uint64_t s = 0; s < num_seqs; ++s) {
@@ -431,7 +406,7 @@ int orc_slot_mapping(int index_bytes, const void* block_table, uint64_t block_ta
         const uint64_t page_in_seq = uint64_t(p) / page_size;
         if (page_in_seq < last - first && first + page_in_seq < block_table_len) {
           const uint64_t phys = read_index(index_bytes, block_table, first + page_in_seq);
-          slot = int64_t(phys * page_size + uint64_t(p) % page_size);
+          if (phys < num_pages) slot = int64_t(phys * page_size + uint64_t(p) % page_size);
         }
       }
       slots[i] = slot;

@@ -70,7 +70,7 @@ def _load():
         "hpkv_element_offset": ([i32, u64, u64, u32, u32, u32, u64, u32, u32, vp, u64, vp, u64,
                                  vp], i32),
         "hpkv_validate_shape": ([u32, vp], i32),
-        "hpkv_slot_mapping": ([i32, vp, u64, vp, u32, u32, vp, vp, u64, vp, vp], i32),
+        "hpkv_slot_mapping": ([i32, vp, u64, vp, u32, u32, u64, vp, vp, u64, vp, vp], i32),
         "hpkv_store_kvcache": ([i32, vp, vp, vp, vp, vp, u64, u32, u64, u32, u32, vp], i32),
         "hpkv_paged_attention_decode_workspace_size": ([i32, u32, u32, u32, u32, u32], sz),
         "hpkv_paged_attention_decode_partition_tokens": ([i32, u32, u32, u32, u32, u32, u32],
@@ -200,8 +200,10 @@ def hpkv_paged_attention_decode_partition_tokens(dtype, num_seqs, num_q_heads, n
 
 # -------------------------------------------------------------- device entry points
 
-def hpkv_slot_mapping(block_table, seq_ptr, page_size, start_pos, cu_new, slots, stream=None):
-    """slots[i] for every new token (int64, -1 where the page is missing)."""
+def hpkv_slot_mapping(block_table, seq_ptr, page_size, num_pages, start_pos, cu_new, slots,
+                      stream=None):
+    """slots[i] for every new token (int64, -1 where the page is missing or outside the pool
+    of num_pages pages)."""
     _contig(block_table, seq_ptr, start_pos, cu_new, slots)
     assert start_pos.dtype == torch.int32 and cu_new.dtype == torch.int64
     assert slots.dtype == torch.int64
@@ -209,7 +211,7 @@ def hpkv_slot_mapping(block_table, seq_ptr, page_size, start_pos, cu_new, slots,
     assert block_table.element_size() == seq_ptr.element_size()
     _check("hpkv_slot_mapping", lib.hpkv_slot_mapping(
         it, _ptr(block_table), block_table.numel(), _ptr(seq_ptr), seq_ptr.numel() - 1,
-        page_size, _ptr(start_pos), _ptr(cu_new), slots.numel(), _ptr(slots),
+        page_size, int(num_pages), _ptr(start_pos), _ptr(cu_new), slots.numel(), _ptr(slots),
         _stream(stream, slots)))
 
 

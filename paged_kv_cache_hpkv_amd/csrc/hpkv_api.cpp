@@ -293,7 +293,7 @@ int hpkv_validate_shape(uint32_t rank, const uint64_t* dims) {
 
 int hpkv_slot_mapping(int index_type, const void* block_table, uint64_t block_table_len,
                       const void* seq_ptr, uint32_t num_seqs, uint32_t page_size,
-                      const int32_t* start_pos, const int64_t* cu_new, uint64_t num_new,
+                      uint64_t num_pages, const int32_t* start_pos, const int64_t* cu_new, uint64_t num_new,
                       int64_t* slots, void* stream) {
   if (!valid_index(index_type)) return HPKV_ERR_INVALID_ARG;
   if (page_size == 0) return HPKV_ERR_INVALID_ARG;
@@ -303,7 +303,7 @@ int hpkv_slot_mapping(int index_type, const void* block_table, uint64_t block_ta
   if (num_new > (uint64_t(0x7fffffff) * 256)) return HPKV_ERR_UNSUPPORTED;
   return hip_status(hpkv::launch_slot_mapping(
       index_type == HPKV_INDEX_U64, block_table, block_table_len, seq_ptr, num_seqs, page_size,
-      start_pos, cu_new, num_new, slots, static_cast<hipStream_t>(stream)));
+      num_pages, start_pos, cu_new, num_new, slots, static_cast<hipStream_t>(stream)));
 }
 
 int hpkv_store_kvcache(int dtype, const void* key, const void* value, void* k_cache,

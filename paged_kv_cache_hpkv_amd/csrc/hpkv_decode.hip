@@ -49,8 +49,8 @@
 // The build compiles this file once per part so that its kernel instantiations
 // compile in parallel: part 0 holds the ordering and reduce kernels and the
 // host-side launch plan, parts 1-3 the fp32, fp16 and bf16 decode kernels and
-// parts 4-6 the quantized-pool kernels for fp32, fp16 and bf16 queries. Compiled without HPKV_DECODE_PART, one
-// object holds every part.
+// parts 4-6 the quantized-pool kernels for fp32, fp16 and bf16 queries.
+// Compiled without HPKV_DECODE_PART, one object holds every part.
 #ifdef HPKV_DECODE_PART
 #define HPKV_DECODE_HAS(p) (HPKV_DECODE_PART == (p))
 #else

@@ -158,7 +158,7 @@ hipError_t launch_store_quant(int dtype, int kv_type, const void* key, const voi
 
 hipError_t launch_slot_mapping(bool idx64, const void* block_table, uint64_t block_table_len,
                                const void* seq_ptr, uint32_t num_seqs, uint32_t page_size,
-                               const int32_t* start_pos, const int64_t* cu_new, uint64_t num_new,
+                               uint64_t num_pages, const int32_t* start_pos, const int64_t* cu_new, uint64_t num_new,
                                int64_t* slots, hipStream_t stream);
 
 hipError_t launch_store(int chunk_bytes, const void* key, const void* value, void* k_cache,

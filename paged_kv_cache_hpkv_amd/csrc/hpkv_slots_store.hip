@@ -25,8 +25,9 @@ constexpr uint32_t kSlotLdsSeqs = 4096;
 template <typename Idx>
 __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
     const Idx* __restrict__ block_table, uint64_t block_table_len, const Idx* __restrict__ seq_ptr,
-    uint32_t num_seqs, uint32_t page_size, const int32_t* __restrict__ start_pos,
-    const int64_t* __restrict__ cu_new, uint64_t num_new, int64_t* __restrict__ slots) {
+    uint32_t num_seqs, uint32_t page_size, uint64_t num_pages,
+    const int32_t* __restrict__ start_pos, const int64_t* __restrict__ cu_new, uint64_t num_new,
+    int64_t* __restrict__ slots) {
   __shared__ int64_t s_cu[kSlotLdsSeqs + 1];
   const bool staged = num_seqs <= kSlotLdsSeqs;
   if (staged) {
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
       const uint64_t page_in_seq = uint64_t(p) / page_size;
       if (page_in_seq < last - first) {
         const uint64_t phys = block_table[first + page_in_seq];
-        slot = int64_t(phys * page_size + uint64_t(p) % page_size);
+        if (phys < num_pages) slot = int64_t(phys * page_size + uint64_t(p) % page_size);
       }
     }
   }
@@ -179,19 +180,19 @@ __global__ __launch_bounds__(kStoreThreads) void store_quant_kernel(
 
 hipError_t launch_slot_mapping(bool idx64, const void* block_table, uint64_t block_table_len,
                                const void* seq_ptr, uint32_t num_seqs, uint32_t page_size,
-                               const int32_t* start_pos, const int64_t* cu_new, uint64_t num_new,
+                               uint64_t num_pages, const int32_t* start_pos, const int64_t* cu_new, uint64_t num_new,
                                int64_t* slots, hipStream_t stream) {
   const uint64_t blocks = (num_new + kSlotThreads - 1) / kSlotThreads;
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
   if (idx64) {
     hipLaunchKernelGGL(slot_mapping_kernel<uint64_t>, dim3(uint32_t(blocks)), dim3(kSlotThreads),
                        0, stream, static_cast<const uint64_t*>(block_table), block_table_len,
-                       static_cast<const uint64_t*>(seq_ptr), num_seqs, page_size, start_pos,
+                       static_cast<const uint64_t*>(seq_ptr), num_seqs, page_size, num_pages, start_pos,
                        cu_new, num_new, slots);
   } else {
     hipLaunchKernelGGL(slot_mapping_kernel<uint32_t>, dim3(uint32_t(blocks)), dim3(kSlotThreads),
                        0, stream, static_cast<const uint32_t*>(block_table), block_table_len,
-                       static_cast<const uint32_t*>(seq_ptr), num_seqs, page_size, start_pos,
+                       static_cast<const uint32_t*>(seq_ptr), num_seqs, page_size, num_pages, start_pos,
                        cu_new, num_new, slots);
   }
   return hipGetLastError();

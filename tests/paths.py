@@ -36,7 +36,7 @@ def used_slots(w: workloads.Workload) -> np.ndarray:
     B = w.num_seqs
     cu = np.zeros(B + 1, dtype=np.int64)
     cu[1:] = np.cumsum(w.context_lens.astype(np.int64))
-    return oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, np.zeros(B, np.int32), cu)
+    return oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, w.num_pages, np.zeros(B, np.int32), cu)
 
 
 def poison_unused(w: workloads.Workload, t: workloads.Tensors):
@@ -62,7 +62,7 @@ def gpu_step(w: workloads.Workload, t: workloads.Tensors, max_context_len=None):
     slots_out = []
     for c, (start, cu) in enumerate(w.chunks):
         slots = torch.empty(int(cu[-1]), dtype=torch.int64, device=dev)
-        hpkv.hpkv_slot_mapping(bt, sp, w.page_size, torch.from_numpy(start).to(dev),
+        hpkv.hpkv_slot_mapping(bt, sp, w.page_size, w.num_pages, torch.from_numpy(start).to(dev),
                                torch.from_numpy(cu).to(dev), slots)
         slots_out.append(slots.cpu().numpy())
         if w.drop_mask is not None and c == 0:
@@ -81,7 +81,7 @@ def oracle_step(w: workloads.Workload, h: dict, threads=None):
     """The same step on the oracle, in place on the host copies `h`."""
     slots_out = []
     for c, (start, cu) in enumerate(w.chunks):
-        slots = oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, start, cu)
+        slots = oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, w.num_pages, start, cu)
         slots_out.append(slots.copy())
         if w.drop_mask is not None and c == 0:
             slots[w.drop_mask] = -1
@@ -204,7 +204,7 @@ def gpu_prefill(w: workloads.Workload, t: workloads.Tensors, queries, max_q_len=
         start_t = torch.from_numpy(start).to(dev)
         cu_t = torch.from_numpy(cu).to(dev)
         slots = torch.empty(int(cu[-1]), dtype=torch.int64, device=dev)
-        hpkv.hpkv_slot_mapping(bt, sp, w.page_size, start_t, cu_t, slots)
+        hpkv.hpkv_slot_mapping(bt, sp, w.page_size, w.num_pages, start_t, cu_t, slots)
         hpkv.hpkv_store_kvcache(t.new_keys[c], t.new_values[c], t.k_cache, t.v_cache, slots)
         out = torch.empty_like(queries[c])
         mq = max_chunk_len(cu) if max_q_len is None else max_q_len
@@ -253,7 +253,7 @@ def oracle_prefill(w: workloads.Workload, h: dict, q_bits_list, sample_rows=None
     mapping + store, then prefill of all its rows (or of sample_rows[c])."""
     outs = []
     for c, (start, cu) in enumerate(w.chunks):
-        slots = oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, start, cu)
+        slots = oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, w.num_pages, start, cu)
         oracle.store_kvcache(h["new_keys"][c], h["new_values"][c], h["k_cache"], h["v_cache"],
                              slots)
         if sample_rows is None:

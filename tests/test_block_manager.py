@@ -28,7 +28,7 @@ def test_xxh64_matches_xxhash_package():
 
 def _slot_by_oracle(bm, sid, pos):
     bt, sp, _ = bm.export([sid])
-    return int(oracle.slot_mapping(bt, sp, bm.page_size, np.array([pos], np.int32),
+    return int(oracle.slot_mapping(bt, sp, bm.page_size, bm.num_pages, np.array([pos], np.int32),
                                    np.array([0, 1], np.int64))[0])
 
 

@@ -260,8 +260,8 @@ def test_store_and_slot_mapping_argument_errors():
         hpkv.ERR_INVALID_ARG
     assert st(hpkv.BF16, None, None, None, None, None, 0, 16, 8, 2, 128, None) == hpkv.OK
     sm = hpkv.lib.hpkv_slot_mapping
-    assert sm(5, FAKE, 4, FAKE, 2, 16, FAKE, FAKE, 4, FAKE, None) == hpkv.ERR_INVALID_ARG
-    assert sm(hpkv.INDEX_U32, FAKE, 4, FAKE, 2, 0, FAKE, FAKE, 4, FAKE, None) == \
+    assert sm(5, FAKE, 4, FAKE, 2, 16, 8, FAKE, FAKE, 4, FAKE, None) == hpkv.ERR_INVALID_ARG
+    assert sm(hpkv.INDEX_U32, FAKE, 4, FAKE, 2, 0, 8, FAKE, FAKE, 4, FAKE, None) == \
         hpkv.ERR_INVALID_ARG
-    assert sm(hpkv.INDEX_U32, FAKE, 4, None, 2, 16, FAKE, FAKE, 4, FAKE, None) == hpkv.ERR_NULL
-    assert sm(hpkv.INDEX_U32, None, 0, None, 0, 16, None, None, 0, None, None) == hpkv.OK
+    assert sm(hpkv.INDEX_U32, FAKE, 4, None, 2, 16, 8, FAKE, FAKE, 4, FAKE, None) == hpkv.ERR_NULL
+    assert sm(hpkv.INDEX_U32, None, 0, None, 0, 16, 8, None, None, 0, None, None) == hpkv.OK

@@ -39,6 +39,7 @@ def test_block_manager_tables_drive_decode(index):
         # the library's slot mapping of position ctx-1 gives the manager's slots
         g_slots = torch.empty(len(ids), dtype=torch.int64, device=DEV)
         hpkv.hpkv_slot_mapping(torch.from_numpy(bt).to(DEV), torch.from_numpy(sp).to(DEV), bs,
+                               bm.num_pages,
                                torch.from_numpy(ctx - 1).to(DEV),
                                torch.arange(len(ids) + 1, device=DEV), g_slots)
         assert np.array_equal(g_slots.cpu().numpy(), slots)

@@ -212,13 +212,15 @@ def test_slot_mapping_edges():
         counts = np.array([9, 2, 0, 4])
         cu = np.zeros(5, dtype=np.int64)
         cu[1:] = np.cumsum(counts)
-        slots = torch.empty(int(cu[-1]), dtype=torch.int64, device=dev)
-        hpkv.hpkv_slot_mapping(torch.from_numpy(bt).to(dev), torch.from_numpy(sp).to(dev), 4,
-                               torch.from_numpy(start).to(dev), torch.from_numpy(cu).to(dev),
-                               slots)
-        want = oracle.slot_mapping(bt, sp, 4, start, cu)
-        np.testing.assert_array_equal(slots.cpu().numpy(), want)
-        assert (want == -1).sum() >= 3  # past the slice, and the empty table
+        for num_pages in (6, 5, 3):  # 5 and 3 put pages 5 / 3-5 outside the pool
+            slots = torch.empty(int(cu[-1]), dtype=torch.int64, device=dev)
+            hpkv.hpkv_slot_mapping(torch.from_numpy(bt).to(dev), torch.from_numpy(sp).to(dev), 4,
+                                   num_pages, torch.from_numpy(start).to(dev),
+                                   torch.from_numpy(cu).to(dev), slots)
+            want = oracle.slot_mapping(bt, sp, 4, num_pages, start, cu)
+            np.testing.assert_array_equal(slots.cpu().numpy(), want)
+            assert (want == -1).sum() >= 3  # past the slice, and the empty table
+            assert (want < num_pages * 4).all()
 
 
 def test_partition_and_reduce_entry_points_match_decode():

@@ -45,14 +45,14 @@ def _step(w, kv, max_context_len=None):
     ctx = torch.from_numpy(w.context_lens).to(DEV)
     for c, (start, cu) in enumerate(w.chunks):
         slots = torch.empty(int(cu[-1]), dtype=torch.int64, device=DEV)
-        hpkv.hpkv_slot_mapping(bt, sp, w.page_size, torch.from_numpy(start).to(DEV),
+        hpkv.hpkv_slot_mapping(bt, sp, w.page_size, w.num_pages, torch.from_numpy(start).to(DEV),
                                torch.from_numpy(cu).to(DEV), slots)
         if w.drop_mask is not None and c == 0:
             slots[torch.from_numpy(w.drop_mask).to(DEV)] = -1
         hpkv.hpkv_store_kvcache_quant(kv, t.new_keys[c], t.new_values[c], qt.k_codes,
                                       qt.v_codes, qt.k_scale, qt.k_zero, qt.v_scale, qt.v_zero,
                                       slots)
-        o_slots = oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, start, cu)
+        o_slots = oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, w.num_pages, start, cu)
         if w.drop_mask is not None and c == 0:
             o_slots[w.drop_mask] = -1
         oracle.store_kvcache_quant(w.dtype, kv, host_bits(t.new_keys[c]),

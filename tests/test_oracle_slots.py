@@ -2,8 +2,8 @@
 
 "Paged KV Cache · AI infra interview lesson": the printed slots of Step 1 and
 the fifth-token question of "Why It Matters" (tests/golden/slot_mapping.txt),
-Step 1's property test (range emission equals the per-token rule for
-bs in {4, 16, 256}) and store test (a -1 slot leaves its row untouched, n-1
+Step 1's property test (slots emitted page by page equal the per-token rule
+for bs in {4, 16, 256}) and store test (a -1 slot leaves its row untouched, n-1
 rows written), the decode-slot pitfall of "Common Pitfalls" and the new-page
 rule of "Walk the Shapes First". Independently of any formula, slots are also
 checked against a numpy gather over a table of slot ids laid out like the pool.
@@ -21,10 +21,21 @@ def _csr(tables, dtype=np.uint32):
     return sp.astype(dtype), np.array([p for t in tables for p in t], dtype=dtype)
 
 
-def _per_token(bt, start, end, bs):
+def _per_token(bt, start, end, bs, num_pages=1 << 40):
     """CSR slot mapping of one sequence's positions [start, end)."""
     sp, flat = _csr([bt])
-    return oracle.slot_mapping(flat, sp, bs, [start], [0, max(0, end - start)]).tolist()
+    return oracle.slot_mapping(flat, sp, bs, num_pages, [start],
+                               [0, max(0, end - start)]).tolist()
+
+
+def _page_runs(bt, start, end, bs):
+    """Slots of positions [start, end) written as one contiguous run per logical page: page k
+    of the table contributes the offsets of [start, end) that fall inside [k*bs, (k+1)*bs)."""
+    out = []
+    for k, page in enumerate(bt):
+        lo, hi = max(start, k * bs), min(end, (k + 1) * bs)
+        out.extend(range(page * bs + lo - k * bs, page * bs + hi - k * bs))
+    return out
 
 
 def test_printed_slots():
@@ -35,7 +46,7 @@ def test_printed_slots():
         want, bt, nums = ints(want.strip()), ints(bt), [int(x) for x in nums]
         if kind == "ranges":
             a, b, bs = nums
-            assert oracle.compute_slot_mapping(bt, a, b, bs) == want
+            assert _page_runs(bt, a, b, bs) == want
             assert _per_token(bt, a, b, bs) == want
         else:  # one token at a position
             p, bs = nums
@@ -48,14 +59,14 @@ def test_printed_slots():
 def test_range_emission_equals_per_token_rule(bs):
     bt = [7, 2, 5]
     for start, end in [(0, 2 * bs + 2), (bs // 2 + 1, 2 * bs + 1), (bs, 2 * bs), (3, 3)]:
-        ranges = oracle.compute_slot_mapping(bt, start, end, bs)
+        ranges = _page_runs(bt, start, end, bs)
         assert ranges == _per_token(bt, start, end, bs)
         # independent of both: gather from a pool-shaped table of slot ids
         slot_ids = np.arange(8 * bs).reshape(8, bs)
         logical = slot_ids[np.array(bt)].reshape(-1)
         assert ranges == logical[start:end].tolist()
-    assert oracle.compute_slot_mapping(bt, 5, 5, bs) == []
-    assert oracle.compute_slot_mapping(bt, 7, 3, bs) == []
+    assert _per_token(bt, 5, 5, bs) == [] and _page_runs(bt, 5, 5, bs) == []
+    assert _per_token(bt, 7, 3, bs) == []
 
 
 def test_batch_slot_mapping_matches_gather():
@@ -71,13 +82,16 @@ def test_batch_slot_mapping_matches_gather():
             counts = rng.integers(0, 2 * bs + 1, size=B)
             cu = np.zeros(B + 1, dtype=np.int64)
             cu[1:] = np.cumsum(counts)
-            got = oracle.slot_mapping(flat, sp, bs, start, cu)
+            # a pool smaller than the ids in use: ids >= pool_pages have no slot
+            pool_pages = num_pages if trial % 2 else int(rng.integers(1, num_pages))
+            got = oracle.slot_mapping(flat, sp, bs, pool_pages, start, cu)
             slot_ids = np.arange(num_pages * bs).reshape(num_pages, bs)
             want = []
             for s, t in enumerate(tables):
                 logical = slot_ids[np.array(t, dtype=np.int64)].reshape(-1) if t else []
                 for p in range(start[s], start[s] + counts[s]):
-                    want.append(int(logical[p]) if p < len(logical) else -1)
+                    ok = p < len(logical) and t[p // bs] < pool_pages
+                    want.append(int(logical[p]) if ok else -1)
             assert got.tolist() == want
 
 
@@ -115,7 +129,7 @@ def test_store_matches_printed_test_and_numpy_scatter(bs):
     v_cache = np.zeros((8, bs, H, d), dtype=np.float32)
     key = rng.standard_normal((n, H, d)).astype(np.float32)
     value = rng.standard_normal((n, H, d)).astype(np.float32)
-    slots = np.array(oracle.compute_slot_mapping(bt, 0, n, bs), dtype=np.int64)
+    slots = np.array(_per_token(bt, 0, n, bs), dtype=np.int64)
     slots[1] = -1
     assert oracle.store_kvcache(key, value, k_cache, v_cache, slots) == 0
     for p in range(n):
