@@ -10,17 +10,29 @@ Default workload: the Llama-2-7B-shaped layer (Hq = Hkv = 32, d = 128,
 16-token pages, 64 sequences with ctx ~ U{512..4096}, bf16, u32 tables), one
 new token per sequence stored at position ctx-1 before decoding.
 
+Timing protocol (cold caches): before every timed call a 1 GiB scratch
+buffer is written, outside the timed interval, so no K/V byte can be served
+from the L2s or the 256 MB Infinity Cache; each call is bracketed by its own
+pair of HIP events on the launch stream, and the median over the calls is
+reported (mean, min and max beside it). --warm times back-to-back calls
+without the scratch writes instead; the warm back-to-back figure is printed
+beside the cold one in any case.
+
 Printed: ONE JSON line with
   value        KV bytes the decode must read per step (sum ctx * 2 * Hkv * d * b)
-               divided by the step time, in GB/s (1e9 B/s);
+               divided by the median step time, in GB/s (1e9 B/s);
   roofline     the partition pass alone (the dominant work: a one-workgroup
                ordering kernel of a few microseconds, then the partition
-               kernel), timed per launch with HIP events on the launch stream:
-               algorithmic bytes per launch (KV + q + out + block-table
-               entries + lengths) over its mean duration, against the 8 TB/s
-               HBM peak;
+               kernel), timed per launch as above: algorithmic bytes per
+               launch (KV + q + out + block-table entries + lengths) over its
+               median duration, against the 8 TB/s HBM peak;
+  ceilings     the library's read-ceiling kernel (hpkv_read_ceiling) on a
+               buffer the size of the step's K/V: a plain streaming read and
+               the decode's row pattern (256-byte rows at an 8 KiB and a
+               2 KiB stride), each timed like the kernels;
   cpu_baseline the CPU oracle (double precision, plain loops) running the same
-               step on host copies of the same inputs, timed on the host.
+               step on host copies of the same inputs, repeated for about ten
+               seconds and timed on the host (median per step).
 Inputs are resident in HBM before timing starts; nothing is skipped inside the
 timed region.
 
@@ -85,7 +97,96 @@ def parse():
                    help="decode over quantized pools (per page-slot, per KV head scales)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    p.add_argument("--warm", action="store_true",
+                   help="time back-to-back calls without clearing the caches in between")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the read-ceiling measurement")
+    p.add_argument("--ceiling", action="store_true",
+                   help="only measure the read ceilings (streaming and the decode's row "
+                        "pattern) on a buffer of the workload's K/V size")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="host time the cpu_baseline repeats the oracle for")
     return p.parse_args()
+
+
+SCRATCH_BYTES = 1 << 30
+
+
+class Timer:
+    """Per-call HIP-event timing on one stream. With cold=True a 1 GiB scratch buffer is
+    written before every call, outside its events, evicting the L2s and the 256 MB
+    Infinity Cache."""
+
+    def __init__(self, dev, stream, cold=True):
+        self.stream = stream
+        self.cold = cold
+        self.scratch = torch.empty(SCRATCH_BYTES, dtype=torch.uint8, device=dev) if cold else None
+        self.k = 0
+
+    def flush(self):
+        if self.scratch is not None:
+            self.k ^= 1
+            self.scratch.fill_(self.k)
+
+    def time(self, fn, n):
+        """Times n calls of fn; returns per-call statistics in ms and the wall time."""
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            self.flush()
+            starts[i].record(self.stream)
+            fn()
+            ends[i].record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        d = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)], dtype=np.float64)
+        return dict(median_ms=float(np.median(d)), mean_ms=float(d.mean()),
+                    min_ms=float(d.min()), max_ms=float(d.max()), wall_s=wall, n=n)
+
+    def warm(self, fn, n):
+        """Mean ms per call of n back-to-back calls (no cache clearing), one event pair."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for _ in range(n):
+            fn()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def protocol(self):
+        if self.cold:
+            return ("cold caches: 1 GiB scratch write before each call, outside its HIP event "
+                    "pair; median over the calls")
+        return "warm: back-to-back calls, each with its own HIP event pair; median"
+
+
+def ceilings(dev, timer, nbytes, launches=20):
+    """HBM read ceilings on a buffer of about nbytes (hpkv_read_ceiling), GB/s (median)."""
+    import paged_kv_cache_hpkv_amd as hpkv
+    stride_max = 8192
+    nbytes = max(stride_max, nbytes // stride_max * stride_max)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {}
+    for name, row, stride, rows_per_wg in (("stream", 4096, 4096, 64),
+                                          ("rows256_stride8k", 256, 8192, 512),
+                                          ("rows256_stride2k", 256, 2048, 512)):
+        def fn():
+            hpkv.hpkv_read_ceiling(buf, row, stride, rows_per_wg, sink)
+        fn()
+        st = timer.time(fn, launches)
+        read = nbytes // stride * stride
+        out[name] = dict(gbs=round(read / (st["median_ms"] * 1e-3) / 1e9, 1),
+                         median_ms=round(st["median_ms"], 5), bytes=read,
+                         row_bytes=row, stride_bytes=stride, rows_per_workgroup=rows_per_wg)
+    del buf
+    out["launches_each"] = launches
+    out["protocol"] = timer.protocol()
+    return out
 
 
 def make_workload(args):
@@ -155,13 +256,16 @@ class Step:
 
 
 def algorithmic_decode_bytes(w):
-    """Bytes the partition kernel must move: KV rows, q, out, table entries, lengths."""
+    """Bytes the partition kernel must move from HBM: KV rows, q, out, table entries,
+    lengths. A pool row that several sequences alias (shared prefix pages) has to come from
+    HBM only once, so the KV term counts distinct rows; without aliasing that is the
+    logical sum(ctx) * 2 * Hkv * d * b."""
     b = torch.tensor([], dtype=w.torch_dtype).element_size()
     idx = w.block_table.dtype.itemsize
     ctx = w.context_lens.astype(np.int64)
     pages = -(-ctx // w.page_size)
     per_seq = 2 * w.num_q_heads * w.head_dim * b + 4 + 2 * idx
-    return int(w.kv_bytes_logical() + pages.sum() * idx + per_seq * w.num_seqs)
+    return int(w.kv_bytes_unique_rows() + pages.sum() * idx + per_seq * w.num_seqs)
 
 
 def recorded_traffic(w, traffic_file=TRAFFIC_FILE, src=DECODE_SRC):
@@ -179,8 +283,22 @@ def recorded_traffic(w, traffic_file=TRAFFIC_FILE, src=DECODE_SRC):
     return rec.get("workloads", {}).get(f"{w.name}/{w.dtype}/{w.index}")
 
 
-def cpu_baseline(w, t, out_gpu):
-    """The oracle on the same step (host copies), all host threads."""
+def host_description():
+    """CPU model and the core counts the host reports."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}; nproc {len(os.sched_getaffinity(0))}, os.cpu_count {os.cpu_count()}"
+
+
+def cpu_baseline(w, t, out_gpu, seconds):
+    """The oracle on the same step (host copies), repeated for about `seconds`."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from paths import decode_errors, host_bits, host_threads, oracle_step  # noqa: E402
     # host copies of the step's inputs (the store already ran on the GPU, so
@@ -190,16 +308,21 @@ def cpu_baseline(w, t, out_gpu):
              new_keys=[host_bits(x) for x in t.new_keys],
              new_values=[host_bits(x) for x in t.new_values])
     threads = host_threads()
-    t0 = time.perf_counter()
-    _, _, out64 = oracle_step(w, h, threads)
-    dt = time.perf_counter() - t0
+    runs = []
+    t_start = time.perf_counter()
+    while not runs or (time.perf_counter() - t_start < seconds and len(runs) < 200):
+        t0 = time.perf_counter()
+        _, _, out64 = oracle_step(w, h, threads)
+        runs.append(time.perf_counter() - t0)
+    dt = float(np.median(runs))
     max_err, ratio, finite = decode_errors(w.dtype, host_bits(out_gpu), out64)
     return dict(value=round(w.kv_bytes_logical() / dt / 1e9, 4), unit="GB/s", cores=threads,
                 kind="oracle",
                 sample=f"the full timed step (slot mapping, store, decode of all {w.num_seqs} "
-                       f"sequences) once, double precision, {threads} host threads, "
-                       f"{dt:.2f} s"), dict(max_abs_err=max_err, within_tolerance=ratio <= 1.0
-                                            and finite)
+                       f"sequences), double precision, {threads} host threads, repeated "
+                       f"{len(runs)} times in {sum(runs):.1f} s, median {dt:.3f} s per step "
+                       f"({host_description()})"), \
+        dict(max_abs_err=max_err, within_tolerance=ratio <= 1.0 and finite)
 
 
 class QuantStep:
@@ -260,27 +383,17 @@ def main_quant(args, dev):
     qt = workloads.make_quant_tensors(w, args.kv, dev)
     step = QuantStep(w, t, qt, args.kv)
     stream = torch.cuda.current_stream(dev)
+    timer = Timer(dev, stream, cold=not args.warm)
     for _ in range(args.warmup):
+        timer.flush()
         step()
     torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.roofline_launches)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.roofline_launches)]
-    for i in range(args.roofline_launches):
-        starts[i].record(stream)
-        step.decode()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    st = timer.time(step, args.steps)
+    ms_per_step = st["median_ms"]
+    t_wall = st["wall_s"]
+    warm_ms = timer.warm(step, args.steps)
+    rt = timer.time(step.decode, args.roofline_launches)
+    dec_ms = rt["median_ms"]
     alg = algorithmic_quant_bytes(w)
     achieved = alg / (dec_ms * 1e-3) / 1e9
     kv = quant_kv_bytes(w)
@@ -307,8 +420,13 @@ def main_quant(args, dev):
             "kv_bytes_per_step": kv,
             "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
             "sequences_per_s_per_layer": round(w.num_seqs / (ms_per_step * 1e-3), 1),
-            "wall_s_timed_region": round(t_wall, 4),
             "step": "slot mapping + quantizing store + quantized decode (separate launches)",
+        },
+        "timing": {
+            "protocol": timer.protocol(),
+            "step_ms": {k: round(v, 5) for k, v in st.items() if k.endswith("_ms")},
+            "wall_s_timed_region": round(t_wall, 4),
+            "warm_back_to_back_ms_per_step": round(warm_ms, 5),
         },
         "roofline": {
             "kernel": "decode_order_kernel + decode_partition_quant_kernel + decode_reduce_kernel",
@@ -319,7 +437,8 @@ def main_quant(args, dev):
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
             "algorithmic_bytes_per_launch": alg,
-            "mean_launch_ms": round(dec_ms, 5),
+            "median_launch_ms": round(dec_ms, 5),
+            "mean_launch_ms": round(rt["mean_ms"], 5),
             "launches": args.roofline_launches,
         },
     }
@@ -408,35 +527,23 @@ def main_prefill(args, dev):
     queries = workloads.make_prefill_queries(w, dev)
     step = PrefillStep(w, t, queries)
     stream = torch.cuda.current_stream(dev)
+    timer = Timer(dev, stream, cold=not args.warm)
     for _ in range(args.warmup):
+        timer.flush()
         step()
     torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    st = timer.time(step, args.steps)
+    ms_per_step = st["median_ms"]
+    t_wall = st["wall_s"]
+    warm_ms = timer.warm(step, args.steps)
 
-    # the prefill kernel alone: per-launch HIP events on the launch stream
+    # the prefill kernel alone, per chunk: per-launch HIP events, same protocol
     nl = max(1, args.roofline_launches // len(w.chunks))
-    durs = [[] for _ in w.chunks]
-    for _ in range(nl):
-        for c in range(len(w.chunks)):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            step.attention(c)
-            b.record(stream)
-            durs[c].append((a, b))
-    torch.cuda.synchronize()
-    mean_ms = [float(np.mean([a.elapsed_time(b) for a, b in d])) for d in durs]
+    per = [timer.time(lambda c=c: step.attention(c), nl) for c in range(len(w.chunks))]
+    med_ms = [x["median_ms"] for x in per]
+    mean_ms = [x["mean_ms"] for x in per]
     flops = [prefill_flops(w, ch) for ch in w.chunks]
-    achieved = sum(flops) / (sum(mean_ms) * 1e-3) / 1e12
+    achieved = sum(flops) / (sum(med_ms) * 1e-3) / 1e12
     value = sum(flops) / (ms_per_step * 1e-3) / 1e12
     prec = recorded_traffic(w, PREFILL_TRAFFIC_FILE, PREFILL_SRC)
     line = {
@@ -459,8 +566,13 @@ def main_prefill(args, dev):
             "head_dim": w.head_dim, "page_size": w.page_size, "index": w.index,
             "query_rows_per_chunk": [int(cu[-1]) for _, cu in w.chunks],
             "flops_per_step": sum(flops),
-            "wall_s_timed_region": round(t_wall, 4),
             "step": "per chunk: slot mapping + store + prefill attention (separate launches)",
+        },
+        "timing": {
+            "protocol": timer.protocol(),
+            "step_ms": {k: round(v, 5) for k, v in st.items() if k.endswith("_ms")},
+            "wall_s_timed_region": round(t_wall, 4),
+            "warm_back_to_back_ms_per_step": round(warm_ms, 5),
         },
         "roofline": {
             "kernel": "prefill_mfma_kernel",
@@ -471,6 +583,7 @@ def main_prefill(args, dev):
             "frac": round(achieved / MFMA16_PEAK_TFLOPS, 4),
             "traffic": None if prec is None else prec.get("hbm_bytes_per_launch"),
             "algorithmic_flops_per_launch": flops,
+            "median_launch_ms": [round(x, 5) for x in med_ms],
             "mean_launch_ms": [round(x, 5) for x in mean_ms],
             "launches": nl * len(w.chunks),
         },
@@ -505,38 +618,31 @@ def main():
         main_quant(args, dev)
         return
     w = make_workload(args)
+    stream = torch.cuda.current_stream(dev)
+    timer = Timer(dev, stream, cold=not args.warm)
+    if args.ceiling:
+        line = {"metric": "HBM read ceiling (hpkv_read_ceiling)", "unit": "GB/s",
+                "config": {"workload": WORKLOAD_TEXT.get(w.name, w.name),
+                           "buffer_bytes": w.kv_bytes_logical()},
+                "ceilings": ceilings(dev, timer, w.kv_bytes_logical())}
+        print(json.dumps(line), flush=True)
+        return
     t = workloads.make_tensors(w, dev)
     step = Step(w, t, fused=is_decode_step(w) and not args.unfused)
-    stream = torch.cuda.current_stream(dev)
 
     if args.copy_calibration:
         calibration_copy(dev)
 
     for _ in range(args.warmup):
+        timer.flush()
         step()
     torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-
-    # dominant work alone (ordering + partition kernels): per-launch HIP events
-    # on the launch stream
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.roofline_launches)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.roofline_launches)]
-    for i in range(args.roofline_launches):
-        starts[i].record(stream)
-        step.partitions_only()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    part_ms = float(np.mean(durs))
+    st = timer.time(step, args.steps)            # the K timed steps
+    ms_per_step = st["median_ms"]
+    warm_ms = timer.warm(step, args.steps)
+    # dominant work alone (ordering + partition kernels), same protocol
+    rt = timer.time(step.partitions_only, args.roofline_launches)
+    part_ms = rt["median_ms"]
     alg = algorithmic_decode_bytes(w)
     achieved = alg / (part_ms * 1e-3) / 1e9
     step()  # leave `out` holding a full decode for the parity check below
@@ -566,13 +672,19 @@ def main():
             "head_dim": w.head_dim, "page_size": w.page_size, "index": w.index,
             "sum_ctx_tokens": int(w.context_lens.astype(np.int64).sum()),
             "kv_bytes_per_step": kv,
-            "kv_bytes_unique_pages": w.kv_bytes_unique() if w.name == "prefix" else kv,
+            "kv_bytes_unique_rows": w.kv_bytes_unique_rows(),
             "bytes_per_elem": b,
             "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
             "sequences_per_s_per_layer": round(w.num_seqs / (ms_per_step * 1e-3), 1),
-            "wall_s_timed_region": round(t_wall, 4),
             "step": ("fused decode step (store of the ctx-1 row inside the decode launch)"
                      if step.fused else "slot mapping + store + decode (separate launches)"),
+        },
+        "timing": {
+            "protocol": timer.protocol(),
+            "step_ms": {k: round(v, 5) for k, v in st.items() if k.endswith("_ms")},
+            "wall_s_timed_region": round(st["wall_s"], 4),
+            "warm_back_to_back_ms_per_step": round(warm_ms, 5),
+            "warm_back_to_back_GBs": round(kv / (warm_ms * 1e-3) / 1e9, 2),
         },
         "roofline": {
             "kernel": "decode_order_kernel + decode_partition[_mfma]_kernel (the partition pass)",
@@ -583,14 +695,17 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None if rec is None else rec.get("hbm_bytes_per_launch"),
             "algorithmic_bytes_per_launch": alg,
-            "mean_launch_ms": round(part_ms, 5),
+            "median_launch_ms": round(part_ms, 5),
+            "mean_launch_ms": round(rt["mean_ms"], 5),
             "launches": args.roofline_launches,
         },
     }
     if rec is not None:
         line["roofline"]["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)"
+    if not args.no_ceiling:
+        line["ceilings"] = ceilings(dev, timer, kv)
     if not args.no_cpu_baseline:
-        cb, parity = cpu_baseline(w, t, step.out)
+        cb, parity = cpu_baseline(w, t, step.out, args.cpu_seconds)
         line["cpu_baseline"] = cb
         line["parity_vs_oracle"] = parity
     print(json.dumps(line), flush=True)

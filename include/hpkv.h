@@ -493,6 +493,30 @@ int hpkv_bm_check(const hpkv_block_manager* bm);
 /* XXH64 of len bytes with the given seed (the page hash above). */
 uint64_t hpkv_xxh64(const void* data, uint64_t len, uint64_t seed);
 
+/* ---------------------------------------------------------------------------
+ * hpkv_read_ceiling  (device; measurement)
+ *
+ * Reads `bytes` of device memory in the access pattern of the decode gather
+ * and nothing else, to measure the HBM read ceiling the decode kernels are
+ * held against (decode attention reads every context row of K and V once:
+ * "Paged KV Cache · AI infra interview lesson", section "Step 2:
+ * paged_attention_decode"). The buffer is viewed as rows of stride_bytes,
+ * each split into stride_bytes / row_bytes columns of row_bytes; one
+ * workgroup reads one column of rows_per_workgroup consecutive rows, with
+ * 16-byte non-temporal loads as the decode kernels issue them. row_bytes ==
+ * stride_bytes is a plain streaming read; row_bytes 256 at stride 8192 is the
+ * (page row, KV head) pattern of a 32-KV-head, d = 128, bf16 pool. Only the
+ * first floor(bytes / stride_bytes) rows are read. sink (device, 4 bytes) is
+ * written only in the practically impossible case that a lane's data folds to
+ * one fixed word; its contents mean nothing.
+ * Requirements: buf 16-byte aligned; row_bytes a power of two in [16, 4096];
+ * stride_bytes a multiple of row_bytes; rows_per_workgroup >= 1
+ * (HPKV_ERR_INVALID_ARG otherwise; HPKV_ERR_NULL for NULL pointers).
+ * ------------------------------------------------------------------------- */
+int hpkv_read_ceiling(const void* buf, uint64_t bytes, uint32_t row_bytes,
+                      uint64_t stride_bytes, uint32_t rows_per_workgroup, uint32_t* sink,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

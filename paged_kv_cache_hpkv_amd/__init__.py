@@ -44,7 +44,7 @@ EXPORTED = [
     "hpkv_paged_attention_prefill", "hpkv_store_kvcache_quant",
     "hpkv_paged_attention_decode_quant", "hpkv_bm_create", "hpkv_bm_destroy", "hpkv_bm_admit",
     "hpkv_bm_append", "hpkv_bm_release", "hpkv_bm_stats", "hpkv_bm_export", "hpkv_bm_check",
-    "hpkv_xxh64",
+    "hpkv_xxh64", "hpkv_read_ceiling",
 ]
 
 
@@ -99,6 +99,7 @@ def _load():
         "hpkv_bm_export": ([vp, vp, u32, i32, vp, u64, vp, vp, vp], i32),
         "hpkv_bm_check": ([vp], i32),
         "hpkv_xxh64": ([vp, u64, u64], u64),
+        "hpkv_read_ceiling": ([vp, u64, u32, u64, u32, vp, vp], i32),
         "hpkv_paged_attention_prefill": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, vp, u32, u64,
                                           u32, u32, u32, u32, u64, f32, u32, vp, vp], i32),
     }
@@ -417,3 +418,14 @@ def alloc_workspace(q, k_cache, max_context_len):
     n = hpkv_paged_attention_decode_workspace_size(q.dtype, B, hq, d, k_cache.shape[1],
                                                    max_context_len)
     return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def hpkv_read_ceiling(buf, row_bytes, stride_bytes, rows_per_workgroup, sink, stream=None):
+    """Reads the device buffer `buf` in rows of row_bytes at stride_bytes (one column per
+    workgroup), the HBM read-ceiling measurement; `sink` is a 4-byte device tensor."""
+    _contig(buf, sink)
+    assert buf.is_cuda and sink.is_cuda and sink.numel() * sink.element_size() >= 4
+    nbytes = buf.numel() * buf.element_size()
+    _check("hpkv_read_ceiling", lib.hpkv_read_ceiling(
+        _ptr(buf), nbytes, int(row_bytes), int(stride_bytes), int(rows_per_workgroup), _ptr(sink),
+        _stream(stream, buf)))

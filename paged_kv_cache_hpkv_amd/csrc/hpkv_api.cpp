@@ -577,4 +577,18 @@ int hpkv_paged_attention_decode_quant(int dtype, int kv_type, int index_type, co
   return hip_status(e);
 }
 
+int hpkv_read_ceiling(const void* buf, uint64_t bytes, uint32_t row_bytes,
+                      uint64_t stride_bytes, uint32_t rows_per_workgroup, uint32_t* sink,
+                      void* stream) {
+  if (!buf || !sink) return HPKV_ERR_NULL;
+  if (row_bytes < 16 || row_bytes > 4096 || (row_bytes & (row_bytes - 1)) != 0)
+    return HPKV_ERR_INVALID_ARG;
+  if (stride_bytes < row_bytes || stride_bytes % row_bytes != 0) return HPKV_ERR_INVALID_ARG;
+  if (rows_per_workgroup == 0) return HPKV_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return HPKV_ERR_INVALID_ARG;
+  return hip_status(hpkv::launch_read_ceiling(buf, bytes, row_bytes, stride_bytes,
+                                              rows_per_workgroup, sink,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -156,6 +156,10 @@ hipError_t launch_store_quant(int dtype, int kv_type, const void* key, const voi
                               uint64_t num_pages, uint32_t num_kv_heads, uint32_t head_dim,
                               hipStream_t stream);
 
+hipError_t launch_read_ceiling(const void* buf, uint64_t bytes, uint32_t row_bytes,
+                               uint64_t stride, uint32_t rows_per_wg, uint32_t* sink,
+                               hipStream_t stream);
+
 hipError_t launch_slot_mapping(bool idx64, const void* block_table, uint64_t block_table_len,
                                const void* seq_ptr, uint32_t num_seqs, uint32_t page_size,
                                uint64_t num_pages, const int32_t* start_pos, const int64_t* cu_new, uint64_t num_new,

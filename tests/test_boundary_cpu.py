@@ -30,7 +30,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared()
-    assert len(declared) == 24
+    assert len(declared) == 25
     out = subprocess.run(["nm", "-D", "--defined-only", hpkv.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(hpkv_\w+)", out))
@@ -265,3 +265,14 @@ def test_store_and_slot_mapping_argument_errors():
         hpkv.ERR_INVALID_ARG
     assert sm(hpkv.INDEX_U32, FAKE, 4, None, 2, 16, 8, FAKE, FAKE, 4, FAKE, None) == hpkv.ERR_NULL
     assert sm(hpkv.INDEX_U32, None, 0, None, 0, 16, 8, None, None, 0, None, None) == hpkv.OK
+
+
+def test_read_ceiling_argument_errors():
+    rc = hpkv.lib.hpkv_read_ceiling
+    assert rc(None, 1 << 20, 256, 8192, 512, FAKE, None) == hpkv.ERR_NULL
+    assert rc(FAKE, 1 << 20, 256, 8192, 512, None, None) == hpkv.ERR_NULL
+    for row, stride, rows in ((8, 8192, 512), (192, 8192, 512), (8192, 8192, 64),
+                              (256, 8000, 512), (256, 128, 512), (256, 8192, 0)):
+        assert rc(FAKE, 1 << 20, row, stride, rows, FAKE, None) == hpkv.ERR_INVALID_ARG
+    assert rc(ctypes.c_void_p(0x1008), 1 << 20, 256, 8192, 512, FAKE, None) == \
+        hpkv.ERR_INVALID_ARG

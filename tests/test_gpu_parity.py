@@ -308,3 +308,16 @@ def test_fused_decode_step_matches_oracle(make):
     decodes to zeros with slot -1."""
     r = check_fused_step(make(), device="cuda")
     print(f"fused max err {r['max_err']:.2e}")
+
+
+def test_read_ceiling_runs_and_leaves_the_buffer_untouched():
+    """hpkv_read_ceiling reads in the decode's row pattern and writes nothing but (at most)
+    its 4-byte sink."""
+    buf = torch.randint(0, 255, (64 << 20,), dtype=torch.uint8, device="cuda")
+    before = buf.clone()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for row, stride, rows in ((4096, 4096, 64), (256, 8192, 512), (256, 2048, 512),
+                              (16, 16, 7)):
+        hpkv.hpkv_read_ceiling(buf, row, stride, rows, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)

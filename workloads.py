@@ -94,6 +94,19 @@ class Workload:
             used.update(self.block_table[sp[s]:sp[s] + n_pages].tolist())
         return len(used) * self.page_size * 2 * self.num_kv_heads * self.head_dim * b
 
+    def kv_bytes_unique_rows(self) -> int:
+        """K+V bytes of the distinct pool rows a decode pass reads (rows t < ctx of every
+        sequence's pages; a row shared by aliased pages counted once)."""
+        b = torch.tensor([], dtype=self.torch_dtype).element_size()
+        rows = {}
+        sp = self.seq_ptr.astype(np.int64)
+        for s in range(self.num_seqs):
+            n = int(self.context_lens[s])
+            for k in range(-(-n // self.page_size)):
+                page = int(self.block_table[sp[s] + k])
+                rows[page] = max(rows.get(page, 0), min(self.page_size, n - k * self.page_size))
+        return sum(rows.values()) * 2 * self.num_kv_heads * self.head_dim * b
+
     def with_dtype(self, dtype: str) -> "Workload":
         w = Workload(**{**self.__dict__})
         w.dtype = dtype
