@@ -53,7 +53,8 @@ typedef enum {
   HPKV_ERR_INVALID_INDEX = -3, /* index buffer contents break an invariant (host checks) */
   HPKV_ERR_UNSUPPORTED = -4,   /* valid but not implemented (e.g. head_dim shape) */
   HPKV_ERR_HIP = -5,           /* the HIP runtime reported an error at launch */
-  HPKV_ERR_WORKSPACE = -6      /* workspace missing or too small */
+  HPKV_ERR_WORKSPACE = -6,     /* workspace missing or too small */
+  HPKV_ERR_SCRATCH_LIMIT = -7  /* needs more scratch than the no-allocation decode holds */
 } hpkv_status;
 
 /* Element type of block_table and seq_ptr ("Block-Paged KV Cache", section
@@ -249,6 +250,33 @@ int hpkv_paged_attention_decode(int dtype, int index_type, const void* q, const 
                                 uint32_t page_size, uint64_t num_pages, float scale,
                                 uint32_t max_context_len, void* workspace, size_t workspace_bytes,
                                 void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * hpkv_paged_attention_decode_noalloc  (device)
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * hpkv_paged_attention_decode, same kernels and results, without the
+ * workspace arguments. The workspace is a fixed array inside the library,
+ * hpkv_paged_attention_decode_noalloc_max_workspace() bytes (128 MiB) per GPU,
+ * held by each GPU the library runs on until the process ends; its device
+ * address is looked up on the first call on each device. The call allocates
+ * nothing. A batch whose hpkv_paged_attention_decode_workspace_size exceeds
+ * that maximum returns HPKV_ERR_SCRATCH_LIMIT before any GPU work. Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (concurrent streams, or threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe. Every other argument,
+ * requirement and error is that of hpkv_paged_attention_decode.
+ * ------------------------------------------------------------------------- */
+size_t hpkv_paged_attention_decode_noalloc_max_workspace(void);
+int hpkv_paged_attention_decode_noalloc(int dtype, int index_type, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const void* block_table, uint64_t block_table_len,
+                                        const void* seq_ptr, const int32_t* context_lens,
+                                        uint32_t num_seqs, uint32_t num_q_heads,
+                                        uint32_t num_kv_heads, uint32_t head_dim,
+                                        uint32_t page_size, uint64_t num_pages, float scale,
+                                        uint32_t max_context_len, void* out, void* stream);
 
 /* The two passes of hpkv_paged_attention_decode, separately: the partition
  * pass (the ordering kernel, then the partition kernel, which writes `out` for

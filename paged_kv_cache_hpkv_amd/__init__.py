@@ -27,6 +27,7 @@ ERR_INVALID_INDEX = -3
 ERR_UNSUPPORTED = -4
 ERR_HIP = -5
 ERR_WORKSPACE = -6
+ERR_SCRATCH_LIMIT = -7
 
 F32, F16, BF16 = 0, 1, 2
 KV_I8, KV_FP8_E4M3 = 3, 4
@@ -44,7 +45,8 @@ EXPORTED = [
     "hpkv_paged_attention_prefill", "hpkv_store_kvcache_quant",
     "hpkv_paged_attention_decode_quant", "hpkv_bm_create", "hpkv_bm_destroy", "hpkv_bm_admit",
     "hpkv_bm_append", "hpkv_bm_release", "hpkv_bm_stats", "hpkv_bm_export", "hpkv_bm_check",
-    "hpkv_xxh64", "hpkv_read_ceiling",
+    "hpkv_xxh64", "hpkv_read_ceiling", "hpkv_paged_attention_decode_noalloc",
+    "hpkv_paged_attention_decode_noalloc_max_workspace",
 ]
 
 
@@ -100,6 +102,9 @@ def _load():
         "hpkv_bm_check": ([vp], i32),
         "hpkv_xxh64": ([vp, u64, u64], u64),
         "hpkv_read_ceiling": ([vp, u64, u32, u64, u32, vp, vp], i32),
+        "hpkv_paged_attention_decode_noalloc": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, u32, u32,
+                                                 u32, u32, u32, u64, f32, u32, vp, vp], i32),
+        "hpkv_paged_attention_decode_noalloc_max_workspace": ([], sz),
         "hpkv_paged_attention_prefill": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, vp, u32, u64,
                                           u32, u32, u32, u32, u64, f32, u32, vp, vp], i32),
     }
@@ -249,6 +254,19 @@ def hpkv_paged_attention_decode(q, k_cache, v_cache, block_table, seq_ptr, conte
                         max_context_len, workspace, out)
     _check("hpkv_paged_attention_decode",
            lib.hpkv_paged_attention_decode(*args, _stream(stream, q)))
+
+
+def hpkv_paged_attention_decode_noalloc(q, k_cache, v_cache, block_table, seq_ptr, context_lens,
+                                        scale, max_context_len, out, stream=None):
+    """hpkv_paged_attention_decode with the library's own fixed device scratch as workspace:
+    allocates nothing (batches needing more than the scratch raise ERR_SCRATCH_LIMIT)."""
+    args = _decode_args(q, k_cache, v_cache, block_table, seq_ptr, context_lens, scale,
+                        max_context_len, None, out)
+    (dt, it, qp, kp, vp_, btp, bt_len, spp, ctxp, B, hq, hkv, d, bs, num_pages, sc, mcl, _, _,
+     outp) = args
+    _check("hpkv_paged_attention_decode_noalloc", lib.hpkv_paged_attention_decode_noalloc(
+        dt, it, qp, kp, vp_, btp, bt_len, spp, ctxp, B, hq, hkv, d, bs, num_pages, sc, mcl, outp,
+        _stream(stream, q)))
 
 
 def hpkv_paged_attention_decode_partitions(q, k_cache, v_cache, block_table, seq_ptr,

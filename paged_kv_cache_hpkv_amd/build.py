@@ -38,6 +38,7 @@ UNITS = [("hpkv_api", "hpkv_api.cpp", []),
          ("hpkv_decode_quant_bf16", "hpkv_decode.hip", ["-DHPKV_DECODE_PART=6"]),
          ("hpkv_prefill", "hpkv_prefill.hip", []),
          ("hpkv_ceiling", "hpkv_ceiling.hip", []),
+         ("hpkv_noalloc", "hpkv_noalloc.hip", []),
          ("hpkv_blocks", "hpkv_blocks.cpp", [])]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -223,6 +223,15 @@ ReduceKernelArgs reduce_args(const DecodeKernelArgs& a, uint32_t head_dim) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? HPKV_OK : HPKV_ERR_HIP; }
 
+// The partition pass, then the reduce when some sequence spans several partitions.
+int launch_decode(int dtype, uint32_t head_dim, const DecodeKernelArgs& a, uint64_t nwg,
+                  hipStream_t s) {
+  hipError_t e = hpkv::launch_decode_partitions(dtype, head_dim, a, nwg, s);
+  if (e != hipSuccess) return HPKV_ERR_HIP;
+  if (a.max_parts > 1) e = hpkv::launch_decode_reduce(dtype, reduce_args(a, head_dim), s);
+  return hip_status(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -236,6 +245,8 @@ const char* hpkv_status_string(int status) {
     case HPKV_ERR_UNSUPPORTED: return "unsupported shape";
     case HPKV_ERR_HIP: return "HIP runtime error at launch";
     case HPKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case HPKV_ERR_SCRATCH_LIMIT:
+      return "batch needs more decode scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -419,11 +430,43 @@ int hpkv_paged_attention_decode(int dtype, int index_type, const void* q, const 
                                 num_kv_heads, head_dim, page_size, num_pages, scale,
                                 max_context_len, workspace, workspace_bytes, out, &a, &nwg);
   if (st <= 0) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hpkv::launch_decode_partitions(dtype, head_dim, a, nwg, s);
-  if (e != hipSuccess) return HPKV_ERR_HIP;
-  if (a.max_parts > 1) e = hpkv::launch_decode_reduce(dtype, reduce_args(a, head_dim), s);
-  return hip_status(e);
+  return launch_decode(dtype, head_dim, a, nwg, static_cast<hipStream_t>(stream));
+}
+
+size_t hpkv_paged_attention_decode_noalloc_max_workspace(void) {
+  return hpkv::kNoallocScratchBytes;
+}
+
+int hpkv_paged_attention_decode_noalloc(int dtype, int index_type, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const void* block_table, uint64_t block_table_len,
+                                        const void* seq_ptr, const int32_t* context_lens,
+                                        uint32_t num_seqs, uint32_t num_q_heads,
+                                        uint32_t num_kv_heads, uint32_t head_dim,
+                                        uint32_t page_size, uint64_t num_pages, float scale,
+                                        uint32_t max_context_len, void* out, void* stream) {
+  const size_t need = hpkv_paged_attention_decode_workspace_size(
+      dtype, num_seqs, num_q_heads, head_dim, page_size, max_context_len);
+  if (need > hpkv::kNoallocScratchBytes) return HPKV_ERR_SCRATCH_LIMIT;
+  // every argument check first, without a workspace: HPKV_ERR_WORKSPACE then
+  // only says that this batch needs one
+  DecodeKernelArgs a;
+  uint64_t nwg = 0;
+  int st = prepare_decode(dtype, index_type, q, k_cache, v_cache, block_table, block_table_len,
+                          seq_ptr, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                          page_size, num_pages, scale, max_context_len, nullptr, 0, out, &a,
+                          &nwg);
+  if (st != 1 && st != HPKV_ERR_WORKSPACE) return st;
+  void* scratch = nullptr;
+  if (hpkv::noalloc_scratch(&scratch) != hipSuccess) return HPKV_ERR_HIP;
+  if (st == HPKV_ERR_WORKSPACE) {
+    st = prepare_decode(dtype, index_type, q, k_cache, v_cache, block_table, block_table_len,
+                        seq_ptr, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        page_size, num_pages, scale, max_context_len, scratch,
+                        hpkv::kNoallocScratchBytes, out, &a, &nwg);
+    if (st <= 0) return st;
+  }
+  return launch_decode(dtype, head_dim, a, nwg, static_cast<hipStream_t>(stream));
 }
 
 int hpkv_paged_attention_decode_step(int dtype, int index_type, const void* q,

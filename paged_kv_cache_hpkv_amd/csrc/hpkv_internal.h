@@ -156,6 +156,11 @@ hipError_t launch_store_quant(int dtype, int kv_type, const void* key, const voi
                               uint64_t num_pages, uint32_t num_kv_heads, uint32_t head_dim,
                               hipStream_t stream);
 
+// Bytes of the fixed device scratch behind hpkv_paged_attention_decode_noalloc
+// (per GPU), and the current device's address of it (looked up on first use).
+constexpr size_t kNoallocScratchBytes = size_t(128) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_read_ceiling(const void* buf, uint64_t bytes, uint32_t row_bytes,
                                uint64_t stride, uint32_t rows_per_wg, uint32_t* sink,
                                hipStream_t stream);

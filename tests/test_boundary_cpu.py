@@ -30,7 +30,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared()
-    assert len(declared) == 25
+    assert len(declared) == 27
     out = subprocess.run(["nm", "-D", "--defined-only", hpkv.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(hpkv_\w+)", out))
@@ -276,3 +276,22 @@ def test_read_ceiling_argument_errors():
         assert rc(FAKE, 1 << 20, row, stride, rows, FAKE, None) == hpkv.ERR_INVALID_ARG
     assert rc(ctypes.c_void_p(0x1008), 1 << 20, 256, 8192, 512, FAKE, None) == \
         hpkv.ERR_INVALID_ARG
+
+
+def test_noalloc_decode_rejects_batches_beyond_its_scratch():
+    """The no-allocation decode refuses, before any GPU work, a batch whose workspace would
+    exceed its fixed scratch; argument errors are those of the workspace decode."""
+    cap = hpkv.lib.hpkv_paged_attention_decode_noalloc_max_workspace()
+    assert cap == 128 << 20
+    na = hpkv.lib.hpkv_paged_attention_decode_noalloc
+    ws = hpkv.lib.hpkv_paged_attention_decode_workspace_size
+    # 4096 sequences x 32 heads x 128-token contexts of 64k tokens: far more than 128 MiB
+    assert ws(hpkv.BF16, 4096, 32, 128, 16, 65536) > cap
+    assert na(hpkv.BF16, hpkv.INDEX_U32, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 4096, 32, 8,
+              128, 16, 1 << 20, 0.1, 65536, FAKE, None) == hpkv.ERR_SCRATCH_LIMIT
+    assert ws(hpkv.BF16, 64, 32, 128, 16, 4096) <= cap
+    assert na(hpkv.BF16, hpkv.INDEX_U32, None, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 64, 32, 8, 128,
+              16, 1 << 20, 0.1, 4096, FAKE, None) == hpkv.ERR_NULL
+    assert na(hpkv.BF16, hpkv.INDEX_U32, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 64, 32, 5, 128,
+              16, 1 << 20, 0.1, 4096, FAKE, None) == hpkv.ERR_INVALID_ARG
+    assert hpkv.status_string(hpkv.ERR_SCRATCH_LIMIT).startswith("batch needs more")
