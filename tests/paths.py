@@ -36,7 +36,8 @@ def used_slots(w: workloads.Workload) -> np.ndarray:
     B = w.num_seqs
     cu = np.zeros(B + 1, dtype=np.int64)
     cu[1:] = np.cumsum(w.context_lens.astype(np.int64))
-    return oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, w.num_pages, np.zeros(B, np.int32), cu)
+    return oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, w.num_pages,
+                               np.zeros(B, np.int32), cu)
 
 
 def poison_unused(w: workloads.Workload, t: workloads.Tensors):

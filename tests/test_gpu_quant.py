@@ -32,11 +32,12 @@ def _poison(w, qt, kv):
         sc[~pages] = float("nan")
 
 
-def _step(w, kv, max_context_len=None):
+def _step(w, kv, max_context_len=None, fp8_full_range=False):
     print(f"[quant parity] {w.name} {w.dtype} {kv} {w.index} B={w.num_seqs} Hq={w.num_q_heads} "
-          f"Hkv={w.num_kv_heads} d={w.head_dim} bs={w.page_size}", flush=True)
+          f"Hkv={w.num_kv_heads} d={w.head_dim} bs={w.page_size} full={fp8_full_range}",
+          flush=True)
     t = workloads.make_tensors(w, DEV)
-    qt = workloads.make_quant_tensors(w, kv, DEV)
+    qt = workloads.make_quant_tensors(w, kv, DEV, fp8_full_range=fp8_full_range)
     _poison(w, qt, kv)
     h = {name: getattr(qt, name).cpu().numpy().copy() for name in
          ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero")}
@@ -45,14 +46,16 @@ def _step(w, kv, max_context_len=None):
     ctx = torch.from_numpy(w.context_lens).to(DEV)
     for c, (start, cu) in enumerate(w.chunks):
         slots = torch.empty(int(cu[-1]), dtype=torch.int64, device=DEV)
-        hpkv.hpkv_slot_mapping(bt, sp, w.page_size, w.num_pages, torch.from_numpy(start).to(DEV),
-                               torch.from_numpy(cu).to(DEV), slots)
+        hpkv.hpkv_slot_mapping(bt, sp, w.page_size, w.num_pages,
+                               torch.from_numpy(start).to(DEV), torch.from_numpy(cu).to(DEV),
+                               slots)
         if w.drop_mask is not None and c == 0:
             slots[torch.from_numpy(w.drop_mask).to(DEV)] = -1
         hpkv.hpkv_store_kvcache_quant(kv, t.new_keys[c], t.new_values[c], qt.k_codes,
                                       qt.v_codes, qt.k_scale, qt.k_zero, qt.v_scale, qt.v_zero,
                                       slots)
-        o_slots = oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, w.num_pages, start, cu)
+        o_slots = oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, w.num_pages,
+                                      start, cu)
         if w.drop_mask is not None and c == 0:
             o_slots[w.drop_mask] = -1
         oracle.store_kvcache_quant(w.dtype, kv, host_bits(t.new_keys[c]),
@@ -75,7 +78,7 @@ def _step(w, kv, max_context_len=None):
     max_err, ratio, finite = decode_errors(w.dtype, host_bits(out), ref)
     assert finite, "non-finite decode output"
     assert ratio <= 1.0, f"decode error {max_err} above tolerance"
-    return out
+    return out, qt
 
 
 @pytest.mark.parametrize("kv", ["i8", "fp8"])
@@ -118,3 +121,25 @@ def test_quant_u64_and_single_partition():
     w.context_lens = np.minimum(w.context_lens, 400).astype(np.int32)
     w.chunks = workloads._decode_step_chunks(w.context_lens)
     _step(w, "i8", max_context_len=512)
+
+
+@pytest.mark.parametrize("case", ["tiny16_bf16", "llama7b_bf16", "gqa_bf16", "gqa_f16",
+                                  "qwen3_bf16", "tiny_f32"])
+def test_fp8_full_code_range(case):
+    """Every non-NaN E4M3 code (exponent fields 0-15, up to +-448) through the decode's
+    conversions, and a quantizing store that saturates at +-448 and meets rounding ties,
+    against the oracle byte for byte ("Block-Paged KV Cache", Quantization compatibility)."""
+    name, dtype = case.split("_")
+    if name.startswith("tiny"):
+        w = workloads.tiny(bs=16 if name == "tiny16" else 4, dtype=dtype)
+        w = workloads.Workload(**{**w.__dict__, "head_dim": 16, "scale": 16 ** -0.5})
+    else:
+        w = workloads.WORKLOADS[name](batch=12).with_dtype(dtype)
+    out, qt = _step(w, "fp8", fp8_full_range=True)
+    # the stored rows saturated somewhere (+-448 is code 0x7e / 0xfe)
+    slots = oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, w.num_pages,
+                                *w.chunks[0])
+    stored = qt.k_codes.view(w.num_pages * w.page_size, -1)[torch.from_numpy(slots).to(DEV)]
+    assert ((stored == 0x7E) | (stored == 0xFE)).any()
+    codes = qt.k_codes.cpu().numpy()
+    assert len(np.unique(codes)) >= 250  # the whole code range is in the pools

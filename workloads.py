@@ -304,21 +304,40 @@ class QuantTensors:
     v_zero: torch.Tensor
 
 
-def make_quant_tensors(w: Workload, kv_type: str, device="cpu") -> QuantTensors:
-    """Random codes for quantized pools (fp8: exponent field at most 7, i.e. magnitudes
-    below 2 and no NaN code) and per (page, KV head)
-    scales and zero points: int8 scales U(0.005, 0.02) with integer zero points in
-    [-8, 8], fp8 scales U(0.25, 1) with zero points U(-0.5, 0.5), so dequantized
-    values stay below ~2.7 in magnitude, the O(1) range of N(0,1) K/V data."""
+def make_quant_tensors(w: Workload, kv_type: str, device="cpu",
+                       fp8_full_range: bool = False) -> QuantTensors:
+    """Random codes for quantized pools and per (page, KV head) scales and zero points:
+    int8 scales U(0.005, 0.02) with integer zero points in [-8, 8], fp8 scales U(0.25, 1)
+    with zero points U(-0.5, 0.5) and codes whose exponent field is at most 7 (magnitudes
+    below 2, never a NaN code), so dequantized values stay below ~2.7 in magnitude, the
+    O(1) range of N(0,1) K/V data.
+
+    fp8_full_range: fp8 codes drawn from all 254 non-NaN codes (every exponent field,
+    magnitudes up to 448) with power-of-two scales 2^-8 or 2^-9 and zero points that are
+    integers in [-32, 32] on even pages and U(-32, 32) on odd ones, so values still
+    dequantize to O(1); new N(0,1) rows stored with such scales land far beyond +-448
+    (saturation) and, being 8-bit-mantissa numbers scaled by a power of two, often exactly
+    halfway between two codes (ties)."""
     g = torch.Generator(device="cpu")
     g.manual_seed(1000 * w.seed + 77)
     shape = (w.num_pages, w.page_size, w.num_kv_heads, w.head_dim)
     k = torch.randint(0, 256, shape, generator=g, dtype=torch.int32).to(torch.uint8)
     v = torch.randint(0, 256, shape, generator=g, dtype=torch.int32).to(torch.uint8)
+    ps = (w.num_pages, w.num_kv_heads)
+    if kv_type == "fp8" and fp8_full_range:
+        for c in (k, v):  # the two NaN codes become +-0
+            c[(c & 0x7F) == 0x7F] &= 0x80
+        ks = torch.exp2(-8.0 - torch.randint(0, 2, ps, generator=g).float())
+        vs = torch.exp2(-8.0 - torch.randint(0, 2, ps, generator=g).float())
+        kz = torch.randint(-32, 33, ps, generator=g).float()
+        vz = torch.randint(-32, 33, ps, generator=g).float()
+        odd = torch.arange(w.num_pages) % 2 == 1
+        kz[odd] = 64.0 * torch.rand((int(odd.sum()), w.num_kv_heads), generator=g) - 32.0
+        vz[odd] = 64.0 * torch.rand((int(odd.sum()), w.num_kv_heads), generator=g) - 32.0
+        return QuantTensors(*[x.contiguous().to(device) for x in (k, v, ks, kz, vs, vz)])
     if kv_type == "fp8":  # exponent field <= 7: magnitudes below 2, never a NaN code
         k &= 0xBF
         v &= 0xBF
-    ps = (w.num_pages, w.num_kv_heads)
     if kv_type == "i8":
         ks = 0.005 + 0.015 * torch.rand(ps, generator=g)
         vs = 0.005 + 0.015 * torch.rand(ps, generator=g)
