@@ -128,7 +128,9 @@ def test_quant_u64_and_single_partition():
 def test_fp8_full_code_range(case):
     """Every non-NaN E4M3 code (exponent fields 0-15, up to +-448) through the decode's
     conversions, and a quantizing store that saturates at +-448 and meets rounding ties,
-    against the oracle byte for byte ("Block-Paged KV Cache", Quantization compatibility)."""
+    against the oracle byte for byte ("Block-Paged KV Cache", Quantization compatibility).
+    The tiny cases store every context row themselves, so they cover the store's
+    saturation and ties; the decode-step cases keep random history codes."""
     name, dtype = case.split("_")
     if name.startswith("tiny"):
         w = workloads.tiny(bs=16 if name == "tiny16" else 4, dtype=dtype)
@@ -141,5 +143,7 @@ def test_fp8_full_code_range(case):
                                 *w.chunks[0])
     stored = qt.k_codes.view(w.num_pages * w.page_size, -1)[torch.from_numpy(slots).to(DEV)]
     assert ((stored == 0x7E) | (stored == 0xFE)).any()
-    codes = qt.k_codes.cpu().numpy()
-    assert len(np.unique(codes)) >= 250  # the whole code range is in the pools
+    if not name.startswith("tiny"):  # tiny rows are all written by the store itself
+        used = torch.from_numpy(used_slots(w)).to(DEV)
+        codes = qt.k_codes.view(w.num_pages * w.page_size, -1)[used].cpu().numpy()
+        assert len(np.unique(codes)) >= 250  # the decode read the whole code range
