@@ -361,6 +361,45 @@ class QuantStep:
         self.decode()
 
 
+def quant_cpu_baseline(w, t, qt, kv, out_gpu, seconds):
+    """The oracle on the quantized step (slot mapping, quantizing store, decode over the
+    codes), on host copies of the same inputs, repeated for about `seconds`."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle  # noqa: E402
+    from paths import decode_errors, host_bits, host_threads  # noqa: E402
+    h = {n: getattr(qt, n).cpu().numpy().copy() for n in
+         ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero")}
+    q = host_bits(t.q)
+    nk = [host_bits(x) for x in t.new_keys]
+    nv = [host_bits(x) for x in t.new_values]
+    threads = host_threads()
+    runs = []
+    t_start = time.perf_counter()
+    while not runs or (time.perf_counter() - t_start < seconds and len(runs) < 200):
+        t0 = time.perf_counter()
+        for c, (start, cu) in enumerate(w.chunks):
+            slots = oracle.slot_mapping(w.block_table, w.seq_ptr, w.page_size, w.num_pages,
+                                        start, cu)
+            if w.drop_mask is not None and c == 0:
+                slots[w.drop_mask] = -1
+            oracle.store_kvcache_quant(w.dtype, kv, nk[c], nv[c], h["k_codes"], h["v_codes"],
+                                       h["k_scale"], h["k_zero"], h["v_scale"], h["v_zero"],
+                                       slots)
+        _, ref = oracle.paged_attention_decode_quant(
+            w.dtype, kv, q, h["k_codes"], h["v_codes"], h["k_scale"], h["k_zero"], h["v_scale"],
+            h["v_zero"], w.block_table, w.seq_ptr, w.context_lens, w.scale, threads)
+        runs.append(time.perf_counter() - t0)
+    dt = float(np.median(runs))
+    max_err, ratio, finite = decode_errors(w.dtype, host_bits(out_gpu), ref)
+    return dict(value=round(quant_kv_bytes(w) / dt / 1e9, 4), unit="GB/s", cores=threads,
+                kind="oracle",
+                sample=f"the full timed step (slot mapping, quantizing store, decode of all "
+                       f"{w.num_seqs} sequences over {kv} codes), double precision, {threads} "
+                       f"host threads, repeated {len(runs)} times in {sum(runs):.1f} s, median "
+                       f"{dt:.3f} s per step ({host_description()})"), \
+        dict(max_abs_err=max_err, within_tolerance=ratio <= 1.0 and finite)
+
+
 def quant_kv_bytes(w):
     """K+V bytes of one-byte codes a decode pass must read: sum(ctx) * 2 * Hkv * d."""
     return int(w.context_lens.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim
@@ -442,6 +481,12 @@ def main_quant(args, dev):
             "launches": args.roofline_launches,
         },
     }
+    if not args.no_cpu_baseline:
+        step()  # leave `out` holding a full decode for the parity check
+        torch.cuda.synchronize()
+        cb, parity = quant_cpu_baseline(w, t, qt, args.kv, step.out, args.cpu_seconds)
+        line["cpu_baseline"] = cb
+        line["parity_vs_oracle"] = parity
     print(json.dumps(line), flush=True)
 
 
@@ -493,31 +538,35 @@ class PrefillStep:
             self.attention(c)
 
 
-def prefill_cpu_baseline(w, t, step, rows_per_chunk=8):
+def prefill_cpu_baseline(w, t, step, seconds, rows_per_chunk=8):
     """The oracle's prefill on sampled query rows of every chunk, on host copies of the
     pools after the step (a row at position p only reads keys 0..p, which hold the same
-    bits at any point after their chunk was stored)."""
+    bits at any point after their chunk was stored); rounds of rows_per_chunk random rows
+    per chunk are added until about `seconds` of oracle time."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from paths import decode_errors, host_bits, oracle_prefill_rows  # noqa: E402
     h = dict(k_cache=host_bits(t.k_cache), v_cache=host_bits(t.v_cache))
+    q_bits = [host_bits(q) for q in step.q]
+    outs = [host_bits(o) for o in step.out]
     rng = np.random.default_rng(0)
-    flops, secs, worst, ok = 0, 0.0, 0.0, True
-    for c, (start, cu) in enumerate(w.chunks):
-        rows = np.sort(rng.choice(int(cu[-1]), rows_per_chunk, replace=False))
-        q_bits = host_bits(step.q[c])
-        seq_of = np.searchsorted(cu, rows, side="right") - 1
-        pos = start[seq_of].astype(np.int64) + rows - cu[seq_of]
-        t0 = time.perf_counter()
-        ref = oracle_prefill_rows(w, h, q_bits, start, cu, rows)
-        secs += time.perf_counter() - t0
-        flops += 4 * w.head_dim * w.num_q_heads * int((pos + 1).sum())
-        err, ratio, finite = decode_errors(w.dtype, host_bits(step.out[c])[rows], ref)
-        worst = max(worst, err)
-        ok = ok and finite and ratio <= 1.0
+    flops, secs, worst, ok, nrows = 0, 0.0, 0.0, True, 0
+    while nrows == 0 or (secs < seconds and nrows < 4096):
+        for c, (start, cu) in enumerate(w.chunks):
+            rows = np.sort(rng.choice(int(cu[-1]), rows_per_chunk, replace=False))
+            seq_of = np.searchsorted(cu, rows, side="right") - 1
+            pos = start[seq_of].astype(np.int64) + rows - cu[seq_of]
+            t0 = time.perf_counter()
+            ref = oracle_prefill_rows(w, h, q_bits[c], start, cu, rows)
+            secs += time.perf_counter() - t0
+            flops += 4 * w.head_dim * w.num_q_heads * int((pos + 1).sum())
+            nrows += len(rows)
+            err, ratio, finite = decode_errors(w.dtype, outs[c][rows], ref)
+            worst = max(worst, err)
+            ok = ok and finite and ratio <= 1.0
     return dict(value=round(flops / secs / 1e12, 6), unit="TFLOP/s", cores=1, kind="oracle",
-                sample=f"{rows_per_chunk} random query rows (all heads) of each of the "
-                       f"{len(w.chunks)} chunks, double precision, 1 host thread, "
-                       f"{secs:.2f} s"), \
+                sample=f"{nrows} random query rows (all heads; {rows_per_chunk} per chunk per "
+                       f"round over the {len(w.chunks)} chunks), double precision, 1 host "
+                       f"thread, {secs:.2f} s ({host_description()})"), \
         dict(max_abs_err=worst, within_tolerance=ok)
 
 
@@ -594,7 +643,7 @@ def main_prefill(args, dev):
     if args.copy_calibration:
         calibration_copy(dev)
     if not args.no_cpu_baseline:
-        cb, parity = prefill_cpu_baseline(w, t, step)
+        cb, parity = prefill_cpu_baseline(w, t, step, args.cpu_seconds)
         line["cpu_baseline"] = cb
         line["parity_vs_oracle"] = parity
     print(json.dumps(line), flush=True)
