@@ -155,10 +155,15 @@ struct Partition {
 };
 
 // One work item: sequence, partition, KV head g and the first query head h0
-// of the tile it serves.
+// of the tile it serves. s == kNoWork: the item does nothing.
 struct WorkItem {
   uint32_t s, part, g, h0;
 };
+
+// Order-list entry (and WorkItem::s) of a pair with nothing to do: a partition
+// past its sequence's context, or not the first partition of a malformed
+// length. Such workgroups exit before reading anything else.
+constexpr uint32_t kNoWork = 0xffffffffu;
 
 // Grid order: head tile fastest, then the (sequence, partition) pair. A head
 // tile is GT query heads of one KV head, or the whole groups of kv_per_wg
@@ -195,8 +200,15 @@ __device__ inline WorkItem grid_item(const DecodeKernelArgs& a) {
   }
   const uint32_t ht = bid % a.head_tiles;
   bid /= a.head_tiles;  // (sequence, partition) pair, partition-major
-  if (a.order != nullptr) bid = a.order[bid];
   WorkItem it;
+  if (a.order != nullptr) {
+    bid = a.order[bid];
+    if (bid == kNoWork) {
+      it.s = kNoWork;
+      it.part = it.g = it.h0 = 0;
+      return it;
+    }
+  }
   it.s = bid % a.num_seqs;
   it.part = bid / a.num_seqs;
   const uint32_t tiles_per_group = a.group / GT;  // 1 when kv_per_wg > 1
@@ -299,7 +311,9 @@ __global__ __launch_bounds__(kOrderWaves * kWave) void decode_order_kernel(
       if (c == k) pos = base[k] + uint32_t(__popcll(m & below));
       base[k] += uint32_t(__popcll(m));
     }
-    if (pos < n) a.order[pos] = j;
+    // pairs past a context (or after the first of a malformed length) do nothing:
+    // their workgroups need not even read the length
+    if (pos < n) a.order[pos] = c == kOrderClasses - 1 && j >= a.num_seqs ? kNoWork : j;
   }
 }
 
@@ -326,6 +340,7 @@ template <int DT, int D, int NH, int NTH, class Hook = NoTokenHook, int NKV = 1,
 __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem& it,
                                        uint64_t (&s_row)[CAP], Partition& w,
                                        Hook on_token = Hook{}) {
+  if (it.s == kNoWork) return false;
   const uint32_t tid = threadIdx.x;
   w.s = it.s;
   w.part = it.part;

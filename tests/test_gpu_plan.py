@@ -106,13 +106,17 @@ def test_quant_decode_plan_shapes(name, ctx, hq, hkv, kv):
 def _expected_order(ctx, num_seqs, max_parts, part, max_ctx):
     """The dispatch order the ordering pass must write: pairs j = s + B * p stably
     sorted by length class (full partitions, 16 bands of partial ones from long to
-    short, then empty or malformed pairs)."""
+    short, then empty or malformed pairs), with the pairs that have nothing to do
+    (empty or malformed, partition 1 or later) written as 0xFFFFFFFF."""
     j = np.arange(num_seqs * max_parts, dtype=np.int64)
     n = np.asarray(ctx, dtype=np.int64)[j % num_seqs]
     p0 = (j // num_seqs) * part
     ln = np.clip(n - p0, 0, part)
     cls = np.where((n <= 0) | (n > max_ctx) | (n <= p0), 16, (part - ln) * 16 // part)
-    return np.argsort(cls, kind="stable").astype(np.uint32)
+    order = np.argsort(cls, kind="stable")
+    # pairs with nothing to do (empty class, not a first partition) are marked 0xFFFFFFFF
+    no_work = (cls[order] == 16) & (order >= num_seqs)
+    return np.where(no_work, 0xFFFFFFFF, order).astype(np.uint32)
 
 
 def _pad256(b):
