@@ -93,6 +93,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--unfused", action="store_true",
                    help="run slot mapping, store and decode as separate calls")
+    p.add_argument("--shared", action="store_true",
+                   help="decode with hpkv_paged_attention_decode_shared (a full partition that "
+                        "consecutive sequences alias is read once for all of them); the "
+                        "roofline then times that whole call")
     p.add_argument("--kv", default=None, choices=["i8", "fp8"],
                    help="decode over quantized pools (per page-slot, per KV head scales)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -217,10 +221,11 @@ class Step:
     hpkv_paged_attention_decode.
     """
 
-    def __init__(self, w, t, fused):
+    def __init__(self, w, t, fused, shared=False):
         import paged_kv_cache_hpkv_amd as hpkv
         self.hpkv, self.w, self.t = hpkv, w, t
-        self.fused = fused
+        self.fused = fused and not shared
+        self.shared = shared
         dev = t.q.device
         self.bt = torch.from_numpy(w.block_table).to(dev)
         self.sp = torch.from_numpy(w.seq_ptr).to(dev)
@@ -245,11 +250,18 @@ class Step:
             if self.drop is not None and c == 0:
                 slots.masked_fill_(self.drop, -1)
             h.hpkv_store_kvcache(t.new_keys[c], t.new_values[c], t.k_cache, t.v_cache, slots)
-        h.hpkv_paged_attention_decode(t.q, t.k_cache, t.v_cache, self.bt, self.sp, self.ctx,
-                                      w.scale, w.max_context_len, self.ws, self.out)
+        decode = (h.hpkv_paged_attention_decode_shared if self.shared
+                  else h.hpkv_paged_attention_decode)
+        decode(t.q, t.k_cache, t.v_cache, self.bt, self.sp, self.ctx, w.scale,
+               w.max_context_len, self.ws, self.out)
 
     def partitions_only(self):
         w, t = self.w, self.t
+        if self.shared:  # the detection, ordering, partition and reduce kernels
+            self.hpkv.hpkv_paged_attention_decode_shared(
+                t.q, t.k_cache, t.v_cache, self.bt, self.sp, self.ctx, w.scale,
+                w.max_context_len, self.ws, self.out)
+            return
         self.hpkv.hpkv_paged_attention_decode_partitions(
             t.q, t.k_cache, t.v_cache, self.bt, self.sp, self.ctx, w.scale, w.max_context_len,
             self.ws, self.out)
@@ -677,7 +689,7 @@ def main():
         print(json.dumps(line), flush=True)
         return
     t = workloads.make_tensors(w, dev)
-    step = Step(w, t, fused=is_decode_step(w) and not args.unfused)
+    step = Step(w, t, fused=is_decode_step(w) and not args.unfused, shared=args.shared)
 
     if args.copy_calibration:
         calibration_copy(dev)
@@ -726,7 +738,8 @@ def main():
             "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
             "sequences_per_s_per_layer": round(w.num_seqs / (ms_per_step * 1e-3), 1),
             "step": ("fused decode step (store of the ctx-1 row inside the decode launch)"
-                     if step.fused else "slot mapping + store + decode (separate launches)"),
+                     if step.fused else "slot mapping + store + decode (separate launches)")
+                    + (", decode by hpkv_paged_attention_decode_shared" if step.shared else ""),
         },
         "timing": {
             "protocol": timer.protocol(),
@@ -736,7 +749,10 @@ def main():
             "warm_back_to_back_GBs": round(kv / (warm_ms * 1e-3) / 1e9, 2),
         },
         "roofline": {
-            "kernel": "decode_order_kernel + decode_partition[_mfma]_kernel (the partition pass)",
+            "kernel": ("decode_share_kernel + decode_order_kernel + decode_partition_mfma_kernel"
+                       " + decode_reduce_kernel (the whole shared decode call)" if step.shared
+                       else "decode_order_kernel + decode_partition[_mfma]_kernel "
+                            "(the partition pass)"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

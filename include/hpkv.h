@@ -172,7 +172,8 @@ int hpkv_store_kvcache(int dtype, const void* key, const void* value, void* k_ca
  * num_seqs sequences no longer than max_context_len tokens: the split-context
  * partials (one fp32 (max, sum) pair and one fp32 head_dim vector per
  * sequence, query head and context partition), then the dispatch order of the
- * (sequence, partition) pairs (one uint32 each), counted with the smallest
+ * (sequence, partition) pairs (one uint32 each) and one byte per pair for
+ * hpkv_paged_attention_decode_shared, counted with the smallest
  * partition the library uses, so it is enough for every num_kv_heads and for
  * the quantized decode. 0 when every sequence fits one partition (no
  * workspace is then read or written) and on invalid arguments.
@@ -277,6 +278,35 @@ int hpkv_paged_attention_decode_noalloc(int dtype, int index_type, const void* q
                                         uint32_t num_kv_heads, uint32_t head_dim,
                                         uint32_t page_size, uint64_t num_pages, float scale,
                                         uint32_t max_context_len, void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * hpkv_paged_attention_decode_shared  (device)
+ *
+ * hpkv_paged_attention_decode for batches whose sequences alias pages, as
+ * shared prefixes do ("Block-Paged KV Cache", "Element lookup through the
+ * block table": aliased tables resolve to the same offsets; "Paged KV Cache ·
+ * AI infra interview lesson", "Step 5": prefix pages shared by reference).
+ * Same arguments, requirements, errors and results, bit for bit: every output
+ * equals what hpkv_paged_attention_decode gives on the same inputs with every
+ * aliased page replaced by a private copy. The difference is the work: on the
+ * matrix-core path (bf16/f16, head_dim in {32, 64, 128}, num_q_heads /
+ * num_kv_heads a multiple of 4 and at most 8 per tile) a detection pass
+ * compares the block tables, and a context partition that is full and covers
+ * the same page ids for consecutive sequences of an aligned block of
+ * 16 / (query heads per tile) sequences is read once, by one workgroup, for
+ * all of them. Elsewhere, and for batches that fit one partition per
+ * sequence, it behaves as hpkv_paged_attention_decode. The detection pass and
+ * the ordering pass run even when nothing is shared (a few microseconds).
+ * ------------------------------------------------------------------------- */
+int hpkv_paged_attention_decode_shared(int dtype, int index_type, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const void* block_table, uint64_t block_table_len,
+                                       const void* seq_ptr, const int32_t* context_lens,
+                                       uint32_t num_seqs, uint32_t num_q_heads,
+                                       uint32_t num_kv_heads, uint32_t head_dim,
+                                       uint32_t page_size, uint64_t num_pages, float scale,
+                                       uint32_t max_context_len, void* workspace,
+                                       size_t workspace_bytes, void* out, void* stream);
 
 /* The two passes of hpkv_paged_attention_decode, separately: the partition
  * pass (the ordering kernel, then the partition kernel, which writes `out` for

@@ -46,6 +46,7 @@ EXPORTED = [
     "hpkv_paged_attention_decode_quant", "hpkv_bm_create", "hpkv_bm_destroy", "hpkv_bm_admit",
     "hpkv_bm_append", "hpkv_bm_release", "hpkv_bm_stats", "hpkv_bm_export", "hpkv_bm_check",
     "hpkv_xxh64", "hpkv_read_ceiling", "hpkv_paged_attention_decode_noalloc",
+    "hpkv_paged_attention_decode_shared",
     "hpkv_paged_attention_decode_noalloc_max_workspace",
 ]
 
@@ -79,6 +80,9 @@ def _load():
                                                          u32),
         "hpkv_paged_attention_decode": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, u32, u32, u32,
                                          u32, u32, u64, f32, u32, vp, sz, vp, vp], i32),
+        "hpkv_paged_attention_decode_shared": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, u32, u32,
+                                                u32, u32, u32, u64, f32, u32, vp, sz, vp, vp],
+                                               i32),
         "hpkv_paged_attention_decode_partitions": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, u32,
                                                     u32, u32, u32, u32, u64, f32, u32, vp, sz,
                                                     vp, vp], i32),
@@ -254,6 +258,16 @@ def hpkv_paged_attention_decode(q, k_cache, v_cache, block_table, seq_ptr, conte
                         max_context_len, workspace, out)
     _check("hpkv_paged_attention_decode",
            lib.hpkv_paged_attention_decode(*args, _stream(stream, q)))
+
+
+def hpkv_paged_attention_decode_shared(q, k_cache, v_cache, block_table, seq_ptr, context_lens,
+                                       scale, max_context_len, workspace, out, stream=None):
+    """hpkv_paged_attention_decode for batches that alias pages: full partitions that
+    consecutive sequences share are read once for all of them (same results)."""
+    args = _decode_args(q, k_cache, v_cache, block_table, seq_ptr, context_lens, scale,
+                        max_context_len, workspace, out)
+    _check("hpkv_paged_attention_decode_shared",
+           lib.hpkv_paged_attention_decode_shared(*args, _stream(stream, q)))
 
 
 def hpkv_paged_attention_decode_noalloc(q, k_cache, v_cache, block_table, seq_ptr, context_lens,

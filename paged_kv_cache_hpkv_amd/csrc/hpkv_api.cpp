@@ -106,21 +106,23 @@ DecodePlan plan_decode(int dtype, bool quant, uint32_t num_seqs, uint32_t num_q_
 }
 
 struct WorkspaceLayout {
-  size_t ml_offset, o_offset, order_offset, bytes;
+  size_t ml_offset, o_offset, order_offset, flags_offset, bytes;
 };
 
 WorkspaceLayout workspace_layout(uint32_t num_seqs, uint32_t num_q_heads, uint32_t head_dim,
                                  uint32_t max_context_len, uint32_t part_tokens) {
   const uint64_t mp = max_parts_for(max_context_len, part_tokens);
-  WorkspaceLayout w{0, 0, 0, 0};
+  WorkspaceLayout w{0, 0, 0, 0, 0};
   if (mp <= 1) return w;  // every sequence fits one partition: no partials
   const uint64_t rows = uint64_t(num_seqs) * num_q_heads * mp;
   const uint64_t ml_bytes = (rows * sizeof(float2) + 255) & ~uint64_t(255);
   const uint64_t o_bytes = (rows * head_dim * sizeof(float) + 255) & ~uint64_t(255);
+  const uint64_t order_bytes = (uint64_t(num_seqs) * mp * sizeof(uint32_t) + 255) & ~uint64_t(255);
   w.ml_offset = 0;
   w.o_offset = ml_bytes;
-  w.order_offset = ml_bytes + o_bytes;  // then one u32 per (sequence, partition)
-  w.bytes = w.order_offset + uint64_t(num_seqs) * mp * sizeof(uint32_t);
+  w.order_offset = ml_bytes + o_bytes;          // one u32 per (sequence, partition)
+  w.flags_offset = w.order_offset + order_bytes;  // then one byte per pair (shared runs)
+  w.bytes = w.flags_offset + uint64_t(num_seqs) * mp;
   return w;
 }
 
@@ -131,7 +133,7 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
                    uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
                    uint32_t page_size, uint64_t num_pages, float scale, uint32_t max_context_len,
                    void* workspace, size_t workspace_bytes, void* out, DecodeKernelArgs* a,
-                   uint64_t* num_workgroups, int kv_type = -1) {
+                   uint64_t* num_workgroups, int kv_type = -1, bool share = false) {
   if (!valid_dtype(dtype) || !valid_index(index_type)) return HPKV_ERR_INVALID_ARG;
   const bool quant = kv_type >= 0;
   if (quant && kv_type != HPKV_KV_I8 && kv_type != HPKV_KV_FP8_E4M3) return HPKV_ERR_INVALID_ARG;
@@ -199,7 +201,17 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
   a->k_scale = a->k_zero = a->v_scale = a->v_zero = nullptr;
   // Longest-first dispatch pays when the grid is deeper than what the chip
   // holds at once; smaller grids keep the plain order and skip the pass.
-  a->order = w.bytes > 0 && nwg > kOrderMinWorkgroups
+  // Shared runs need the ordering pass (it drops the runs' followers), whatever the
+  // grid: matrix-core tiles only, groups of at most 8 query heads per tile (16/gt
+  // sequences per run), and pair indices that leave the run length room.
+  const bool shared = share && !quant && w.bytes > 0 &&
+                      hpkv::decode_on_matrix_cores(dtype, head_dim, group) && gt <= 8 &&
+                      uint64_t(num_seqs) * max_parts <= hpkv::kPairMask;
+  a->share_block = shared ? 16 / gt : 1;
+  a->share_flags =
+      shared ? reinterpret_cast<uint8_t*>(static_cast<char*>(workspace) + w.flags_offset)
+             : nullptr;
+  a->order = w.bytes > 0 && (nwg > kOrderMinWorkgroups || shared)
                  ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + w.order_offset)
                  : nullptr;
   *num_workgroups = nwg;
@@ -429,6 +441,26 @@ int hpkv_paged_attention_decode(int dtype, int index_type, const void* q, const 
                                 block_table_len, seq_ptr, context_lens, num_seqs, num_q_heads,
                                 num_kv_heads, head_dim, page_size, num_pages, scale,
                                 max_context_len, workspace, workspace_bytes, out, &a, &nwg);
+  if (st <= 0) return st;
+  return launch_decode(dtype, head_dim, a, nwg, static_cast<hipStream_t>(stream));
+}
+
+int hpkv_paged_attention_decode_shared(int dtype, int index_type, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const void* block_table, uint64_t block_table_len,
+                                       const void* seq_ptr, const int32_t* context_lens,
+                                       uint32_t num_seqs, uint32_t num_q_heads,
+                                       uint32_t num_kv_heads, uint32_t head_dim,
+                                       uint32_t page_size, uint64_t num_pages, float scale,
+                                       uint32_t max_context_len, void* workspace,
+                                       size_t workspace_bytes, void* out, void* stream) {
+  DecodeKernelArgs a;
+  uint64_t nwg = 0;
+  const int st = prepare_decode(dtype, index_type, q, k_cache, v_cache, block_table,
+                                block_table_len, seq_ptr, context_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, page_size, num_pages, scale,
+                                max_context_len, workspace, workspace_bytes, out, &a, &nwg, -1,
+                                true);
   if (st <= 0) return st;
   return launch_decode(dtype, head_dim, a, nwg, static_cast<hipStream_t>(stream));
 }

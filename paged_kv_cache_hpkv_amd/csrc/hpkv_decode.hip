@@ -155,9 +155,10 @@ struct Partition {
 };
 
 // One work item: sequence, partition, KV head g and the first query head h0
-// of the tile it serves. s == kNoWork: the item does nothing.
+// of the tile it serves, and the sequences s .. s+members-1 it serves (more
+// than one for a shared run). s == kNoWork: the item does nothing.
 struct WorkItem {
-  uint32_t s, part, g, h0;
+  uint32_t s, part, g, h0, members;
 };
 
 // Order-list entry (and WorkItem::s) of a pair with nothing to do: a partition
@@ -201,12 +202,17 @@ __device__ inline WorkItem grid_item(const DecodeKernelArgs& a) {
   const uint32_t ht = bid % a.head_tiles;
   bid /= a.head_tiles;  // (sequence, partition) pair, partition-major
   WorkItem it;
+  it.members = 1;
   if (a.order != nullptr) {
     bid = a.order[bid];
     if (bid == kNoWork) {
       it.s = kNoWork;
       it.part = it.g = it.h0 = 0;
       return it;
+    }
+    if (a.share_block > 1) {
+      it.members = (bid >> kRunShift) + 1;
+      bid &= kPairMask;
     }
   }
   it.s = bid % a.num_seqs;
@@ -236,6 +242,7 @@ constexpr uint32_t kOrderLdsSeqs = 8192;  // batches up to this size read length
 
 __device__ inline uint32_t order_class(const DecodeKernelArgs& a, const int32_t* lens,
                                        uint32_t j) {
+  if (a.share_flags != nullptr && a.share_flags[j]) return kOrderClasses - 1;  // a follower
   const uint32_t s = j % a.num_seqs, part = j / a.num_seqs;
   const int32_t n = lens[s];
   const uint32_t p0 = part * a.part_tokens;  // < max_context_len + part_tokens < 2^32
@@ -245,6 +252,57 @@ __device__ inline uint32_t order_class(const DecodeKernelArgs& a, const int32_t*
 }
 
 #if HPKV_DECODE_HAS(0)
+// Shared partitions ("Block-Paged KV Cache", "Element lookup through the block
+// table": sequences that alias the same pages read the same K/V rows). One wave
+// per (sequence, partition) pair j = s + B*part: the flag is 1 when s is not the
+// first of its aligned block of share_block sequences, both s and s - 1 have a
+// valid length and slice, partition `part` is full for both, and every page id
+// of that partition (at most kSharePagesMax pages) is the same, inside the pool,
+// in both tables. Then the two read exactly the same rows for that partition.
+constexpr uint32_t kSharePagesMax = 256;
+constexpr int kShareWaves = 4;
+
+__global__ __launch_bounds__(kShareWaves * kWave) void decode_share_kernel(
+    const DecodeKernelArgs a) {
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t j = blockIdx.x * kShareWaves + threadIdx.x / kWave;
+  if (j >= a.num_seqs * a.max_parts) return;
+  const uint32_t s = j % a.num_seqs, part = j / a.num_seqs;
+  bool same = false;
+  if (s % a.share_block != 0) {
+    const uint32_t P = a.part_tokens, p0 = part * P;
+    const int32_t n1 = a.context_lens[s], n0 = a.context_lens[s - 1];
+    const uint64_t f1 = read_idx(a.seq_ptr, s, a.idx64);
+    const uint64_t l1 = read_idx(a.seq_ptr, uint64_t(s) + 1, a.idx64);
+    const uint64_t f0 = read_idx(a.seq_ptr, s - 1, a.idx64);
+    auto full = [&](int32_t n, uint64_t f, uint64_t l) {
+      return !length_is_bad(n, a.max_context_len) && uint32_t(n) >= p0 + P && f <= l &&
+             l <= a.block_table_len && uint64_t(n) <= (l - f) * uint64_t(a.page_size);
+    };
+    const uint32_t k0 = fastdiv(p0, a.page_div), k1 = fastdiv(p0 + P - 1, a.page_div);
+    const uint32_t npp = k1 - k0 + 1;
+    // s - 1's slice ends where s's begins (CSR), so f0 <= l0 == f1
+    if (full(n1, f1, l1) && full(n0, f0, f1) && npp <= kSharePagesMax) {
+      bool eq = true;
+      for (uint32_t k = lane; k < npp; k += kWave) {
+        const uint64_t a1 = read_idx(a.block_table, f1 + k0 + k, a.idx64);
+        const uint64_t a0 = read_idx(a.block_table, f0 + k0 + k, a.idx64);
+        eq = eq && a1 == a0 && a1 < a.num_pages;
+      }
+      same = __all(eq);
+    }
+  }
+  if (lane == 0) a.share_flags[j] = same ? 1 : 0;
+}
+
+hipError_t launch_share(const DecodeKernelArgs& a, hipStream_t stream) {
+  if (a.share_flags == nullptr) return hipSuccess;
+  const uint32_t pairs = a.num_seqs * a.max_parts;
+  hipLaunchKernelGGL(decode_share_kernel, dim3((pairs + kShareWaves - 1) / kShareWaves),
+                     dim3(kShareWaves * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(kOrderWaves * kWave) void decode_order_kernel(
     const DecodeKernelArgs a) {
   __shared__ uint32_t s_cnt[kOrderClasses][kOrderWaves];
@@ -311,14 +369,32 @@ __global__ __launch_bounds__(kOrderWaves * kWave) void decode_order_kernel(
       if (c == k) pos = base[k] + uint32_t(__popcll(m & below));
       base[k] += uint32_t(__popcll(m));
     }
-    // pairs past a context (or after the first of a malformed length) do nothing:
-    // their workgroups need not even read the length
-    if (pos < n) a.order[pos] = c == kOrderClasses - 1 && j >= a.num_seqs ? kNoWork : j;
+    // pairs past a context (or after the first of a malformed length) and the
+    // followers of shared runs do nothing: their workgroups need not even read the
+    // length; the first pair of a run carries the run's length
+    if (pos < n) {
+      uint32_t e = c == kOrderClasses - 1 && j >= a.num_seqs ? kNoWork : j;
+      if (a.share_flags != nullptr && c < kOrderClasses) {
+        if (a.share_flags[j]) {
+          e = kNoWork;
+        } else if (c < kOrderClasses - 1) {
+          const uint32_t s = j % a.num_seqs;
+          uint32_t k = 1;
+          while (k < a.share_block && (s + k) % a.share_block != 0 && s + k < a.num_seqs &&
+                 a.share_flags[j + k])
+            ++k;
+          e = j | ((k - 1) << kRunShift);
+        }
+      }
+      a.order[pos] = e;
+    }
   }
 }
 
 hipError_t launch_order(const DecodeKernelArgs& a, hipStream_t stream) {
   if (a.order == nullptr) return hipSuccess;
+  const hipError_t e = launch_share(a, stream);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderWaves * kWave), 0, stream, a);
   return hipGetLastError();
 }
@@ -1052,12 +1128,15 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
   constexpr int VROW = D * 2 + 32; // LDS bytes per V row (transposing 8-byte reads likewise)
   constexpr int KS = D / 32;       // score MFMAs per 16 tokens (d steps)
   constexpr int NB = D / 16;       // P.V MFMAs per tile (16-column blocks of d)
+  constexpr int R = 16 / GT;       // sequences a shared run can bring into the 16 columns
+  constexpr int NC = R * GT;       // columns in use when a run fills the tile (16)
 
   __shared__ uint64_t s_row[HPW > 1 ? kWidePartTokens : kMaxPartTokens];
   __shared__ __attribute__((aligned(16))) char s_tile[NW][TT * (KROW + VROW)];
-  __shared__ float s_m[NW][GT];
-  __shared__ float s_l[NW][GT];
-  static_assert(sizeof(float) * GT * D <= TT * (KROW + VROW), "merge buffer must fit the tiles");
+  __shared__ float s_m[NW][NC];
+  __shared__ float s_l[NW][NC];
+  __shared__ uint32_t s_np[R];  // partitions of each served sequence
+  static_assert(sizeof(float) * NC * D <= TT * (KROW + VROW), "merge buffer must fit the tiles");
 
   const uint32_t lane = threadIdx.x % kWave;
   // wave-uniform: kept in a scalar register, so the tile loop branches are scalar
@@ -1065,22 +1144,32 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
   const uint32_t hw = wave % HPW;   // the wave's KV head within the workgroup's heads
   const uint32_t sub = wave / HPW;  // the wave's share of the partition's tiles
   Partition w;
+  const WorkItem item = grid_item<GT, (HPW > 1)>(a);
   // s_row holds the rows of the first KV head; head hw's rows follow at hw*D
-  if (!setup_partition<DT, D, HPW * GT, NTH, NoTokenHook, HPW>(a, grid_item<GT, (HPW > 1)>(a),
-                                                               s_row, w))
-    return;
+  if (!setup_partition<DT, D, HPW * GT, NTH, NoTokenHook, HPW>(a, item, s_row, w)) return;
   const uint32_t cnt = w.cnt;
 
+  // A shared run: sequences s .. s+members-1 read exactly these rows for this
+  // partition (the ordering pass checked every page id), so each gets GT columns of
+  // the tile; a column of a matrix-core result depends only on its own q column,
+  // so every member gets the arithmetic of its own workgroup.
+  const uint32_t members = R > 1 ? min(item.members, uint32_t(R)) : 1u;
+  if (threadIdx.x < members)
+    s_np[threadIdx.x] =
+        threadIdx.x == 0 ? w.nparts : num_parts(a.context_lens[w.s + threadIdx.x], a.part_tokens);
+  const uint32_t ncol = members * GT;  // columns in use: member col / GT, head col % GT
+
   const uint32_t q4 = lane / 16;   // lane quarter
-  const uint32_t col = lane % 16;  // MFMA column: query head of the tile (valid if < GT)
+  const uint32_t col = lane % 16;  // MFMA column
 
   u32x4 qop[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     qop[ks] = u32x4{0, 0, 0, 0};
-    if (col < GT) {
-      const char* qp = static_cast<const char*>(a.q) +
-                       ((w.out_row0 + hw * GT + col) * D + 32 * ks + 8 * q4) * 2;
+    if (col < ncol) {
+      const uint64_t row =
+          w.out_row0 + uint64_t(col / GT) * a.num_q_heads + hw * GT + col % GT;
+      const char* qp = static_cast<const char*>(a.q) + (row * D + 32 * ks + 8 * q4) * 2;
       qop[ks] = *reinterpret_cast<const u32x4*>(qp);
     }
   }
@@ -1163,7 +1252,7 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
         psum += widen_bits16<DT>(b0) + widen_bits16<DT>(b1);
         pw[j / 2] = b0 | (b1 << 16);
       }
-      // Columns col >= GT carry q = 0: scores 0 (or -inf past the context), finite
+      // Columns col >= ncol carry q = 0: scores 0 (or -inf past the context), finite
       // weights. A column of an MFMA result depends only on the same column of its B
       // operand, so they never reach a served head, and they are never stored.
       l += psum;
@@ -1188,8 +1277,8 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   __syncthreads();  // every wave is done with its tile before the tiles become merge space
-  float(*s_acc)[GT][D] = reinterpret_cast<float(*)[GT][D]>(&s_tile[0][0]);
-  if (col < GT) {
+  float(*s_acc)[NC][D] = reinterpret_cast<float(*)[NC][D]>(&s_tile[0][0]);
+  if (col < ncol) {
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
 #pragma unroll
@@ -1201,7 +1290,31 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
     }
   }
   __syncthreads();
-  finish_partition<DT, D, GT, NW, HPW>(a, w, s_m, s_l, s_acc);
+  // Merge the waves of each served column (log-sum-exp rule) and write the result, or
+  // the partition's partial when the column's sequence has several partitions: the
+  // arithmetic of finish_partition, per served sequence.
+  for (uint32_t i = threadIdx.x; i < HPW * ncol * D; i += NTH) {
+    const uint32_t hw_ = i / (ncol * D), c = (i / D) % ncol, e = i % D;
+    float mx = s_m[hw_][c];
+#pragma unroll
+    for (int v = 1; v < SPLIT; ++v) mx = fmaxf(mx, s_m[v * HPW + hw_][c]);
+    const float mref = mx == -INFINITY ? 0.0f : mx;
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int v = 0; v < SPLIT; ++v) {
+      const float f = __builtin_amdgcn_exp2f(s_m[v * HPW + hw_][c] - mref);
+      L = fmaf(s_l[v * HPW + hw_][c], f, L);
+      O = fmaf(s_acc[v * HPW + hw_][c][e], f, O);
+    }
+    const uint64_t row = w.out_row0 + uint64_t(c / GT) * a.num_q_heads + hw_ * GT + c % GT;
+    if (s_np[c / GT] == 1) {
+      store_out<DT>(a.out, row * D + e, L > 0.0f ? O / L : 0.0f);
+    } else {
+      const uint64_t r = row * a.max_parts + w.part;
+      a.ws_o[r * D + e] = O;
+      if (e == 0) a.ws_ml[r] = make_float2(mx, L);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -82,6 +82,14 @@ struct DecodeKernelArgs {
   // the ordering pass ahead of the partition pass. Null: plain partition-major
   // order.
   uint32_t* order;
+  // Shared partitions (hpkv_paged_attention_decode_shared on the matrix cores):
+  // sequences are grouped in aligned blocks of share_block (1: no sharing), and
+  // share_flags[s + num_seqs * part] = 1 when partition `part` of sequence s is
+  // full and covers the same page ids as that of sequence s - 1 in its block.
+  // The ordering pass then writes such a follower as no work, and the entry of
+  // the run's first sequence carries the run's length in its top bits.
+  uint32_t share_block;
+  uint8_t* share_flags;
 };
 
 struct ReduceKernelArgs {
@@ -173,6 +181,11 @@ hipError_t launch_slot_mapping(bool idx64, const void* block_table, uint64_t blo
 hipError_t launch_store(int chunk_bytes, const void* key, const void* value, void* k_cache,
                         void* v_cache, const int64_t* slots, uint64_t num_tokens,
                         uint64_t row_chunks, int64_t num_slots, hipStream_t stream);
+
+// Order-list entries of a shared run: pair index in the low bits, run length - 1
+// above them.
+constexpr uint32_t kRunShift = 29;
+constexpr uint32_t kPairMask = (1u << kRunShift) - 1;
 
 hipError_t launch_decode_partitions(int dtype, uint32_t head_dim, const DecodeKernelArgs& a,
                                     uint64_t num_workgroups, hipStream_t stream);

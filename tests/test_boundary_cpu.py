@@ -30,7 +30,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared()
-    assert len(declared) == 27
+    assert len(declared) == 28
     out = subprocess.run(["nm", "-D", "--defined-only", hpkv.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(hpkv_\w+)", out))
@@ -237,7 +237,8 @@ def test_reduce_argument_errors():
 def test_workspace_size_accounting():
     """The workspace is counted with the smaller, 512-token partition, so it covers
     every shape's plan: the (max, sum) pairs and the partial vectors, each padded
-    to 256 bytes, then one u32 per (sequence, partition) for the dispatch order."""
+    to 256 bytes, then one u32 per (sequence, partition) for the dispatch order
+    (padded), then one byte per pair for the shared-run flags."""
     P = hpkv.lib.hpkv_paged_attention_decode_partition_tokens(hpkv.BF16, 1, 32, 32, 128, 16,
                                                               4096)
     assert P == 512
@@ -246,9 +247,11 @@ def test_workspace_size_accounting():
     parts = -(-4096 // P)
     rows = 64 * 32 * parts
     pad = lambda b: -(-b // 256) * 256
-    assert ws(hpkv.BF16, 64, 32, 128, 16, 4096) == pad(rows * 8) + pad(rows * 128 * 4) + 64 * parts * 4
+    assert ws(hpkv.BF16, 64, 32, 128, 16, 4096) == \
+        pad(rows * 8) + pad(rows * 128 * 4) + pad(64 * parts * 4) + 64 * parts
     rows = 3 * 5 * 2  # ragged: 3 sequences, 5 query heads, d = 8, two partitions
-    assert ws(hpkv.F32, 3, 5, 8, 4, 513) == pad(rows * 8) + pad(rows * 8 * 4) + 3 * 2 * 4
+    assert ws(hpkv.F32, 3, 5, 8, 4, 513) == \
+        pad(rows * 8) + pad(rows * 8 * 4) + pad(3 * 2 * 4) + 3 * 2
     assert ws(9, 64, 32, 128, 16, 4096) == 0
 
 
