@@ -12,9 +12,10 @@ namespace {
 using hpkv::DecodeKernelArgs;
 using hpkv::ReduceKernelArgs;
 
-// Context tokens per split-context partition: 512 (kPartTokens) or 1024
-// (hpkv::kWidePartTokens, where the kernel's row table holds that many and the
-// batch still gives enough workgroups). The partials stay ~1-2 % of the KV bytes.
+// Context tokens per split-context partition: 512 (kPartTokens), 1024 or 2048
+// (hpkv::kWidePartTokens, hpkv::kLongPartTokens, where the kernel's row table
+// holds that many and the batch still gives enough workgroups). The partials
+// stay ~1-2 % of the KV bytes.
 constexpr uint32_t kPartTokens = 512;
 static_assert(kPartTokens <= hpkv::kMaxPartTokens, "partition larger than the LDS row table");
 static_assert(kPartTokens <= hpkv::kWidePartTokens, "the workspace is sized for the smaller one");
@@ -23,6 +24,10 @@ static_assert(kPartTokens <= hpkv::kWidePartTokens, "the workspace is sized for 
 // partitions beat 1024 one-head workgroups (44 vs 47 us); at 1 x 4096 tokens,
 // 64 one-head workgroups beat 16 two-head ones (13 vs 23 us).
 constexpr uint64_t kMinWorkgroups = 256;
+// 2048-token partitions halve the workgroups, and with them each workgroup's
+// fixed costs (row table, merge), for long contexts; they need four times the
+// workgroups of the other shapes so that the longest-first order still balances.
+constexpr uint64_t kMinLongWorkgroups = 4 * kMinWorkgroups;
 // Grids up to this many workgroups are resident on the 256 CUs at once (two
 // per CU), so their dispatch order does not matter.
 constexpr uint64_t kOrderMinWorkgroups = 512;
@@ -74,7 +79,7 @@ struct DecodePlan {
 DecodePlan plan_decode(int dtype, bool quant, uint32_t num_seqs, uint32_t num_q_heads,
                        uint32_t num_kv_heads, uint32_t head_dim, uint32_t max_context_len) {
   const uint32_t group = num_q_heads / num_kv_heads;
-  DecodePlan c[4];  // candidate shapes, coarsest first
+  DecodePlan c[6];  // candidate shapes, coarsest first
   int n = 0;
   if (quant) {
     const uint32_t gt = hpkv::heads_per_workgroup_quant(dtype, head_dim, group);
@@ -85,22 +90,25 @@ DecodePlan plan_decode(int dtype, bool quant, uint32_t num_seqs, uint32_t num_q_
   } else if (hpkv::decode_on_matrix_cores(dtype, head_dim, group)) {
     const uint32_t gt = hpkv::heads_per_workgroup(dtype, head_dim, group);
     if (hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads) > 1) {
+      c[n++] = {gt, 2, hpkv::kLongPartTokens};
       c[n++] = {gt, 2, hpkv::kWidePartTokens};
       c[n++] = {gt, 2, kPartTokens};
     }
     c[n++] = {gt, 1, kPartTokens};
   } else {
     const uint32_t gt = hpkv::heads_per_workgroup(dtype, head_dim, group);
-    for (uint32_t h = hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads); h > 1;
-         h /= 2)
-      c[n++] = {gt, h, hpkv::kWidePartTokens};
+    const uint32_t hpw = hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads);
+    c[n++] = {gt, hpw, hpkv::kLongPartTokens};
+    for (uint32_t h = hpw; h > 1; h /= 2) c[n++] = {gt, h, hpkv::kWidePartTokens};
     c[n++] = {gt, 1, hpkv::kWidePartTokens};
     c[n++] = {gt, 1, kPartTokens};
   }
   for (int i = 0; i + 1 < n; ++i) {
     const uint64_t grid = uint64_t(num_kv_heads / c[i].hpw) * (group / c[i].gt) * num_seqs *
                           max_parts_for(max_context_len, c[i].part_tokens);
-    if (grid >= kMinWorkgroups) return c[i];
+    const uint64_t need =
+        c[i].part_tokens == hpkv::kLongPartTokens ? kMinLongWorkgroups : kMinWorkgroups;
+    if (grid >= need) return c[i];
   }
   return c[n - 1];
 }
@@ -163,6 +171,12 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
   if (w.bytes > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return HPKV_ERR_INVALID_ARG;
 
+  // the two-head matrix-core kernel keeps 32-bit pool slots in its row table; a
+  // pool of more slots holds at least 2^32 * 256 bytes per K and V, beyond any one
+  // GPU's memory
+  if (!quant && hpw > 1 && hpkv::decode_on_matrix_cores(dtype, head_dim, group) &&
+      num_pages > (uint64_t(1) << 32) / page_size)
+    return HPKV_ERR_UNSUPPORTED;
   const uint32_t max_parts = max_parts_for(max_context_len, part_tokens);
   const uint64_t head_tiles = uint64_t(num_kv_heads / hpw) * (group / gt);
   const uint64_t nwg = head_tiles * max_parts * num_seqs;

@@ -412,10 +412,13 @@ struct NoTokenHook {
 };
 
 template <int DT, int D, int NH, int NTH, class Hook = NoTokenHook, int NKV = 1,
-          uint32_t CAP = 0>
+          class RowT = uint64_t, uint32_t CAP = 0>
 __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem& it,
-                                       uint64_t (&s_row)[CAP], Partition& w,
+                                       RowT (&s_row)[CAP], Partition& w,
                                        Hook on_token = Hook{}) {
+  // 64-bit entries hold element offsets; 32-bit entries hold the token's pool slot
+  // (the host takes a shape with them only for pools of at most 2^32 slots)
+  constexpr bool kSlots = sizeof(RowT) == 4;
   if (it.s == kNoWork) return false;
   const uint32_t tid = threadIdx.x;
   w.s = it.s;
@@ -470,7 +473,8 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
         bad_page = 1;
         ph = 0;
       }
-      s_row[i] = ((ph * a.page_size + off) * a.num_kv_heads + w.g) * uint64_t(D);
+      const uint64_t slot = ph * a.page_size + off;
+      s_row[i] = kSlots ? RowT(slot) : RowT((slot * a.num_kv_heads + w.g) * uint64_t(D));
       on_token(i, ph);
     }
   }
@@ -502,7 +506,10 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
     if (w.cnt > 0) {
       constexpr int EB = Elem<DT>::bytes;
       constexpr int CH = NKV * D * EB / 16;  // 16-byte chunks of the heads' rows
-      const uint64_t dst = s_row[w.cnt - 1] * EB;
+      const uint64_t last_row =
+          kSlots ? (uint64_t(s_row[w.cnt - 1]) * a.num_kv_heads + w.g) * uint64_t(D)
+                 : uint64_t(s_row[w.cnt - 1]);  // element offset of the token's row
+      const uint64_t dst = last_row * EB;
       const uint64_t src = (uint64_t(w.s) * a.num_kv_heads + w.g) * D * EB;
       for (uint32_t i = tid; i < uint32_t(CH); i += NTH) {
         const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.new_k) + src + i * 16);
@@ -511,7 +518,7 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
         *reinterpret_cast<u32x4*>(const_cast<char*>(static_cast<const char*>(a.v_cache)) + dst + i * 16) = vv;
       }
       if (slot_writer) {
-        const uint64_t row = s_row[w.cnt - 1] / D;  // (slot * Hkv + g)
+        const uint64_t row = last_row / D;  // (slot * Hkv + g)
         a.slots_out[w.s] = int64_t((row - w.g) / a.num_kv_heads);
       }
       __syncthreads();
@@ -580,7 +587,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_kernel
                     (HPW & (HPW - 1)) == 0,
                 "unsupported head_dim");
 
-  __shared__ uint64_t s_row[kWidePartTokens];
+  __shared__ uint64_t s_row[kLongPartTokens];
   __shared__ float s_m[NW][GW];
   __shared__ float s_l[NW][GW];
   __shared__ float s_acc[NW][GW][D];
@@ -1131,7 +1138,10 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
   constexpr int R = 16 / GT;       // sequences a shared run can bring into the 16 columns
   constexpr int NC = R * GT;       // columns in use when a run fills the tile (16)
 
-  __shared__ uint64_t s_row[HPW > 1 ? kWidePartTokens : kMaxPartTokens];
+  // two-head workgroups: pool slots (32 bits) for up to kLongPartTokens tokens, so
+  // the table stays at 8 KB and two workgroups still share a CU; else offsets
+  using RowT = std::conditional_t<(HPW > 1), uint32_t, uint64_t>;
+  __shared__ RowT s_row[HPW > 1 ? kLongPartTokens : kMaxPartTokens];
   __shared__ __attribute__((aligned(16))) char s_tile[NW][TT * (KROW + VROW)];
   __shared__ float s_m[NW][NC];
   __shared__ float s_l[NW][NC];
@@ -1182,8 +1192,11 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
   const uint32_t lr = lane / LPR, lc = lane % LPR;  // row-major load: row, 16-byte chunk
   char* kt = s_tile[wave];
   char* vt = s_tile[wave] + TT * KROW;
-  const char* kbase = static_cast<const char*>(a.k_cache) + (hw * D + lc * 8) * 2;
-  const char* vbase = static_cast<const char*>(a.v_cache) + (hw * D + lc * 8) * 2;
+  // with a slot table, head g's row of a token starts g*D elements into its pool row
+  const uint64_t row_bytes = uint64_t(a.num_kv_heads) * D * 2;
+  const uint64_t head0 = HPW > 1 ? uint64_t(w.g) * D : 0;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (head0 + hw * D + lc * 8) * 2;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (head0 + hw * D + lc * 8) * 2;
 
   uint32_t tb = sub * TT;
   if (tb < cnt) {
@@ -1192,7 +1205,8 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const uint32_t li = t0 + i * RPL + lr;
-        const uint64_t off = s_row[li < cnt ? li : cnt - 1] * 2;
+        const uint64_t off = HPW > 1 ? uint64_t(s_row[li < cnt ? li : cnt - 1]) * row_bytes
+                                     : uint64_t(s_row[li < cnt ? li : cnt - 1]) * 2;
         kr[i] = load16<true>(kbase + off);
         vr[i] = load16<true>(vbase + off);
       }

@@ -17,9 +17,12 @@ inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : 2; }
 // Split-context partitions, in context tokens, as sizes of the decode kernels'
 // LDS row tables: the quantized kernels and the matrix-core kernel with one KV
 // head per workgroup hold kMaxPartTokens; the VALU kernel and the matrix-core
-// kernel with two KV heads per workgroup hold kWidePartTokens.
+// kernel with two KV heads per workgroup hold kLongPartTokens (the latter as
+// 32-bit pool slots). Partitions of kWidePartTokens and kLongPartTokens run on
+// those two kernels.
 constexpr uint32_t kMaxPartTokens = 512;
 constexpr uint32_t kWidePartTokens = 1024;
+constexpr uint32_t kLongPartTokens = 2048;
 
 // Division by a runtime divisor 1 <= d < 2^31 for numerators n < 2^31:
 // n / d == (n * mul) >> shift with shift = 31 + ceil(log2 d) and

@@ -121,6 +121,9 @@ def test_decode_argument_errors():
     assert _decode_call(d=96) == hpkv.ERR_UNSUPPORTED
     assert _decode_call(d=512) == hpkv.ERR_UNSUPPORTED
     assert _decode_call(dtype=hpkv.F32, d=512) == hpkv.ERR_UNSUPPORTED
+    # the two-head matrix-core shape keeps 32-bit pool slots: at most 2^32 slots
+    assert _decode_call(B=1024, hq=8, hkv=2, num_pages=(1 << 28) + 1, ws_bytes=1 << 34) == \
+        hpkv.ERR_UNSUPPORTED
     assert _decode_call(ws=None) == hpkv.ERR_WORKSPACE            # max_ctx 4096 needs partials
     need = hpkv.lib.hpkv_paged_attention_decode_workspace_size(hpkv.BF16, 2, 4, 128, 16, 4096)
     assert need > 0
@@ -204,18 +207,23 @@ def test_quant_argument_errors():
 
 
 def test_partition_tokens_per_shape():
-    """1024-token partitions where the batch still gives >= 256 workgroups with them
-    (KV heads / heads per workgroup x sequences x partitions), else 512."""
+    """2048-token partitions where the batch still gives >= 1024 workgroups with them,
+    else 1024-token ones where it gives >= 256 (KV heads / heads per workgroup x
+    sequences x partitions), else 512."""
     pt = hpkv.lib.hpkv_paged_attention_decode_partition_tokens
     # GQA 32/8 on the matrix cores, two KV heads per workgroup: 4 head tiles
-    assert pt(hpkv.BF16, 256, 32, 8, 128, 16, 8192) == 1024    # 4 * 256 * 8
+    assert pt(hpkv.BF16, 256, 32, 8, 128, 16, 8192) == 2048    # 4 * 256 * 4
+    assert pt(hpkv.BF16, 64, 32, 8, 128, 16, 8192) == 2048     # 4 * 64 * 4 = 1024
+    assert pt(hpkv.BF16, 63, 32, 8, 128, 16, 8192) == 1024     # 1008 < 1024
     assert pt(hpkv.BF16, 8, 32, 8, 128, 16, 8192) == 1024      # 4 * 8 * 8 = 256
     assert pt(hpkv.BF16, 7, 32, 8, 128, 16, 8192) == 512       # 224 < 256
     assert pt(hpkv.BF16, 1, 32, 8, 128, 16, 4096) == 512
-    # MHA 32/32 on the VALU kernel: 32 head tiles
+    # MHA 32/32 on the VALU kernel: 16 two-head tiles, or 32 one-head tiles
+    assert pt(hpkv.BF16, 64, 32, 32, 128, 16, 4096) == 2048    # 16 * 64 * 2
+    assert pt(hpkv.BF16, 16, 32, 32, 128, 16, 4096) == 1024    # 16 * 16 * 4
     assert pt(hpkv.BF16, 2, 32, 32, 128, 16, 4096) == 1024     # 32 * 2 * 4 = 256
     assert pt(hpkv.BF16, 1, 32, 32, 128, 16, 4096) == 512      # 128 < 256
-    assert pt(hpkv.F32, 128, 32, 8, 128, 16, 8192) == 1024     # VALU, 8 heads per tile
+    assert pt(hpkv.F32, 128, 32, 8, 128, 16, 8192) == 2048     # VALU, 8 heads per tile
     assert pt(hpkv.BF16, 512, 24, 3, 128, 16, 8192) == 512     # odd Hkv on the matrix cores
     assert pt(hpkv.BF16, 8, 32, 0, 128, 16, 4096) == 0
     assert pt(hpkv.BF16, 8, 30, 8, 128, 16, 4096) == 0

@@ -1,6 +1,7 @@
 """GPU parity across the decode launch plan's shapes.
 
-The decode picks a launch shape per call: the coarsest one (two KV heads per
+The decode picks a launch shape per call: 2048-token partitions when their
+grid still has 1024 workgroups, else the coarsest shape (two KV heads per
 workgroup and/or 1024-token partitions) whose grid still has 256 workgroups,
 else finer ones. Batch sizes here straddle those thresholds so that every
 shape runs: for each case the partition size the library reports is checked
@@ -31,13 +32,18 @@ def _shape(name, ctx, hq, hkv, d=128, dtype="bf16", bs=16, seed=11):
 
 # (name, context lengths, Hq, Hkv, planned partition tokens, head_dim)
 CASES = [
-    # matrix cores, GQA 32/8: two KV heads & 1024 (4*8*8 = 256 workgroups) ...
+    # matrix cores, GQA 32/8: two KV heads & 2048 (4*64*4 = 1024 workgroups; slot
+    # row table, partial last partitions) ...
+    ("mfma-2h-2048", [8192] * 40 + [5000] * 20 + [3000] * 4, 32, 8, 2048, 128),
+    # ... two KV heads & 1024 (4*8*8 = 256 workgroups) ...
     ("mfma-2h-1024", [8192] * 8, 32, 8, 1024, 128),
     # ... two KV heads & 512 (4*7*8 = 224 < 256; 4*7*16 = 448) ...
     ("mfma-2h-512", [8192] * 6 + [1000], 32, 8, 512, 128),
     # ... one KV head & 512 (4*1*4 = 16 and 4*1*8 = 32 are below 256)
     ("mfma-1h-512", [4096], 32, 8, 512, 128),
-    # VALU kernel (MHA 32/32): 1024 (32*2*4 = 256), then 512 (32*1*4 = 128)
+    # VALU kernel (MHA 32/32): two KV heads & 2048 (16*32*2 = 1024; a ragged last
+    # partition), then 1024 (32*2*4 = 256), then 512 (32*1*4 = 128)
+    ("valu-2h-2048", [4096] * 31 + [3001], 32, 32, 2048, 128),
     ("valu-1024", [4096, 2500], 32, 32, 1024, 128),
     ("valu-512", [4096], 32, 32, 512, 128),
     # VALU kernel at d=64 (128-byte head rows): four KV heads & 1024 (4*16*4 = 256)
@@ -176,8 +182,8 @@ def test_decode_dispatch_order_many_seqs():
     of LDS in the ordering pass; the order must be the same permutation."""
     rng = np.random.default_rng(21)
     B, bs, d = 8300, 16, 64
-    ctx = rng.integers(0, 2049, B).astype(np.int32)
-    ctx[::97] = 2048  # the longest context sets max_context_len
+    ctx = rng.integers(0, 4097, B).astype(np.int32)
+    ctx[::97] = 4096  # the longest context sets max_context_len (two 2048-token partitions)
     pages = -(-ctx // bs)
     seq_ptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.uint32)
     num_pages = int(seq_ptr[-1])
