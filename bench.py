@@ -28,8 +28,9 @@ Printed: ONE JSON line with
                median duration, against the 8 TB/s HBM peak;
   ceilings     the library's read-ceiling kernel (hpkv_read_ceiling) on a
                buffer the size of the step's K/V: a plain streaming read and
-               the decode's row pattern (256-byte rows at an 8 KiB and a
-               2 KiB stride), each timed like the kernels;
+               the decode's row patterns (one head's 256-byte rows and two
+               heads' 512-byte rows at an 8 KiB and a 2 KiB stride), each
+               timed like the kernels;
   cpu_baseline the CPU oracle (double precision, plain loops) running the same
                step on host copies of the same inputs, repeated for about ten
                seconds and timed on the host (median per step).
@@ -169,7 +170,10 @@ class Timer:
 
 
 def ceilings(dev, timer, nbytes, launches=20):
-    """HBM read ceilings on a buffer of about nbytes (hpkv_read_ceiling), GB/s (median)."""
+    """HBM read ceilings on a buffer of about nbytes (hpkv_read_ceiling), GB/s (median):
+    a plain streaming read; one head row (256 B at d=128 bf16) of every token at the
+    8 KiB and 2 KiB token strides of 32 and 8 KV heads; and two adjacent heads' 512 B,
+    the rows the two-head decode workgroups read."""
     import paged_kv_cache_hpkv_amd as hpkv
     stride_max = 8192
     nbytes = max(stride_max, nbytes // stride_max * stride_max)
@@ -178,7 +182,9 @@ def ceilings(dev, timer, nbytes, launches=20):
     out = {}
     for name, row, stride, rows_per_wg in (("stream", 4096, 4096, 64),
                                           ("rows256_stride8k", 256, 8192, 512),
-                                          ("rows256_stride2k", 256, 2048, 512)):
+                                          ("rows256_stride2k", 256, 2048, 512),
+                                          ("rows512_stride8k", 512, 8192, 512),
+                                          ("rows512_stride2k", 512, 2048, 512)):
         def fn():
             hpkv.hpkv_read_ceiling(buf, row, stride, rows_per_wg, sink)
         fn()
@@ -280,9 +286,10 @@ def algorithmic_decode_bytes(w):
     return int(w.kv_bytes_unique_rows() + pages.sum() * idx + per_seq * w.num_seqs)
 
 
-def recorded_traffic(w, traffic_file=TRAFFIC_FILE, src=DECODE_SRC):
+def recorded_traffic(w, traffic_file=TRAFFIC_FILE, src=DECODE_SRC, variant=""):
     """HBM bytes per launch of the dominant kernel from committed counter runs, if the
-    kernel source has not changed since they were taken."""
+    kernel source has not changed since they were taken (variant: "/shared" for the
+    shared decode's record)."""
     try:
         with open(traffic_file) as f:
             rec = json.load(f)
@@ -292,7 +299,7 @@ def recorded_traffic(w, traffic_file=TRAFFIC_FILE, src=DECODE_SRC):
         return None
     if rec.get("kernel_source_sha256") != src_hash:
         return None  # the kernel changed since the counters were taken
-    return rec.get("workloads", {}).get(f"{w.name}/{w.dtype}/{w.index}")
+    return rec.get("workloads", {}).get(f"{w.name}/{w.dtype}/{w.index}{variant}")
 
 
 def host_description():
@@ -711,7 +718,7 @@ def main():
 
     kv = w.kv_bytes_logical()
     value = kv / (ms_per_step * 1e-3) / 1e9
-    rec = recorded_traffic(w)
+    rec = recorded_traffic(w, variant="/shared" if args.shared else "")
     b = torch.tensor([], dtype=w.torch_dtype).element_size()
     line = {
         "metric": METRIC,

@@ -184,9 +184,9 @@ size_t hpkv_paged_attention_decode_workspace_size(int dtype, uint32_t num_seqs,
 
 /* Context tokens covered by one split-context partition of
  * hpkv_paged_attention_decode (and of the _step and _reduce entry points) for
- * this call shape: 1024 when the batch still gives at least 256 workgroups (one
- * per CU) with partitions that long, else 512 (the quantized decode always
- * uses 512).
+ * this call shape: 2048 when the batch still gives at least 1024 workgroups
+ * with partitions that long, else 1024 when it gives at least 256 (one per
+ * CU), else 512 (the quantized decode always uses 512).
  * Exposed for accounting and tests. 0 on invalid arguments. */
 uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_seqs,
                                                       uint32_t num_q_heads,
@@ -231,7 +231,11 @@ uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_se
  * head_dim * sizeof(dtype) a
  * multiple of 16 bytes with head_dim * sizeof(dtype) / 16 a power of two
  * <= 64 (bf16/f16: head_dim in {8,16,32,64,128,256}; f32: {4,...,256}),
- * otherwise HPKV_ERR_UNSUPPORTED.
+ * otherwise HPKV_ERR_UNSUPPORTED. When the matrix-core kernel serves two KV
+ * heads per workgroup (16-bit dtype, GQA groups of 4 or more, even
+ * num_kv_heads, large batches), num_pages * page_size must not exceed 2^32
+ * (its row table holds 32-bit pool slots; such a pool takes at least 512 GiB):
+ * HPKV_ERR_UNSUPPORTED otherwise.
  * Malformed contents (caller error): a sequence with n < 0,
  * n > max_context_len, n beyond its slice, or a page id >= num_pages in the
  * pages it reads, gets NaN in all its outputs.
