@@ -186,13 +186,26 @@ size_t hpkv_paged_attention_decode_workspace_size(int dtype, uint32_t num_seqs,
  * hpkv_paged_attention_decode (and of the _step and _reduce entry points) for
  * this call shape: 2048 when the batch still gives at least 1024 workgroups
  * with partitions that long, else 1024 when it gives at least 256 (one per
- * CU), else 512 (the quantized decode always uses 512).
+ * CU), else 512.
  * Exposed for accounting and tests. 0 on invalid arguments. */
 uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_seqs,
                                                       uint32_t num_q_heads,
                                                       uint32_t num_kv_heads, uint32_t head_dim,
                                                       uint32_t page_size,
                                                       uint32_t max_context_len);
+
+/* The same for hpkv_paged_attention_decode_quant (kv_type HPKV_KV_I8 or
+ * HPKV_KV_FP8_E4M3): the same thresholds, among the partitions whose pages fit
+ * the kernels' per-page table (at most 520 pages: 2048 tokens needs pages of 4
+ * or more tokens, 1024 of 2 or more); 2048-token partitions only where the
+ * matrix-core kernel runs (16-bit dtype, GQA groups of 4 or more, head_dim 32,
+ * 64 or 128). 0 on invalid arguments. */
+uint32_t hpkv_paged_attention_decode_quant_partition_tokens(int dtype, int kv_type,
+                                                            uint32_t num_seqs,
+                                                            uint32_t num_q_heads,
+                                                            uint32_t num_kv_heads,
+                                                            uint32_t head_dim, uint32_t page_size,
+                                                            uint32_t max_context_len);
 
 /* ---------------------------------------------------------------------------
  * hpkv_paged_attention_decode  (device)

@@ -48,6 +48,7 @@ EXPORTED = [
     "hpkv_xxh64", "hpkv_read_ceiling", "hpkv_paged_attention_decode_noalloc",
     "hpkv_paged_attention_decode_shared",
     "hpkv_paged_attention_decode_noalloc_max_workspace",
+    "hpkv_paged_attention_decode_quant_partition_tokens",
 ]
 
 
@@ -78,6 +79,8 @@ def _load():
         "hpkv_paged_attention_decode_workspace_size": ([i32, u32, u32, u32, u32, u32], sz),
         "hpkv_paged_attention_decode_partition_tokens": ([i32, u32, u32, u32, u32, u32, u32],
                                                          u32),
+        "hpkv_paged_attention_decode_quant_partition_tokens": (
+            [i32, i32, u32, u32, u32, u32, u32, u32], u32),
         "hpkv_paged_attention_decode": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, u32, u32, u32,
                                          u32, u32, u64, f32, u32, vp, sz, vp, vp], i32),
         "hpkv_paged_attention_decode_shared": ([i32, i32, vp, vp, vp, vp, u64, vp, vp, u32, u32,
@@ -206,6 +209,14 @@ def hpkv_paged_attention_decode_partition_tokens(dtype, num_seqs, num_q_heads, n
     return int(lib.hpkv_paged_attention_decode_partition_tokens(
         _DTYPE_CODE[dtype], num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
         max_context_len))
+
+
+def hpkv_paged_attention_decode_quant_partition_tokens(dtype, kv_type, num_seqs, num_q_heads,
+                                                       num_kv_heads, head_dim, page_size,
+                                                       max_context_len):
+    return int(lib.hpkv_paged_attention_decode_quant_partition_tokens(
+        _DTYPE_CODE[dtype], KV_TYPES[kv_type], num_seqs, num_q_heads, num_kv_heads, head_dim,
+        page_size, max_context_len))
 
 
 # -------------------------------------------------------------- device entry points

@@ -77,16 +77,25 @@ struct DecodePlan {
 };
 
 DecodePlan plan_decode(int dtype, bool quant, uint32_t num_seqs, uint32_t num_q_heads,
-                       uint32_t num_kv_heads, uint32_t head_dim, uint32_t max_context_len) {
+                       uint32_t num_kv_heads, uint32_t head_dim, uint32_t page_size,
+                       uint32_t max_context_len) {
   const uint32_t group = num_q_heads / num_kv_heads;
   DecodePlan c[6];  // candidate shapes, coarsest first
   int n = 0;
   if (quant) {
+    // Partitions whose pages fit the kernels' per-page table. 2048 tokens only on the
+    // matrix cores: the VALU kernel's two-wave workgroups (six per CU) are left too
+    // few rounds by them (measured: qwen3 int8 0.506 ms at 1024, 0.588 at 2048;
+    // quantized GQA on the matrix cores 0.222 at 1024, 0.209 at 2048).
+    const bool mfma = hpkv::decode_quant_on_matrix_cores(dtype, head_dim, group);
     const uint32_t gt = hpkv::heads_per_workgroup_quant(dtype, head_dim, group);
-    if (!hpkv::decode_quant_on_matrix_cores(dtype, head_dim, group) && gt == group &&
-        num_kv_heads % 2 == 0)
-      c[n++] = {gt, 2, kPartTokens};
-    c[n++] = {gt, 1, kPartTokens};
+    const uint32_t hpw = !mfma && gt == group && num_kv_heads % 2 == 0 ? 2 : 1;
+    for (uint32_t p : {hpkv::kLongPartTokens, hpkv::kWidePartTokens})
+      if ((mfma || p != hpkv::kLongPartTokens) &&
+          hpkv::partition_pages_max(p, page_size) <= hpkv::kQuantTablePages)
+        c[n++] = {gt, hpw, p};
+    c[n++] = {gt, hpw, kPartTokens};
+    if (hpw > 1) c[n++] = {gt, 1, kPartTokens};
   } else if (hpkv::decode_on_matrix_cores(dtype, head_dim, group)) {
     const uint32_t gt = hpkv::heads_per_workgroup(dtype, head_dim, group);
     if (hpkv::kv_heads_per_workgroup(dtype, head_dim, group, num_kv_heads) > 1) {
@@ -163,7 +172,7 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
     return HPKV_ERR_INVALID_ARG;
   const uint32_t group = num_q_heads / num_kv_heads;
   const DecodePlan plan = plan_decode(dtype, quant, num_seqs, num_q_heads, num_kv_heads,
-                                      head_dim, max_context_len);
+                                      head_dim, page_size, max_context_len);
   const uint32_t hpw = plan.hpw, gt = plan.gt, part_tokens = plan.part_tokens;
   const WorkspaceLayout w =
       workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, part_tokens);
@@ -370,11 +379,24 @@ uint32_t hpkv_paged_attention_decode_partition_tokens(int dtype, uint32_t num_se
                                                       uint32_t num_kv_heads, uint32_t head_dim,
                                                       uint32_t page_size,
                                                       uint32_t max_context_len) {
-  (void)page_size;
   if (!valid_dtype(dtype) || num_q_heads == 0 || num_kv_heads == 0 ||
       num_q_heads % num_kv_heads != 0)
     return 0;
-  return plan_decode(dtype, false, num_seqs, num_q_heads, num_kv_heads, head_dim,
+  return plan_decode(dtype, false, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                     max_context_len)
+      .part_tokens;
+}
+
+uint32_t hpkv_paged_attention_decode_quant_partition_tokens(int dtype, int kv_type,
+                                                            uint32_t num_seqs,
+                                                            uint32_t num_q_heads,
+                                                            uint32_t num_kv_heads,
+                                                            uint32_t head_dim, uint32_t page_size,
+                                                            uint32_t max_context_len) {
+  if (!valid_dtype(dtype) || (kv_type != HPKV_KV_I8 && kv_type != HPKV_KV_FP8_E4M3) ||
+      num_q_heads == 0 || num_kv_heads == 0 || num_q_heads % num_kv_heads != 0 || page_size == 0)
+    return 0;
+  return plan_decode(dtype, true, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                      max_context_len)
       .part_tokens;
 }
@@ -421,7 +443,7 @@ int hpkv_paged_attention_decode_reduce(int dtype, const int32_t* context_lens, u
   if (max_context_len > 0x7fffffffu) return HPKV_ERR_INVALID_ARG;
   if (!decode_head_dim_supported(dtype, head_dim)) return HPKV_ERR_UNSUPPORTED;
   const uint32_t part_tokens = plan_decode(dtype, false, num_seqs, num_q_heads, num_kv_heads,
-                                           head_dim, max_context_len)
+                                           head_dim, page_size, max_context_len)
                                    .part_tokens;
   const WorkspaceLayout w =
       workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, part_tokens);

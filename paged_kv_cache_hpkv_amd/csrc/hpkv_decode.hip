@@ -411,14 +411,14 @@ struct NoTokenHook {
   __device__ void operator()(uint32_t, uint64_t) const {}
 };
 
-template <int DT, int D, int NH, int NTH, class Hook = NoTokenHook, int NKV = 1,
-          class RowT = uint64_t, uint32_t CAP = 0>
-__device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem& it,
-                                       RowT (&s_row)[CAP], Partition& w,
-                                       Hook on_token = Hook{}) {
-  // 64-bit entries hold element offsets; 32-bit entries hold the token's pool slot
-  // (the host takes a shape with them only for pools of at most 2^32 slots)
-  constexpr bool kSlots = sizeof(RowT) == 4;
+// The checks every workgroup makes before it resolves its rows: no-work entry,
+// partition past the context, malformed length (its NaN result is written here),
+// malformed table slice or a partition longer than the row table holds
+// (`fits` false; reported through `bad`). Fills w (w.cnt = 0 when bad).
+template <int DT, int D, int NH, int NTH>
+__device__ inline bool begin_partition(const DecodeKernelArgs& a, const WorkItem& it, bool fits,
+                                       Partition& w, uint64_t& first, bool& bad,
+                                       bool& slot_writer) {
   if (it.s == kNoWork) return false;
   const uint32_t tid = threadIdx.x;
   w.s = it.s;
@@ -428,13 +428,13 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
 
   // the length and the table slice bounds are independent loads: issue both
   const int32_t n = a.context_lens[w.s];
-  const uint64_t first = read_idx(a.seq_ptr, w.s, a.idx64);
+  first = read_idx(a.seq_ptr, w.s, a.idx64);
   const uint64_t last = read_idx(a.seq_ptr, uint64_t(w.s) + 1, a.idx64);
   w.nparts = num_parts(n, a.part_tokens);
   if (w.part >= w.nparts) return false;
 
   w.out_row0 = uint64_t(w.s) * a.num_q_heads + h0;
-  const bool slot_writer = a.slots_out != nullptr && tid == 0 && h0 == 0;  // once per sequence
+  slot_writer = a.slots_out != nullptr && tid == 0 && h0 == 0;  // once per sequence
   if (length_is_bad(n, a.max_context_len)) {
     if (w.part == 0) {
       for (uint32_t i = tid; i < NH * D; i += NTH) store_out<DT>(a.out, w.out_row0 * D + i, NAN);
@@ -445,11 +445,44 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
 
   // (a partition longer than the row table cannot come from the host's plan; it is
   // refused here rather than written past the table)
-  bool bad = first > last || last > a.block_table_len ||
-             uint64_t(n) > (last - first) * uint64_t(a.page_size) || a.part_tokens > CAP;
-
+  bad = first > last || last > a.block_table_len ||
+        uint64_t(n) > (last - first) * uint64_t(a.page_size) || !fits;
   const uint32_t p0 = w.part * a.part_tokens;
   w.cnt = bad || n == 0 ? 0u : min(uint32_t(n) - p0, a.part_tokens);
+  return true;
+}
+
+// Malformed index buffers: NaN result (or NaN partials) for this partition.
+template <int DT, int D, int NH, int NTH>
+__device__ inline void fail_partition(const DecodeKernelArgs& a, const Partition& w,
+                                      bool slot_writer) {
+  const uint32_t tid = threadIdx.x;
+  if (w.nparts == 1) {
+    for (uint32_t i = tid; i < NH * D; i += NTH) store_out<DT>(a.out, w.out_row0 * D + i, NAN);
+  } else {
+    for (uint32_t i = tid; i < NH * D; i += NTH) {
+      const uint64_t r = (w.out_row0 + i / D) * a.max_parts + w.part;
+      a.ws_o[r * D + i % D] = NAN;
+      if (i % D == 0) a.ws_ml[r] = make_float2(NAN, NAN);
+    }
+  }
+  if (slot_writer && w.part + 1 == w.nparts) a.slots_out[w.s] = -1;
+}
+
+template <int DT, int D, int NH, int NTH, class Hook = NoTokenHook, int NKV = 1,
+          class RowT = uint64_t, uint32_t CAP = 0>
+__device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem& it,
+                                       RowT (&s_row)[CAP], Partition& w,
+                                       Hook on_token = Hook{}) {
+  // 64-bit entries hold element offsets; 32-bit entries hold the token's pool slot
+  // (the host takes a shape with them only for pools of at most 2^32 slots)
+  constexpr bool kSlots = sizeof(RowT) == 4;
+  const uint32_t tid = threadIdx.x;
+  uint64_t first = 0;
+  bool bad = false, slot_writer = false;
+  if (!begin_partition<DT, D, NH, NTH>(a, it, a.part_tokens <= CAP, w, first, bad, slot_writer))
+    return false;
+  const uint32_t p0 = w.part * a.part_tokens;
 
   // Each thread resolves tokens tid, tid + NTH, ...: all of its table reads are
   // issued before the first is used, so the table costs one memory round trip.
@@ -481,18 +514,8 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
   bad = __syncthreads_or(bad_page) != 0 || bad;
 
   const bool last_part = w.part + 1 == w.nparts;
-  if (bad) {  // malformed index buffers: NaN result for this partition
-    if (w.nparts == 1) {
-      for (uint32_t i = tid; i < NH * D; i += NTH)
-        store_out<DT>(a.out, w.out_row0 * D + i, NAN);
-    } else {
-      for (uint32_t i = tid; i < NH * D; i += NTH) {
-        const uint64_t r = (w.out_row0 + i / D) * a.max_parts + w.part;
-        a.ws_o[r * D + i % D] = NAN;
-        if (i % D == 0) a.ws_ml[r] = make_float2(NAN, NAN);
-      }
-    }
-    if (slot_writer && last_part) a.slots_out[w.s] = -1;
+  if (bad) {
+    fail_partition<DT, D, NH, NTH>(a, w, slot_writer);
     return false;
   }
 
@@ -525,6 +548,62 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
     } else if (slot_writer) {
       a.slots_out[w.s] = -1;  // empty context: nothing appended
     }
+  }
+  return true;
+}
+
+// Quantized pools: the row table is kept per page instead of per token (the
+// page factors are per page and KV head anyway), so a partition of up to
+// kQuantTablePages pages fits: 512 tokens of 1-token pages, 2048 tokens of pages
+// of 4 or more. Entry k of s_page is the pool page of the partition's k-th page,
+// k = fastdiv(p) - k0 for the token at position p, and s_fac[k][h] holds that
+// page's (k scale, k zero + bias, v scale, v zero + bias) for KV head g + h.
+// Same checks and malformed-input results as setup_partition; no fused store.
+template <int DT, int D, int NH, int NTH, int NKV, uint32_t CAPP>
+__device__ inline bool setup_pages(const DecodeKernelArgs& a, const WorkItem& it, float bias,
+                                   uint32_t (&s_page)[CAPP], float4 (&s_fac)[CAPP][NKV],
+                                   Partition& w, uint32_t& k0) {
+  const uint32_t tid = threadIdx.x;
+  uint64_t first = 0;
+  bool bad = false, slot_writer = false;
+  if (!begin_partition<DT, D, NH, NTH>(a, it, true, w, first, bad, slot_writer)) return false;
+  const uint32_t p0 = w.part * a.part_tokens;
+  k0 = fastdiv(p0, a.page_div);
+  uint32_t npg = w.cnt == 0 ? 0u : fastdiv(p0 + w.cnt - 1, a.page_div) - k0 + 1;
+  if (npg > CAPP) {  // not from the host's plan: refused rather than written past the table
+    bad = true;
+    npg = 0;
+  }
+  constexpr uint32_t KP = (CAPP + NTH - 1) / NTH;
+  uint64_t phys[KP];
+#pragma unroll
+  for (uint32_t k = 0; k < KP; ++k) {
+    const uint32_t i = tid + k * NTH;
+    phys[k] = i < npg ? read_idx(a.block_table, first + k0 + i, a.idx64) : 0;
+  }
+  int bad_page = 0;
+#pragma unroll
+  for (uint32_t k = 0; k < KP; ++k) {
+    const uint32_t i = tid + k * NTH;
+    if (i < npg) {
+      uint64_t ph = phys[k];
+      if (ph >= a.num_pages) {
+        bad_page = 1;
+        ph = 0;
+      }
+      s_page[i] = uint32_t(ph);  // num_pages * Hkv < 2^32 for quantized pools
+#pragma unroll
+      for (int h = 0; h < NKV; ++h) {
+        const uint64_t f = ph * a.num_kv_heads + w.g + h;
+        s_fac[i][h] = make_float4(a.k_scale[f], a.k_zero[f] + bias, a.v_scale[f],
+                                  a.v_zero[f] + bias);
+      }
+    }
+  }
+  bad = __syncthreads_or(bad_page) != 0 || bad;
+  if (bad) {
+    fail_partition<DT, D, NH, NTH>(a, w, slot_writer);
+    return false;
   }
   return true;
 }
@@ -862,30 +941,24 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
                 "unsupported head_dim");
   constexpr float kBias = QT == kI8 ? 128.0f : 0.0f;
 
-  __shared__ uint64_t s_row[kMaxPartTokens];
-  __shared__ float4 s_fac[kMaxPartTokens][HPW];  // (ks, kz + bias, vs, vz + bias) per token, head
+  __shared__ uint32_t s_page[kQuantTablePages];
+  __shared__ float4 s_fac[kQuantTablePages][HPW];  // (ks, kz + bias, vs, vz + bias) per page, head
   __shared__ float s_m[NW][GW];
   __shared__ float s_l[NW][GW];
   __shared__ float s_acc[NW][GW][D];
 
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t wave = threadIdx.x / kWave;
-  const WorkItem item = grid_item<GT>(a);
-  const uint64_t kvh = item.g;
-  auto stage_factors = [&](uint32_t i, uint64_t phys) {
-#pragma unroll
-    for (int h = 0; h < HPW; ++h) {
-      const uint64_t f = phys * a.num_kv_heads + kvh + h;
-      s_fac[i][h] =
-          make_float4(a.k_scale[f], a.k_zero[f] + kBias, a.v_scale[f], a.v_zero[f] + kBias);
-    }
-  };
   Partition w;
-  if (!setup_partition<DT, D, GW, NTH, decltype(stage_factors), HPW>(a, item, s_row, w,
-                                                                      stage_factors))
+  uint32_t k0 = 0;
+  if (!setup_pages<DT, D, GW, NTH, HPW>(a, grid_item<GT>(a), kBias, s_page, s_fac, w, k0))
     return;
   const uint32_t cnt = w.cnt;
   const uint64_t out_row0 = w.out_row0;
+  const uint32_t p0 = w.part * a.part_tokens;
+  // a token's codes of head g start at (slot * Hkv + g) * D bytes
+  const uint64_t row_bytes = uint64_t(a.num_kv_heads) * D;
+  const uint64_t head0 = uint64_t(w.g) * D;
 
   const uint32_t row = lane / LPR;
   const uint32_t hw = (lane % LPR) / LPH;  // the lane's KV head within the workgroup's
@@ -939,8 +1012,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
     for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.0f;
   }
 
-  const char* kbase = static_cast<const char*>(a.k_cache) + hw * D + c * 16;
-  const char* vbase = static_cast<const char*>(a.v_cache) + hw * D + c * 16;
+  const char* kbase = static_cast<const char*>(a.k_cache) + head0 + hw * D + c * 16;
+  const char* vbase = static_cast<const char*>(a.v_cache) + head0 + hw * D + c * 16;
 
   for (uint32_t tb = wave * TT; tb < cnt; tb += NW * TT) {
     u32x4 kr[NLOAD], vr[NLOAD];
@@ -948,11 +1021,13 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
 #pragma unroll
     for (int k = 0; k < NLOAD; ++k) {
       const uint32_t li = tb + k * RPL + row;
-      const uint32_t ti = li < cnt ? li : cnt - 1;
-      const uint64_t off = s_row[ti];
+      const uint32_t p = p0 + (li < cnt ? li : cnt - 1);
+      const uint32_t kp = fastdiv(p, a.page_div);
+      const uint64_t slot = uint64_t(s_page[kp - k0]) * a.page_size + (p - kp * a.page_size);
+      const uint64_t off = slot * row_bytes;
       kr[k] = load16<TU::NT>(kbase + off);
       vr[k] = load16<TU::NT>(vbase + off);
-      fac[k] = s_fac[ti][hw];
+      fac[k] = s_fac[kp - k0][hw];
     }
 
     float sc[GT][NLOAD];
@@ -1365,8 +1440,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   constexpr int NB = D / 16;
   constexpr float kBias = QT == kI8 ? 128.0f : 0.0f;
 
-  __shared__ uint64_t s_row[kMaxPartTokens];
-  __shared__ float4 s_fac[kMaxPartTokens];  // (ks, kz + bias, vs, vz + bias) of each token
+  __shared__ uint32_t s_page[kQuantTablePages];
+  __shared__ float4 s_fac[kQuantTablePages][1];  // (ks, kz + bias, vs, vz + bias) of each page
   __shared__ __attribute__((aligned(16))) char s_tile[NW][TT * (KROW + VROW)];
   __shared__ float s_m[NW][GT];
   __shared__ float s_l[NW][GT];
@@ -1375,14 +1450,9 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   const uint32_t lane = threadIdx.x % kWave;
   // wave-uniform: kept in a scalar register, so the tile loop branches are scalar
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const WorkItem item = grid_item<GT>(a);
-  const uint64_t kvh = item.g;
-  auto stage_factors = [&](uint32_t i, uint64_t phys) {
-    const uint64_t f = phys * a.num_kv_heads + kvh;
-    s_fac[i] = make_float4(a.k_scale[f], a.k_zero[f] + kBias, a.v_scale[f], a.v_zero[f] + kBias);
-  };
   Partition w;
-  if (!setup_partition<DT, D, GT, NTH>(a, item, s_row, w, stage_factors)) return;
+  uint32_t k0 = 0;
+  if (!setup_pages<DT, D, GT, NTH, 1>(a, grid_item<GT>(a), kBias, s_page, s_fac, w, k0)) return;
   const uint32_t cnt = w.cnt;
 
   const uint32_t q4 = lane / 16;
@@ -1422,8 +1492,11 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   const uint32_t lr = lane / LPR, lc = lane % LPR;  // row-major load: row, 16-code chunk
   char* kt = s_tile[wave];
   char* vt = s_tile[wave] + TT * KROW;
-  const char* kbase = static_cast<const char*>(a.k_cache) + lc * 16;
-  const char* vbase = static_cast<const char*>(a.v_cache) + lc * 16;
+  // a token's codes of head g start at (slot * Hkv + g) * D bytes
+  const uint32_t p0 = w.part * a.part_tokens;
+  const uint64_t row_bytes = uint64_t(a.num_kv_heads) * D;
+  const char* kbase = static_cast<const char*>(a.k_cache) + uint64_t(w.g) * D + lc * 16;
+  const char* vbase = static_cast<const char*>(a.v_cache) + uint64_t(w.g) * D + lc * 16;
 
   uint32_t tb = wave * TT;
   if (tb < cnt) {
@@ -1434,7 +1507,10 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const uint32_t li = t0 + i * RPL + lr;
-        const uint64_t off = s_row[FULL || li < cnt ? li : cnt - 1];  // one byte per element
+        const uint32_t p = p0 + (FULL || li < cnt ? li : cnt - 1);
+        const uint32_t kp = fastdiv(p, a.page_div);
+        const uint64_t off =
+            (uint64_t(s_page[kp - k0]) * a.page_size + (p - kp * a.page_size)) * row_bytes;
         kr[i] = load16<TU::NT>(kbase + off);
         vr[i] = load16<TU::NT>(vbase + off);
       }
@@ -1470,7 +1546,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t t = tb + 16 * (j / 4) + 4 * q4 + (j % 4);
-        fac[j] = s_fac[FULL || t < cnt ? t : cnt - 1];
+        fac[j] = s_fac[fastdiv(p0 + (FULL || t < cnt ? t : cnt - 1), a.page_div) - k0][0];
         sv[j] = fac[j].x * fmaf(-fac[j].y, qsum, sacc[j / 4][j % 4]);
         if constexpr (!FULL) {
           if (t >= cnt) sv[j] = -INFINITY;

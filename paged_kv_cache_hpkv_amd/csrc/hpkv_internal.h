@@ -23,6 +23,14 @@ inline int dtype_bytes(int dt) { return dt == kF32 ? 4 : 2; }
 constexpr uint32_t kMaxPartTokens = 512;
 constexpr uint32_t kWidePartTokens = 1024;
 constexpr uint32_t kLongPartTokens = 2048;
+// The quantized kernels keep their row table per page: a partition may touch at
+// most this many pages (P tokens starting anywhere in a page of bs tokens touch
+// at most (P + bs - 2) / bs + 1): 512 tokens of 1-token pages, 1024 of 2-token
+// pages, 2048 of pages of 4 or more.
+constexpr uint32_t kQuantTablePages = 520;
+inline uint32_t partition_pages_max(uint32_t part_tokens, uint32_t page_size) {
+  return (part_tokens + page_size - 2) / page_size + 1;
+}
 
 // Division by a runtime divisor 1 <= d < 2^31 for numerators n < 2^31:
 // n / d == (n * mul) >> shift with shift = 31 + ceil(log2 d) and

@@ -30,7 +30,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared()
-    assert len(declared) == 28
+    assert len(declared) == 29
     out = subprocess.run(["nm", "-D", "--defined-only", hpkv.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(hpkv_\w+)", out))
@@ -228,6 +228,31 @@ def test_partition_tokens_per_shape():
     assert pt(hpkv.BF16, 8, 32, 0, 128, 16, 4096) == 0
     assert pt(hpkv.BF16, 8, 30, 8, 128, 16, 4096) == 0
     assert pt(9, 8, 32, 8, 128, 16, 4096) == 0
+
+
+def test_quant_partition_tokens_per_shape():
+    """Quantized pools: the same thresholds, among partitions whose pages fit the
+    kernels' 520-entry page table (2048 tokens needs pages of >= 4 tokens, 1024 of >= 2);
+    2048-token partitions on the matrix cores only."""
+    pt = hpkv.lib.hpkv_paged_attention_decode_quant_partition_tokens
+    fp8, i8 = hpkv.KV_FP8_E4M3, hpkv.KV_I8
+    # GQA 32/8 on the matrix cores (one KV head per workgroup): 8 head tiles
+    assert pt(hpkv.BF16, fp8, 256, 32, 8, 128, 16, 8192) == 2048   # 8 * 256 * 4
+    assert pt(hpkv.BF16, i8, 32, 32, 8, 128, 16, 8192) == 2048     # 8 * 32 * 4 = 1024
+    assert pt(hpkv.BF16, i8, 31, 32, 8, 128, 16, 8192) == 1024     # 992 < 1024
+    assert pt(hpkv.BF16, fp8, 4, 32, 8, 128, 16, 8192) == 1024     # 8 * 4 * 8 = 256
+    assert pt(hpkv.BF16, fp8, 3, 32, 8, 128, 16, 8192) == 512
+    # page sizes bound the partition: 1-token pages 512, 2- and 3-token pages 1024
+    assert pt(hpkv.BF16, fp8, 256, 32, 8, 128, 1, 8192) == 512
+    assert pt(hpkv.BF16, fp8, 256, 32, 8, 128, 2, 8192) == 1024
+    assert pt(hpkv.BF16, fp8, 256, 32, 8, 128, 3, 8192) == 1024
+    assert pt(hpkv.BF16, fp8, 256, 32, 8, 128, 4, 8192) == 2048
+    # VALU kernel, MHA 32/32 (two KV heads per workgroup: 16 head tiles): at most 1024
+    assert pt(hpkv.F16, i8, 64, 32, 32, 128, 16, 4096) == 1024     # 16 * 64 * 4
+    assert pt(hpkv.F32, fp8, 256, 32, 8, 128, 16, 8192) == 1024    # f32 q: VALU
+    assert pt(hpkv.BF16, fp8, 2, 32, 32, 128, 16, 4096) == 512     # 32 * 2 * 8 = 512 at 512
+    assert pt(hpkv.BF16, 5, 8, 32, 8, 128, 16, 4096) == 0          # not a quantized type
+    assert pt(hpkv.BF16, fp8, 8, 32, 8, 128, 0, 4096) == 0         # page size 0
 
 
 def test_reduce_argument_errors():

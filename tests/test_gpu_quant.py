@@ -147,3 +147,60 @@ def test_fp8_full_code_range(case):
         used = torch.from_numpy(used_slots(w)).to(DEV)
         codes = qt.k_codes.view(w.num_pages * w.page_size, -1)[used].cpu().numpy()
         assert len(np.unique(codes)) >= 250  # the decode read the whole code range
+
+
+def _shape(name, ctx, hq, hkv, d, bs, dtype="bf16", seed=41):
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx, dtype=np.int32)
+    num_pages, seq_ptr, bt = workloads._random_pool_tables(rng, ctx, bs, "u32")
+    return workloads.Workload(name, dtype, "u32", hq, hkv, d, bs, num_pages, ctx, seq_ptr, bt,
+                              d ** -0.5, chunks=workloads._decode_step_chunks(ctx), seed=seed)
+
+
+@pytest.mark.parametrize("bs,part", [(1, 512), (2, 1024), (3, 1024), (4, 2048), (16, 2048)])
+def test_quant_page_table_sizes(bs, part):
+    """The quantized kernels keep one row-table entry per page: 1-token pages fill
+    the 512 entries of a 512-token partition, 2-token pages 513 of 1024, 4-token
+    pages 513 of 2048; 3-token pages start partitions inside a page. Matrix cores
+    (GQA 32/8) and, where pages allow 1024-token partitions, the two-head VALU
+    kernel (MHA 16/16)."""
+    rng = np.random.default_rng(bs)
+    ctx = rng.integers(1, 4097, 64)
+    ctx[::7] = 4096
+    w = _shape(f"pages-bs{bs}", ctx, 32, 8, 128, bs)
+    got = hpkv.hpkv_paged_attention_decode_quant_partition_tokens(
+        w.torch_dtype, "fp8", w.num_seqs, 32, 8, 128, bs, w.max_context_len)
+    assert got == part
+    _step(w, "fp8" if bs % 2 else "i8")
+    if part > 512:
+        w = _shape(f"pages-valu-bs{bs}", ctx, 16, 16, 128, bs, dtype="f16")
+        assert hpkv.hpkv_paged_attention_decode_quant_partition_tokens(
+            w.torch_dtype, "i8", w.num_seqs, 16, 16, 128, bs, w.max_context_len) == 1024
+        _step(w, "i8")
+        _step(w, "fp8")
+
+
+def test_quant_malformed_page_in_a_long_partition():
+    """A page id past the pool in the second 2048-token partition of one sequence gives
+    that sequence NaN rows; every other sequence keeps finite results."""
+    ctx = np.full(64, 3000, dtype=np.int32)
+    w = _shape("pages-bad", ctx, 32, 8, 128, 16)
+    assert hpkv.hpkv_paged_attention_decode_quant_partition_tokens(
+        w.torch_dtype, "fp8", 64, 32, 8, 128, 16, w.max_context_len) == 2048
+    t = workloads.make_tensors(w, DEV)
+    qt = workloads.make_quant_tensors(w, "fp8", DEV)
+    bt = w.block_table.copy()
+    bad = 5
+    bt[int(w.seq_ptr[bad]) + 2048 // 16 + 3] = w.num_pages + 7  # partition 1 of sequence 5
+    out = torch.empty_like(t.q)
+    ws = hpkv.alloc_workspace(t.q, qt.k_codes, w.max_context_len)
+    hpkv.hpkv_paged_attention_decode_quant(
+        "fp8", t.q, qt.k_codes, qt.v_codes, qt.k_scale, qt.k_zero, qt.v_scale, qt.v_zero,
+        torch.from_numpy(bt).to(DEV), torch.from_numpy(w.seq_ptr).to(DEV),
+        torch.from_numpy(w.context_lens).to(DEV), w.scale, w.max_context_len, ws, out)
+    torch.cuda.synchronize()
+    o = out.float().cpu()
+    assert torch.isnan(o[bad]).all()
+    good = torch.ones(64, dtype=torch.bool)
+    good[bad] = False
+    assert torch.isfinite(o[good]).all()
