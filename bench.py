@@ -66,6 +66,7 @@ PREFILL_METRIC = "paged chunked-prefill attention: achieved TFLOP/s (causal flop
 METRIC = "paged decode: achieved KV HBM GB/s (% of peak) + sequences/s per layer"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_hpkv_amd", "csrc", "hpkv_decode.hip")
+QUANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_quant_traffic.json")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
 PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_hpkv_amd", "csrc", "hpkv_prefill.hip")
 
@@ -435,6 +436,14 @@ def algorithmic_quant_bytes(w):
                + per_seq * w.num_seqs)
 
 
+def quant_partition_kernel(w):
+    """The library's quantized partition kernel for this shape: the matrix-core one for
+    16-bit q, head_dim 32/64/128 and GQA groups of 4 or more, else the VALU one."""
+    mfma = (w.dtype != "f32" and w.head_dim in (32, 64, 128)
+            and (w.num_q_heads // w.num_kv_heads) % 4 == 0)
+    return "decode_partition_mfma_quant_kernel" if mfma else "decode_partition_quant_kernel"
+
+
 def main_quant(args, dev):
     w = make_workload(args)
     t = workloads.make_tensors(w, dev)
@@ -456,6 +465,7 @@ def main_quant(args, dev):
     achieved = alg / (dec_ms * 1e-3) / 1e9
     kv = quant_kv_bytes(w)
     value = kv / (ms_per_step * 1e-3) / 1e9
+    rec = recorded_traffic(w, QUANT_TRAFFIC_FILE, variant=f"/{args.kv}")
     line = {
         "metric": METRIC + " (quantized pools)",
         "value": round(value, 2),
@@ -487,19 +497,24 @@ def main_quant(args, dev):
             "warm_back_to_back_ms_per_step": round(warm_ms, 5),
         },
         "roofline": {
-            "kernel": "decode_order_kernel + decode_partition_quant_kernel + decode_reduce_kernel",
+            "kernel": f"decode_order_kernel + {quant_partition_kernel(w)} + decode_reduce_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": None if rec is None else rec.get("hbm_bytes_per_launch"),
             "algorithmic_bytes_per_launch": alg,
             "median_launch_ms": round(dec_ms, 5),
             "mean_launch_ms": round(rt["mean_ms"], 5),
             "launches": args.roofline_launches,
         },
     }
+    if rec is not None:
+        line["roofline"]["traffic_unit"] = ("HBM bytes per launch of the partition kernel "
+                                            "(rocprofv3 FETCH_SIZE + WRITE_SIZE)")
+    if args.copy_calibration:
+        calibration_copy(dev)
     if not args.no_cpu_baseline:
         step()  # leave `out` holding a full decode for the parity check
         torch.cuda.synchronize()
