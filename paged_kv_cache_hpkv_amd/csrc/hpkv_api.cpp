@@ -89,7 +89,7 @@ DecodePlan plan_decode(int dtype, bool quant, uint32_t num_seqs, uint32_t num_q_
     // quantized GQA on the matrix cores 0.222 at 1024, 0.209 at 2048).
     const bool mfma = hpkv::decode_quant_on_matrix_cores(dtype, head_dim, group);
     const uint32_t gt = hpkv::heads_per_workgroup_quant(dtype, head_dim, group);
-    const uint32_t hpw = !mfma && gt == group && num_kv_heads % 2 == 0 ? 2 : 1;
+    const uint32_t hpw = gt == group && num_kv_heads % 2 == 0 ? 2 : 1;
     for (uint32_t p : {hpkv::kLongPartTokens, hpkv::kWidePartTokens})
       if ((mfma || p != hpkv::kLongPartTokens) &&
           hpkv::partition_pages_max(p, page_size) <= hpkv::kQuantTablePages)

@@ -1424,11 +1424,13 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
 // 32 bytes so those 8-byte reads fall on distinct banks.
 // ---------------------------------------------------------------------------
 
-template <int DT, int QT, int D, int GT, class TU>
+template <int DT, int QT, int D, int GT, class TU, int HPW>
 __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_quant_kernel(
     const DecodeKernelArgs a) {
   static_assert(DT != kF32 && D % 32 == 0 && D <= 128 && GT <= 16, "unsupported shape");
-  constexpr int NW = TU::NW;
+  constexpr int NW = TU::NW;          // HPW adjacent KV heads, NW / HPW waves per head
+  constexpr int SPLIT = NW / HPW;
+  static_assert(NW % HPW == 0, "waves per head");
   constexpr int NTH = NW * kWave;
   constexpr int LPR = D / 16;       // lanes per row: 16 codes per lane
   constexpr int RPL = kWave / LPR;  // rows per wave load
@@ -1441,7 +1443,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   constexpr float kBias = QT == kI8 ? 128.0f : 0.0f;
 
   __shared__ uint32_t s_page[kQuantTablePages];
-  __shared__ float4 s_fac[kQuantTablePages][1];  // (ks, kz + bias, vs, vz + bias) of each page
+  __shared__ float4 s_fac[kQuantTablePages][HPW];  // (ks, kz + bias, vs, vz + bias) per page, head
   __shared__ __attribute__((aligned(16))) char s_tile[NW][TT * (KROW + VROW)];
   __shared__ float s_m[NW][GT];
   __shared__ float s_l[NW][GT];
@@ -1450,9 +1452,13 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   const uint32_t lane = threadIdx.x % kWave;
   // wave-uniform: kept in a scalar register, so the tile loop branches are scalar
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t hw = wave % HPW;   // the wave's KV head within the workgroup's heads
+  const uint32_t sub = wave / HPW;  // the wave's share of the partition's tiles
   Partition w;
   uint32_t k0 = 0;
-  if (!setup_pages<DT, D, GT, NTH, 1>(a, grid_item<GT>(a), kBias, s_page, s_fac, w, k0)) return;
+  if (!setup_pages<DT, D, HPW * GT, NTH, HPW>(a, grid_item<GT, (HPW > 1)>(a), kBias, s_page,
+                                              s_fac, w, k0))
+    return;
   const uint32_t cnt = w.cnt;
 
   const uint32_t q4 = lane / 16;
@@ -1472,7 +1478,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   for (int ks = 0; ks < KS; ++ks) {
     qop[ks] = u32x4{0, 0, 0, 0};
     if (col < GT) {
-      const char* qp = static_cast<const char*>(a.q) + ((w.out_row0 + col) * D + 32 * ks + 8 * q4) * 2;
+      const char* qp =
+          static_cast<const char*>(a.q) + ((w.out_row0 + hw * GT + col) * D + 32 * ks + 8 * q4) * 2;
       qop[ks] = *reinterpret_cast<const u32x4*>(qp) ^ qflip;
       float f[8];
       widen16<DT>(qop[ks], f);
@@ -1495,10 +1502,10 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   // a token's codes of head g start at (slot * Hkv + g) * D bytes
   const uint32_t p0 = w.part * a.part_tokens;
   const uint64_t row_bytes = uint64_t(a.num_kv_heads) * D;
-  const char* kbase = static_cast<const char*>(a.k_cache) + uint64_t(w.g) * D + lc * 16;
-  const char* vbase = static_cast<const char*>(a.v_cache) + uint64_t(w.g) * D + lc * 16;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (uint64_t(w.g) + hw) * D + lc * 16;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (uint64_t(w.g) + hw) * D + lc * 16;
 
-  uint32_t tb = wave * TT;
+  uint32_t tb = sub * TT;
   if (tb < cnt) {
     u32x4 kr[NL], vr[NL];
     // rows past the partition (only in its last tile) reuse its last row
@@ -1546,7 +1553,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t t = tb + 16 * (j / 4) + 4 * q4 + (j % 4);
-        fac[j] = s_fac[fastdiv(p0 + (FULL || t < cnt ? t : cnt - 1), a.page_div) - k0][0];
+        fac[j] = s_fac[fastdiv(p0 + (FULL || t < cnt ? t : cnt - 1), a.page_div) - k0][hw];
         sv[j] = fac[j].x * fmaf(-fac[j].y, qsum, sacc[j / 4][j % 4]);
         if constexpr (!FULL) {
           if (t >= cnt) sv[j] = -INFINITY;
@@ -1601,7 +1608,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
     else load_tile(std::false_type{}, tb);
     store_tile();
     while (true) {
-      const uint32_t tn = tb + NW * TT;
+      const uint32_t tn = tb + SPLIT * TT;
       const bool has_next = tn < cnt;
       if (has_next) {
         if (tn + TT <= cnt) load_tile(std::true_type{}, tn);
@@ -1634,7 +1641,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
     }
   }
   __syncthreads();
-  finish_partition<DT, D, GT, NW>(a, w, s_m, s_l, s_acc);
+  finish_partition<DT, D, GT, NW, HPW>(a, w, s_m, s_l, s_acc);
 }
 
 // One wave per (sequence, query head) with more than one partition: merges the
@@ -1816,9 +1823,24 @@ hipError_t launch_quant(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t str
 
 template <int DT, int QT, int D, int GT>
 hipError_t launch_quant_mfma(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
-  using TU = Tune<2, 0, true, 2>;
-  hipLaunchKernelGGL((decode_partition_mfma_quant_kernel<DT, QT, D, GT, TU>),
-                     dim3(uint32_t(nwg)), dim3(TU::NW * kWave), 0, stream, a);
+  // two waves per KV head; one KV head per workgroup, or two adjacent ones (whole GQA
+  // groups) whose codes are 2*d contiguous bytes of each token row
+  switch (a.kv_per_wg) {
+    case 1: {
+      using TU = Tune<2, 0, true, 2>;
+      hipLaunchKernelGGL((decode_partition_mfma_quant_kernel<DT, QT, D, GT, TU, 1>),
+                         dim3(uint32_t(nwg)), dim3(TU::NW * kWave), 0, stream, a);
+      break;
+    }
+    case 2: {
+      using TU = Tune<4, 0, true, 2>;
+      hipLaunchKernelGGL((decode_partition_mfma_quant_kernel<DT, QT, D, GT, TU, 2>),
+                         dim3(uint32_t(nwg)), dim3(TU::NW * kWave), 0, stream, a);
+      break;
+    }
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

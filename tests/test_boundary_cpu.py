@@ -236,12 +236,14 @@ def test_quant_partition_tokens_per_shape():
     2048-token partitions on the matrix cores only."""
     pt = hpkv.lib.hpkv_paged_attention_decode_quant_partition_tokens
     fp8, i8 = hpkv.KV_FP8_E4M3, hpkv.KV_I8
-    # GQA 32/8 on the matrix cores (one KV head per workgroup): 8 head tiles
-    assert pt(hpkv.BF16, fp8, 256, 32, 8, 128, 16, 8192) == 2048   # 8 * 256 * 4
-    assert pt(hpkv.BF16, i8, 32, 32, 8, 128, 16, 8192) == 2048     # 8 * 32 * 4 = 1024
-    assert pt(hpkv.BF16, i8, 31, 32, 8, 128, 16, 8192) == 1024     # 992 < 1024
-    assert pt(hpkv.BF16, fp8, 4, 32, 8, 128, 16, 8192) == 1024     # 8 * 4 * 8 = 256
-    assert pt(hpkv.BF16, fp8, 3, 32, 8, 128, 16, 8192) == 512
+    # GQA 32/8 on the matrix cores, two KV heads per workgroup: 4 head tiles (one KV
+    # head, 8 tiles, when the batch is too small even for 512-token partitions)
+    assert pt(hpkv.BF16, fp8, 256, 32, 8, 128, 16, 8192) == 2048   # 4 * 256 * 4
+    assert pt(hpkv.BF16, i8, 64, 32, 8, 128, 16, 8192) == 2048     # 4 * 64 * 4 = 1024
+    assert pt(hpkv.BF16, i8, 63, 32, 8, 128, 16, 8192) == 1024     # 1008 < 1024
+    assert pt(hpkv.BF16, fp8, 8, 32, 8, 128, 16, 8192) == 1024     # 4 * 8 * 8 = 256
+    assert pt(hpkv.BF16, fp8, 4, 32, 8, 128, 16, 8192) == 512      # 4 * 4 * 16 = 256
+    assert pt(hpkv.BF16, fp8, 3, 32, 8, 128, 16, 8192) == 512      # one KV head, 512
     # page sizes bound the partition: 1-token pages 512, 2- and 3-token pages 1024
     assert pt(hpkv.BF16, fp8, 256, 32, 8, 128, 1, 8192) == 512
     assert pt(hpkv.BF16, fp8, 256, 32, 8, 128, 2, 8192) == 1024

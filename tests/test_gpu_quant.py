@@ -165,7 +165,7 @@ def test_quant_page_table_sizes(bs, part):
     (GQA 32/8) and, where pages allow 1024-token partitions, the two-head VALU
     kernel (MHA 16/16)."""
     rng = np.random.default_rng(bs)
-    ctx = rng.integers(1, 4097, 64)
+    ctx = rng.integers(1, 4097, 128)
     ctx[::7] = 4096
     w = _shape(f"pages-bs{bs}", ctx, 32, 8, 128, bs)
     got = hpkv.hpkv_paged_attention_decode_quant_partition_tokens(
@@ -183,10 +183,10 @@ def test_quant_page_table_sizes(bs, part):
 def test_quant_malformed_page_in_a_long_partition():
     """A page id past the pool in the second 2048-token partition of one sequence gives
     that sequence NaN rows; every other sequence keeps finite results."""
-    ctx = np.full(64, 3000, dtype=np.int32)
+    ctx = np.full(128, 3000, dtype=np.int32)
     w = _shape("pages-bad", ctx, 32, 8, 128, 16)
     assert hpkv.hpkv_paged_attention_decode_quant_partition_tokens(
-        w.torch_dtype, "fp8", 64, 32, 8, 128, 16, w.max_context_len) == 2048
+        w.torch_dtype, "fp8", 128, 32, 8, 128, 16, w.max_context_len) == 2048
     t = workloads.make_tensors(w, DEV)
     qt = workloads.make_quant_tensors(w, "fp8", DEV)
     bt = w.block_table.copy()
@@ -201,6 +201,6 @@ def test_quant_malformed_page_in_a_long_partition():
     torch.cuda.synchronize()
     o = out.float().cpu()
     assert torch.isnan(o[bad]).all()
-    good = torch.ones(64, dtype=torch.bool)
+    good = torch.ones(128, dtype=torch.bool)
     good[bad] = False
     assert torch.isfinite(o[good]).all()
