@@ -225,12 +225,13 @@ int prepare_decode(int dtype, int index_type, const void* q, const void* k_cache
   // Longest-first dispatch pays when the grid is deeper than what the chip
   // holds at once; smaller grids keep the plain order and skip the pass.
   // Shared runs need the ordering pass (it drops the runs' followers), whatever the
-  // grid: matrix-core tiles only, groups of at most 8 query heads per tile (16/gt
-  // sequences per run), and pair indices that leave the run length room.
+  // grid: matrix-core tiles only, groups of at most 8 query heads per tile (runs of up
+  // to 32/gt sequences: two blocks of 16 tile columns), and pair indices that leave the
+  // run length room.
   const bool shared = share && !quant && w.bytes > 0 &&
                       hpkv::decode_on_matrix_cores(dtype, head_dim, group) && gt <= 8 &&
                       uint64_t(num_seqs) * max_parts <= hpkv::kPairMask;
-  a->share_block = shared ? 16 / gt : 1;
+  a->share_block = shared ? 32 / gt : 1;
   a->share_flags =
       shared ? reinterpret_cast<uint8_t*>(static_cast<char*>(workspace) + w.flags_offset)
              : nullptr;

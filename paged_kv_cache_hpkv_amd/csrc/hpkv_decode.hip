@@ -1195,7 +1195,7 @@ __device__ inline uint2 lds_read_tr16(const char* p) {
   return r;
 }
 
-template <int DT, int D, int GT, int HPW, int SPLIT, int MINW>
+template <int DT, int D, int GT, int HPW, int SPLIT, int MINW, int CB = 1>
 __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_kernel(
     const DecodeKernelArgs a) {
   static_assert(DT != kF32 && D % 32 == 0 && D <= 128 && GT <= 16, "unsupported shape");
@@ -1210,8 +1210,10 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
   constexpr int VROW = D * 2 + 32; // LDS bytes per V row (transposing 8-byte reads likewise)
   constexpr int KS = D / 32;       // score MFMAs per 16 tokens (d steps)
   constexpr int NB = D / 16;       // P.V MFMAs per tile (16-column blocks of d)
-  constexpr int R = 16 / GT;       // sequences a shared run can bring into the 16 columns
-  constexpr int NC = R * GT;       // columns in use when a run fills the tile (16)
+  // A shared run fills CB blocks of 16 tile columns (CB = 1 on the plain decode): each
+  // K and V operand read from LDS feeds CB matrix-core products.
+  constexpr int R = CB * 16 / GT;  // sequences a shared run can bring into the columns
+  constexpr int NC = R * GT;       // columns in use when a run fills them (16 * CB)
 
   // two-head workgroups: pool slots (32 bits) for up to kLongPartTokens tokens, so
   // the table stays at 8 KB and two workgroups still share a CU; else offsets
@@ -1242,27 +1244,35 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
   if (threadIdx.x < members)
     s_np[threadIdx.x] =
         threadIdx.x == 0 ? w.nparts : num_parts(a.context_lens[w.s + threadIdx.x], a.part_tokens);
-  const uint32_t ncol = members * GT;  // columns in use: member col / GT, head col % GT
+  const uint32_t ncol = members * GT;  // columns in use: member c / GT, head c % GT
 
   const uint32_t q4 = lane / 16;   // lane quarter
-  const uint32_t col = lane % 16;  // MFMA column
+  const uint32_t col = lane % 16;  // MFMA column; column c = 16 * cb + col of block cb
 
-  u32x4 qop[KS];
+  u32x4 qop[CB][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qop[ks] = u32x4{0, 0, 0, 0};
-    if (col < ncol) {
-      const uint64_t row =
-          w.out_row0 + uint64_t(col / GT) * a.num_q_heads + hw * GT + col % GT;
-      const char* qp = static_cast<const char*>(a.q) + (row * D + 32 * ks + 8 * q4) * 2;
-      qop[ks] = *reinterpret_cast<const u32x4*>(qp);
+  for (int cb = 0; cb < CB; ++cb) {
+    const uint32_t c = 16 * cb + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qop[cb][ks] = u32x4{0, 0, 0, 0};
+      if (c < ncol) {
+        const uint64_t row = w.out_row0 + uint64_t(c / GT) * a.num_q_heads + hw * GT + c % GT;
+        const char* qp = static_cast<const char*>(a.q) + (row * D + 32 * ks + 8 * q4) * 2;
+        qop[cb][ks] = *reinterpret_cast<const u32x4*>(qp);
+      }
     }
   }
 
-  f32x4 acc[NB];
+  f32x4 acc[CB][NB];
+  float m[CB], l[CB];  // running max (base 2) and weight sum of column 16 * cb + col
 #pragma unroll
-  for (int n = 0; n < NB; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY, l = 0.0f;  // running max (base 2) and weight sum of head `col`
+  for (int cb = 0; cb < CB; ++cb) {
+    m[cb] = -INFINITY;
+    l[cb] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[cb][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   const uint32_t lr = lane / LPR, lc = lane % LPR;  // row-major load: row, 16-byte chunk
   char* kt = s_tile[wave];
@@ -1301,51 +1311,58 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
       const bool has_next = tn < cnt;
       if (has_next) load_tile(tn);
 
-      // scores of tokens 16g + 4*q4 + r for head `col`
-      f32x4 sacc[2];
+      // scores of tokens 16g + 4*q4 + r for column `col` of each block
+      f32x4 sacc[CB][2];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        sacc[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) sacc[cb][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const u32x4 kop =
               *reinterpret_cast<const u32x4*>(kt + (16 * g + col) * KROW + (32 * ks + 8 * q4) * 2);
-          sacc[g] = mfma_16x16x32<DT>(kop, qop[ks], sacc[g]);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            sacc[cb][g] = mfma_16x16x32<DT>(kop, qop[cb][ks], sacc[cb][g]);
         }
       }
-      float z[8];
+      u32x4 pop[CB];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t t = 16 * (j / 4) + 4 * q4 + (j % 4);
-        const float zz = sacc[j / 4][j % 4] * a.scale_log2;
-        z[j] = tb + t < cnt ? zz : -INFINITY;
-      }
-      float mt = z[0];
+      for (int cb = 0; cb < CB; ++cb) {
+        float z[8];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) mt = fmaxf(mt, z[j]);
-      mt = col_max4(mt);
-      const float mn = fmaxf(m, mt);
-      const float mu = mn == -INFINITY ? 0.0f : mn;
-      const float corr = __builtin_amdgcn_exp2f(m - mu);
-      m = mn;
-      l *= corr;
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t t = 16 * (j / 4) + 4 * q4 + (j % 4);
+          const float zz = sacc[cb][j / 4][j % 4] * a.scale_log2;
+          z[j] = tb + t < cnt ? zz : -INFINITY;
+        }
+        float mt = z[0];
 #pragma unroll
-      for (int n = 0; n < NB; ++n) acc[n] *= corr;
+        for (int j = 1; j < 8; ++j) mt = fmaxf(mt, z[j]);
+        mt = col_max4(mt);
+        const float mn = fmaxf(m[cb], mt);
+        const float mu = mn == -INFINITY ? 0.0f : mn;
+        const float corr = __builtin_amdgcn_exp2f(m[cb] - mu);
+        m[cb] = mn;
+        l[cb] *= corr;
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[cb][n] *= corr;
 
-      uint32_t pw[4];
-      float psum = 0.0f;
+        uint32_t pw[4];
+        float psum = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const uint32_t b0 = round16<DT>(__builtin_amdgcn_exp2f(z[j] - mu));
-        const uint32_t b1 = round16<DT>(__builtin_amdgcn_exp2f(z[j + 1] - mu));
-        psum += widen_bits16<DT>(b0) + widen_bits16<DT>(b1);
-        pw[j / 2] = b0 | (b1 << 16);
+        for (int j = 0; j < 8; j += 2) {
+          const uint32_t b0 = round16<DT>(__builtin_amdgcn_exp2f(z[j] - mu));
+          const uint32_t b1 = round16<DT>(__builtin_amdgcn_exp2f(z[j + 1] - mu));
+          psum += widen_bits16<DT>(b0) + widen_bits16<DT>(b1);
+          pw[j / 2] = b0 | (b1 << 16);
+        }
+        // Columns c >= ncol carry q = 0: scores 0 (or -inf past the context), finite
+        // weights. A column of an MFMA result depends only on the same column of its B
+        // operand, so they never reach a served head, and they are never stored.
+        l[cb] += psum;
+        pop[cb] = u32x4{pw[0], pw[1], pw[2], pw[3]};
       }
-      // Columns col >= ncol carry q = 0: scores 0 (or -inf past the context), finite
-      // weights. A column of an MFMA result depends only on the same column of its B
-      // operand, so they never reach a served head, and they are never stored.
-      l += psum;
-      const u32x4 pop = u32x4{pw[0], pw[1], pw[2], pw[3]};
 
       // V^T: lane (q4, col) fetches row 4*q4 + col/4 (and 16 + that), columns
       // 16n + 4*(col%4) .. +3, and receives column 16n + col
@@ -1354,7 +1371,9 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
       for (int n = 0; n < NB; ++n) {
         const uint2 lo = lds_read_tr16(vrow0 + 32 * n);
         const uint2 hi = lds_read_tr16(vrow0 + 16 * VROW + 32 * n);
-        acc[n] = mfma_16x16x32<DT>(u32x4{lo.x, lo.y, hi.x, hi.y}, pop, acc[n]);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          acc[cb][n] = mfma_16x16x32<DT>(u32x4{lo.x, lo.y, hi.x, hi.y}, pop[cb], acc[cb][n]);
       }
       if (!has_next) break;
       store_tile();
@@ -1362,20 +1381,25 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
     }
   }
 
-  // the four lane quarters hold disjoint tokens of each head: add their sums
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
   __syncthreads();  // every wave is done with its tile before the tiles become merge space
   float(*s_acc)[NC][D] = reinterpret_cast<float(*)[NC][D]>(&s_tile[0][0]);
-  if (col < ncol) {
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
+  for (int cb = 0; cb < CB; ++cb) {
+    // the four lane quarters hold disjoint tokens of each column: add their sums
+    float ls = l[cb];
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    const uint32_t c = 16 * cb + col;
+    if (c < ncol) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_acc[wave][col][16 * n + 4 * q4 + r] = acc[n][r];
-    }
-    if (q4 == 0) {
-      s_m[wave][col] = m;
-      s_l[wave][col] = l;
+      for (int n = 0; n < NB; ++n) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_acc[wave][c][16 * n + 4 * q4 + r] = acc[cb][n][r];
+      }
+      if (q4 == 0) {
+        s_m[wave][c] = m[cb];
+        s_l[wave][c] = ls;
+      }
     }
   }
   __syncthreads();
@@ -1742,6 +1766,14 @@ inline bool mfma_eligible(int dtype, uint32_t head_dim, uint32_t group) {
 
 template <int DT, int D, int GT, int HPW, int SPLIT>
 hipError_t launch_pm_shape(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t stream) {
+  // shared runs longer than one block of 16 columns take two blocks
+  if constexpr (GT <= 8) {
+    if (a.share_block > 16 / GT) {
+      hipLaunchKernelGGL((decode_partition_mfma_kernel<DT, D, GT, HPW, SPLIT, 2, 2>),
+                         dim3(uint32_t(nwg)), dim3(HPW * SPLIT * kWave), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((decode_partition_mfma_kernel<DT, D, GT, HPW, SPLIT, 2>), dim3(uint32_t(nwg)),
                      dim3(HPW * SPLIT * kWave), 0, stream, a);
   return hipGetLastError();

@@ -3,7 +3,7 @@
 Sequences that alias the same pages ("Block-Paged KV Cache", "Element lookup
 through the block table"; the shared prefix pages of "Paged KV Cache · AI infra
 interview lesson", Step 5) are served by one workgroup on the matrix cores when
-they sit in one aligned block of 16/G consecutive sequences and a whole
+they sit in one aligned block of 32/G consecutive sequences and a whole
 partition covers the same page ids. Each sequence must get exactly the result
 it gets when it owns private copies of those pages: the shared entry point on
 the aliased batch, the plain decode on the aliased batch and the plain decode
@@ -102,8 +102,8 @@ def _subset(w, keep):
 @pytest.mark.parametrize("group_size", [16, 6, 3])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_aliased_prefix_equals_private_pages(group_size, dtype):
-    """Aligned groups (runs of four sequences fill the tile's columns), groups that cross
-    the blocks of four, and groups smaller than a block."""
+    """Aligned groups (runs of eight sequences fill two blocks of tile columns), groups that
+    cross the blocks of eight, and groups smaller than a block."""
     w = workloads.chunked_prefill(dtype=dtype, groups=5, group_size=group_size,
                                   prefix_tokens=2048, tail_lo=4, tail_hi=900)
     _check(w, expect_runs=True)
@@ -112,7 +112,7 @@ def test_aliased_prefix_equals_private_pages(group_size, dtype):
 @pytest.mark.parametrize("shape", [(64, 8, 128, 16), (32, 8, 64, 16), (32, 4, 32, 4),
                                    (128, 8, 128, 16), (32, 8, 128, 1)])
 def test_shared_runs_other_shapes(shape):
-    """Groups of 8 (runs of two), 16 (no runs), head sizes 64 and 32, 4-token pages
+    """Groups of 8 (runs of four), 16 (no runs), head sizes 64 and 32, 4-token pages
     (256 pages per partition, the most compared) and 1-token pages (too many pages to
     compare: no runs)."""
     hq, hkv, d, bs = shape
