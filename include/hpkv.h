@@ -310,7 +310,7 @@ int hpkv_paged_attention_decode_noalloc(int dtype, int index_type, const void* q
  * num_kv_heads a multiple of 4 and at most 8 per tile) a detection pass
  * compares the block tables, and a context partition that is full and covers
  * the same page ids for consecutive sequences of an aligned block of
- * 16 / (query heads per tile) sequences is read once, by one workgroup, for
+ * 32 / (query heads per tile) sequences is read once, by one workgroup, for
  * all of them. Elsewhere, and for batches that fit one partition per
  * sequence, it behaves as hpkv_paged_attention_decode. The detection pass and
  * the ordering pass run even when nothing is shared (a few microseconds).
