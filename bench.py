@@ -101,6 +101,9 @@ def parse():
                         "roofline then times that whole call")
     p.add_argument("--kv", default=None, choices=["i8", "fp8"],
                    help="decode over quantized pools (per page-slot, per KV head scales)")
+    p.add_argument("--graph", action="store_true",
+                   help="decode path: time the step as a HIP graph replay (captured once "
+                        "after the warmup; the roofline leg stays a direct call)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     p.add_argument("--warm", action="store_true",
@@ -720,9 +723,23 @@ def main():
         timer.flush()
         step()
     torch.cuda.synchronize()
-    st = timer.time(step, args.steps)            # the K timed steps
+    run = step
+    if args.graph:
+        # capture one step (every argument is a device address fixed at capture) and
+        # replay it; the cache-clearing writes stay outside the graph
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+    st = timer.time(run, args.steps)             # the K timed steps
     ms_per_step = st["median_ms"]
-    warm_ms = timer.warm(step, args.steps)
+    warm_ms = timer.warm(run, args.steps)
     # dominant work alone (ordering + partition kernels), same protocol
     rt = timer.time(step.partitions_only, args.roofline_launches)
     part_ms = rt["median_ms"]
@@ -761,7 +778,8 @@ def main():
             "sequences_per_s_per_layer": round(w.num_seqs / (ms_per_step * 1e-3), 1),
             "step": ("fused decode step (store of the ctx-1 row inside the decode launch)"
                      if step.fused else "slot mapping + store + decode (separate launches)")
-                    + (", decode by hpkv_paged_attention_decode_shared" if step.shared else ""),
+                    + (", decode by hpkv_paged_attention_decode_shared" if step.shared else "")
+                    + (", replayed from a HIP graph" if args.graph else ""),
         },
         "timing": {
             "protocol": timer.protocol(),
