@@ -327,11 +327,15 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
           if (int32_t(tb + 16 * (e / 4) + 4 * q4 + (e % 4)) > pos[jt]) sv[e] = -INFINITY;
         }
       }
-      float mt = smax(smax(smax(sv[0], sv[1]), smax(sv[2], sv[3])),
-                      smax(smax(sv[4], sv[5]), smax(sv[6], sv[7])));
-      mt = row_max4(mt);
-      const bool need = mt > mthr[jt];
-      if (__any(need)) {
+      // this lane's max of its eight scores (four v_maximum3); a row's max exceeds its
+      // threshold exactly when the max of one of its four lanes does, so the exchange
+      // between the lanes is only needed on the (rare) rescale branch
+      const float la = smax(smax(sv[0], sv[1]), sv[2]);
+      const float lb = smax(smax(sv[3], sv[4]), sv[5]);
+      const float lmax = smax(lb, smax(smax(sv[6], sv[7]), la));
+      if (__any(lmax > mthr[jt])) {
+        const float mt = row_max4(lmax);
+        const bool need = mt > mthr[jt];
         const float mcn = need ? mt * c : mc[jt];
         // no earlier weights on first use (mthr still -inf): the accumulators are zero
         const float corr = mthr[jt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mc[jt] - mcn);
