@@ -293,6 +293,28 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
     }
   };
 
+  // Direct-to-LDS tiles: this lane's byte offsets within a tile buffer of its K operand
+  // read at each k-step (row col of a 16-row block) and of its transposed V read for each
+  // 16-column block of O^T (the first of the two 16-row halves). Each is one register
+  // held across the loop, so every LDS read below is that register plus a constant (the
+  // buffer, the row block) that the read instruction carries as its offset. The empty asm
+  // keeps the compiler from splitting them back into a row part and a swizzle part that
+  // it would add again in every tile.
+  uint32_t koff[KS], voff[NB];
+  if constexpr (DL) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      koff[ks] = col * KROW + (((4 * ks + q4) ^ col) * 16);
+      asm volatile("" : "+v"(koff[ks]));
+    }
+    const uint32_t vr = 4 * q4 + col / 4;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      voff[nb] = vr * VROW + 8 * ((col % 4) & 1) + 16 * ((2 * nb + (col % 4) / 2) ^ (2 * (vr & 7)));
+      asm volatile("" : "+v"(voff[nb]));
+    }
+  }
+
   // One 32-key tile: scores, online softmax, P.V. MASK: some key of the tile lies past
   // the position of some row of this wave (the diagonal tiles); the others skip the mask.
   // buf: the LDS buffer, a compile-time constant on the direct-to-LDS path (each buffer a
@@ -309,7 +331,7 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const u32x4 kop = *reinterpret_cast<const u32x4*>(
-            DL ? &(b ? s_k1 : s_k0)[(16 * u + col) * KROW + (((4 * ks + q4) ^ col) * 16)]
+            DL ? &(b ? s_k1 : s_k0)[16 * u * KROW + koff[ks]]
                : &(b ? s_k1 : s_k0)[(16 * u + col) * KROW + (32 * ks + 8 * q4) * 2]);
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
@@ -356,12 +378,11 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
     // tile, columns 16*nb + 4*(col%4) .. +3, and receives column 16*nb + col.
     const uint32_t vr_row = 4 * q4 + col / 4;
     const char* vrow0 = &(b ? s_v1 : s_v0)[vr_row * VROW + 8 * (col % 4)];
-    const char* vrowd = &(b ? s_v1 : s_v0)[vr_row * VROW + 8 * ((col % 4) & 1)];
+    const char* vbuf = b ? s_v1 : s_v0;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const uint32_t vch = (2 * nb + (col % 4) / 2) ^ (2 * (vr_row & 7));
-      const uint2 lo = lds_read_tr16(DL ? vrowd + 16 * vch : vrow0 + 32 * nb);
-      const uint2 hi = lds_read_tr16(DL ? vrowd + 16 * VROW + 16 * vch : vrow0 + 16 * VROW + 32 * nb);
+      const uint2 lo = lds_read_tr16(DL ? vbuf + voff[nb] : vrow0 + 32 * nb);
+      const uint2 hi = lds_read_tr16(DL ? vbuf + 16 * VROW + voff[nb] : vrow0 + 16 * VROW + 32 * nb);
       const u32x4 vop = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) acc[jt][nb] = mfma_16x16x32<DT>(vop, pop[jt], acc[jt][nb]);
