@@ -404,7 +404,7 @@ int hpkv_paged_attention_decode_step(int dtype, int index_type, const void* q,
  *                 must be >= 1 when num_q_tokens > 0
  *   stream        hipStream_t or NULL; the call only enqueues (asynchronous)
  * Supported: dtype bf16 or f16, head_dim in {32, 64, 128, 256}, and
- * num_q_heads / num_kv_heads at most 256 (128 at head_dim 256); otherwise
+ * num_q_heads / num_kv_heads at most 128 (the rows of one workgroup); otherwise
  * HPKV_ERR_UNSUPPORTED. Argument errors (NULL pointers, zero sizes, heads not
  * divisible, NaN scale, misaligned buffers) return before any GPU work.
  * Malformed contents (caller error): a sequence whose chunk is longer than

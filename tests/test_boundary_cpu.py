@@ -168,8 +168,11 @@ def test_prefill_argument_errors():
     assert _prefill_call(d=96) == hpkv.ERR_UNSUPPORTED
     assert _prefill_call(d=16) == hpkv.ERR_UNSUPPORTED
     assert _prefill_call(dtype=hpkv.F32) == hpkv.ERR_UNSUPPORTED
-    assert _prefill_call(hq=512, hkv=1) == hpkv.ERR_UNSUPPORTED    # group wider than a workgroup
-    assert _prefill_call(hq=256, hkv=1, d=256) == hpkv.ERR_UNSUPPORTED
+    # a group wider than the 128 rows of a workgroup, at every head size
+    assert _prefill_call(hq=512, hkv=1) == hpkv.ERR_UNSUPPORTED
+    assert _prefill_call(hq=258, hkv=2) == hpkv.ERR_UNSUPPORTED
+    for d in (32, 64, 128, 256):
+        assert _prefill_call(hq=256, hkv=1, d=d) == hpkv.ERR_UNSUPPORTED, d
     # nothing to do: no sequences or no query rows
     assert _prefill_call(B=0, q=None, k=None, v=None, out=None) == hpkv.OK
     assert _prefill_call(nq=0, q=None, k=None, v=None, out=None, max_q=0) == hpkv.OK

@@ -46,6 +46,10 @@ SHAPES = {
     # 16 heads per KV head: 16 positions per workgroup
     "g16_d64_bs16": dict(groups=1, group_size=3, prefix_tokens=16, n_chunks=2, num_q_heads=32,
                          num_kv_heads=2, head_dim=64, bs=16, tail_lo=10, tail_hi=80),
+    # the widest group a workgroup holds (128 query heads per KV head: one position per
+    # workgroup at every head size)
+    "g128_d64_bs16": dict(groups=1, group_size=2, prefix_tokens=16, n_chunks=2, num_q_heads=128,
+                          num_kv_heads=1, head_dim=64, bs=16, tail_lo=5, tail_hi=40),
     # whole prompts from position 0, one chunk each, no prefix
     "from0_g4_d128": dict(groups=4, group_size=1, prefix_tokens=0, n_chunks=1, num_q_heads=8,
                           num_kv_heads=2, head_dim=128, bs=16, tail_lo=1, tail_hi=300),
