@@ -248,7 +248,8 @@ uint32_t hpkv_paged_attention_decode_quant_partition_tokens(int dtype, int kv_ty
  * heads per workgroup (16-bit dtype, GQA groups of 4 or more, even
  * num_kv_heads, large batches), num_pages * page_size must not exceed 2^32
  * (its row table holds 32-bit pool slots; such a pool takes at least 512 GiB):
- * HPKV_ERR_UNSUPPORTED otherwise.
+ * HPKV_ERR_UNSUPPORTED otherwise. The partition grid (head tiles x partitions x
+ * num_seqs workgroups) must stay below 2^24 workgroups (HPKV_ERR_UNSUPPORTED).
  * Malformed contents (caller error): a sequence with n < 0,
  * n > max_context_len, n beyond its slice, or a page id >= num_pages in the
  * pages it reads, gets NaN in all its outputs.
@@ -404,7 +405,10 @@ int hpkv_paged_attention_decode_step(int dtype, int index_type, const void* q,
  *                 must be >= 1 when num_q_tokens > 0
  *   stream        hipStream_t or NULL; the call only enqueues (asynchronous)
  * Supported: dtype bf16 or f16, head_dim in {32, 64, 128, 256}, and
- * num_q_heads / num_kv_heads at most 128 (the rows of one workgroup); otherwise
+ * num_q_heads / num_kv_heads at most 128 (the rows of one workgroup),
+ * num_pages * page_size below 2^32 (pool rows are kept in 32 bits) and fewer
+ * than 2^31 workgroups (ceil(min(max_q_len, num_q_tokens) * group / 128)
+ * position blocks x num_kv_heads x num_seqs); otherwise
  * HPKV_ERR_UNSUPPORTED. Argument errors (NULL pointers, zero sizes, heads not
  * divisible, NaN scale, misaligned buffers) return before any GPU work.
  * Malformed contents (caller error): a sequence whose chunk is longer than

@@ -173,6 +173,8 @@ def test_prefill_argument_errors():
     assert _prefill_call(hq=258, hkv=2) == hpkv.ERR_UNSUPPORTED
     for d in (32, 64, 128, 256):
         assert _prefill_call(hq=256, hkv=1, d=d) == hpkv.ERR_UNSUPPORTED, d
+    # pool rows (page * page_size + offset) are kept in 32 bits
+    assert _prefill_call(num_pages=(1 << 28) + 1, bs=16) == hpkv.ERR_UNSUPPORTED
     # nothing to do: no sequences or no query rows
     assert _prefill_call(B=0, q=None, k=None, v=None, out=None) == hpkv.OK
     assert _prefill_call(nq=0, q=None, k=None, v=None, out=None, max_q=0) == hpkv.OK
