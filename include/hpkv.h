@@ -241,9 +241,7 @@ uint32_t hpkv_paged_attention_decode_quant_partition_tokens(int dtype, int kv_ty
  *                     bytes (contents need no initialisation)
  * Requirements: q, k_cache, v_cache and workspace 16-byte aligned
  * (HPKV_ERR_INVALID_ARG otherwise); num_q_heads % num_kv_heads == 0;
- * head_dim * sizeof(dtype) a
- * multiple of 16 bytes with head_dim * sizeof(dtype) / 16 a power of two
- * <= 64 (bf16/f16: head_dim in {8,16,32,64,128,256}; f32: {4,...,256}),
+ * head_dim in {8, 16, 32, 64, 128, 256} (any dtype),
  * otherwise HPKV_ERR_UNSUPPORTED. When the matrix-core kernel serves two KV
  * heads per workgroup (16-bit dtype, GQA groups of 4 or more, even
  * num_kv_heads, large batches), num_pages * page_size must not exceed 2^32

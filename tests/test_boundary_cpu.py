@@ -120,6 +120,8 @@ def test_decode_argument_errors():
     assert _decode_call(q=ctypes.c_void_p(0x1008)) == hpkv.ERR_INVALID_ARG  # not 16-B aligned
     assert _decode_call(d=96) == hpkv.ERR_UNSUPPORTED
     assert _decode_call(d=512) == hpkv.ERR_UNSUPPORTED
+    for dt in (hpkv.F32, hpkv.BF16):
+        assert _decode_call(dtype=dt, d=4) == hpkv.ERR_UNSUPPORTED
     assert _decode_call(dtype=hpkv.F32, d=512) == hpkv.ERR_UNSUPPORTED
     # the two-head matrix-core shape keeps 32-bit pool slots: at most 2^32 slots
     assert _decode_call(B=1024, hq=8, hkv=2, num_pages=(1 << 28) + 1, ws_bytes=1 << 34) == \

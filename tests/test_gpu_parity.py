@@ -61,7 +61,7 @@ def test_prefix_sharing_chunked_prefill():
                                             (8, 1, 256, "f32"), (8, 2, 32, "f16"),
                                             (16, 4, 128, "f16"), (16, 2, 64, "f16"),
                                             (24, 2, 128, "bf16"), (32, 1, 64, "f16"),
-                                            (8, 2, 256, "bf16")])
+                                            (8, 2, 256, "bf16"), (4, 2, 8, "f32")])
 def test_other_head_shapes(hq, hkv, d, dtype):
     rng = np.random.default_rng(hq * 1000 + d)
     ctx = rng.integers(1, 1500, size=5).astype(np.int32)
