@@ -152,7 +152,7 @@ __global__ __launch_bounds__(NW * kWave, MINB) void prefill_mfma_kernel(const Pr
   const uint32_t per_xcd = gridDim.x / 8;
   const uint32_t work = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (work >= a.num_work) return;
-  const uint32_t pb = work % a.pos_blocks;
+  const uint32_t pb = a.pos_blocks - 1 - work % a.pos_blocks;  // a sequence's longest first
   const uint32_t sg = work / a.pos_blocks;
   const uint32_t s = sg % a.num_seqs;
   const uint32_t g = sg / a.num_seqs;
