@@ -29,9 +29,11 @@
 //    registers for the whole loop; lane layout A[l%16][8(l/16)+e],
 //    B[8(l/16)+e][l%16], D[4(l/16)+r][l%16]). Lane l ends with keys
 //    16u+4(l/16)+r of row l%16 of its column block.
-//  * Causal mask (key <= position) and online softmax in base 2 per row
-//    (scores pre-multiplied by scale*log2(e)); the row max is shared by the
-//    four lanes holding the row.
+//  * Causal mask (key <= position) and online softmax in base 2 per row (the
+//    scale times log2(e) enters in the exponent's FMA), with a lazy rescale:
+//    each lane tests the max of its own scores against the row's threshold,
+//    and the row max is exchanged among the four lanes holding the row only
+//    when a rescale is due.
 //  * O^T = V^T P^T. The contraction index k = 8(l/16)+e is mapped to key
 //    16(e/4)+4(l/16)+(e%4), where the scores already sit, so P needs no data
 //    movement. V^T comes straight from the row-major LDS tile through the
