@@ -18,9 +18,10 @@
 //    and both for quantized pools; ahead of them a one-workgroup ordering
 //    pass lists the partitions longest first, and after them the reduce
 //    kernel merges the partitions.
-//  * The workgroup first resolves every token of its partition to a pool row
-//    through the block table and keeps the row offsets in LDS; the token
-//    loop then needs no division and no table reads.
+//  * The workgroup first resolves its partition through the block table into
+//    an LDS table: every token's row offset (or 32-bit pool slot, on the
+//    matrix-core kernel with two KV heads), or for quantized pools every
+//    page's id and factors; the token loop then reads no block table.
 //  * VALU kernel: a 16-byte vector load per lane; a token row of head_dim
 //    elements is covered by LPR = head_dim*bytes/16 adjacent lanes, so one
 //    wave load fetches RPL = 64/LPR whole rows (coalesced 2x128 B per 256 B
@@ -1781,7 +1782,7 @@ hipError_t launch_pm_shape(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t 
 
 // Two waves share each KV head's tiles. A workgroup serves one KV head, or two
 // adjacent ones when a tile holds the whole GQA group: it then reads 2*d*b
-// contiguous bytes of each token row and covers 1024-token partitions, so its
+// contiguous bytes of each token row and covers 1024- or 2048-token partitions, so its
 // fixed costs (row table, first loads, merge) are spread over four times the
 // bytes. Measured on MI355X (bf16, d=128, GQA 32/8): 5.2 -> 5.6 TB/s on mixed
 // lengths, 5.6 -> 6.3 TB/s on equal ones.
