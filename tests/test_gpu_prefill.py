@@ -46,6 +46,11 @@ SHAPES = {
     # 16 heads per KV head: 16 positions per workgroup
     "g16_d64_bs16": dict(groups=1, group_size=3, prefix_tokens=16, n_chunks=2, num_q_heads=32,
                          num_kv_heads=2, head_dim=64, bs=16, tail_lo=10, tail_hi=80),
+    # one-token pages (every key its own page) and three-token pages
+    "g2_d64_bs1": dict(groups=2, group_size=2, prefix_tokens=5, n_chunks=2, num_q_heads=4,
+                       num_kv_heads=2, head_dim=64, bs=1, tail_lo=20, tail_hi=150),
+    "g4_d128_bs3": dict(groups=1, group_size=3, prefix_tokens=9, n_chunks=3, num_q_heads=8,
+                        num_kv_heads=2, head_dim=128, bs=3, tail_lo=30, tail_hi=200),
     # the widest group a workgroup holds (128 query heads per KV head: one position per
     # workgroup at every head size)
     "g128_d64_bs16": dict(groups=1, group_size=2, prefix_tokens=16, n_chunks=2, num_q_heads=128,
