@@ -562,7 +562,7 @@ __device__ inline bool setup_partition(const DecodeKernelArgs& a, const WorkItem
 // Same checks and malformed-input results as setup_partition; no fused store.
 template <int DT, int D, int NH, int NTH, int NKV, uint32_t CAPP>
 __device__ inline bool setup_pages(const DecodeKernelArgs& a, const WorkItem& it, float bias,
-                                   uint32_t (&s_page)[CAPP], float4 (&s_fac)[CAPP][NKV],
+                                   float vbias, uint32_t (&s_page)[CAPP], float4 (&s_fac)[CAPP][NKV],
                                    Partition& w, uint32_t& k0) {
   const uint32_t tid = threadIdx.x;
   uint64_t first = 0;
@@ -597,7 +597,7 @@ __device__ inline bool setup_pages(const DecodeKernelArgs& a, const WorkItem& it
       for (int h = 0; h < NKV; ++h) {
         const uint64_t f = ph * a.num_kv_heads + w.g + h;
         s_fac[i][h] = make_float4(a.k_scale[f], a.k_zero[f] + bias, a.v_scale[f],
-                                  a.v_zero[f] + bias);
+                                  a.v_zero[f] + vbias);
       }
     }
   }
@@ -940,10 +940,23 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
   constexpr int GW = HPW * GT;         // query heads of the workgroup
   static_assert(D % EPL == 0 && LPR <= kWave && (LPH & (LPH - 1)) == 0 && (HPW & (HPW - 1)) == 0,
                 "unsupported head_dim");
+  // With a 16-bit q the K products run as v_dot2 on exact 16-bit values of the codes,
+  // two products per instruction with fp32 accumulation (fp32 q: one FMA per element):
+  // fp8 codes by one packed conversion per two codes, in q's type; int8 codes
+  // (I8F16) as the f16 numbers 1024 + (code + 128), built two at a time by one v_perm
+  // from the code bytes, against q in f16 (a bf16 q multiplied by a power of two per
+  // head that brings its largest element into [2^14, 2^15): exact, and undone on each
+  // dot product). The K zero point then carries the 1024 + 128 offset. With one query
+  // head per KV head int8 codes keep the fp32 FMAs (measured faster on MI355X for
+  // MHA layers).
+  constexpr bool I8F16 = DT != kF32 && QT == kI8 && GT > 1;
+  constexpr bool DOT2 = DT != kF32 && (QT == kFP8 || I8F16);
   constexpr float kBias = QT == kI8 ? 128.0f : 0.0f;
+  constexpr float kKBias = I8F16 ? 1152.0f : kBias;
 
   __shared__ uint32_t s_page[kQuantTablePages];
-  __shared__ float4 s_fac[kQuantTablePages][HPW];  // (ks, kz + bias, vs, vz + bias) per page, head
+  // (ks, kz + K bias, vs, vz + bias) per page and head
+  __shared__ float4 s_fac[kQuantTablePages][HPW];
   __shared__ float s_m[NW][GW];
   __shared__ float s_l[NW][GW];
   __shared__ float s_acc[NW][GW][D];
@@ -952,7 +965,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
   const uint32_t wave = threadIdx.x / kWave;
   Partition w;
   uint32_t k0 = 0;
-  if (!setup_pages<DT, D, GW, NTH, HPW>(a, grid_item<GT>(a), kBias, s_page, s_fac, w, k0))
+  if (!setup_pages<DT, D, GW, NTH, HPW>(a, grid_item<GT>(a), kKBias, kBias, s_page, s_fac, w,
+                                        k0))
     return;
   const uint32_t cnt = w.cnt;
   const uint64_t out_row0 = w.out_row0;
@@ -965,20 +979,17 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
   const uint32_t hw = (lane % LPR) / LPH;  // the lane's KV head within the workgroup's
   const uint32_t c = lane % LPH;           // the lane's chunk of that head's row
 
-  // q of the lane's 16 elements of each head, and sum(q) over the head. With a
-  // 16-bit q and fp8 codes the K products run as v_dot2 on the codes' exact
-  // 16-bit values (one packed conversion per two codes, two products per
-  // instruction, fp32 accumulation), so q stays packed (qw); otherwise one FMA
-  // per element on fp32 values (qf): int8 codes take three instructions per
-  // pair to reach 16 bits, more than the products they would save.
-  constexpr bool DOT2 = DT != kF32 && QT == kFP8;
+  // q of the lane's 16 elements of each head, and sum(q) over the head: packed (qw)
+  // for the v_dot2 products, else fp32 (qf). qex: the exponent that undoes the
+  // scaling of a bf16 q converted to f16 (I8F16).
   float qf[DOT2 ? 1 : GT][EPL], qsum[GT];
+  int qex[GT];
   uint32_t qw[DOT2 ? GT : 1][EPL / 2];
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
     const char* qp =
         static_cast<const char*>(a.q) + ((out_row0 + hw * GT + hh) * D + c * EPL) * EQ;
-    float sq = 0.0f;
+    float sq = 0.0f, amax = 0.0f;
 #pragma unroll
     for (int h2 = 0; h2 < EPL * EQ / 16; ++h2) {
       const u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 16 * h2);
@@ -988,6 +999,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
       for (int e = 0; e < 16 / EQ; ++e) {
         if constexpr (DOT2) {
           sq += t[e];
+          amax = fmaxf(amax, fabsf(t[e]));
         } else {
           qf[hh][h2 * (16 / EQ) + e] = t[e];
           sq += t[e];
@@ -1001,6 +1013,22 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
       }
     }
     qsum[hh] = row_sum<LPH>(sq);
+    qex[hh] = 0;
+    if constexpr (I8F16 && DT == kBF16) {
+      // the head's largest |q| over its LPH lanes sets the power of two; elements
+      // under 2^-31 of it fall below f16's normal range (rounded toward zero there)
+#pragma unroll
+      for (int o = 1; o < LPH; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+      const int ex = __builtin_amdgcn_frexp_expf(amax) - 15;
+      qex[hh] = ex;
+#pragma unroll
+      for (int i = 0; i < EPL / 2; ++i) {
+        const float lo = ldexpf(__uint_as_float(qw[hh][i] << 16), -ex);
+        const float hi = ldexpf(__uint_as_float(qw[hh][i] & 0xffff0000u), -ex);
+        const auto h = __builtin_amdgcn_cvt_pkrtz(lo, hi);
+        __builtin_memcpy(&qw[hh][i], &h, 4);
+      }
+    }
   }
 
   float m[GT], l[GT], accz[GT], acc[GT][EPL];
@@ -1037,7 +1065,16 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
       const bool valid = tb + k * RPL + row < cnt;
       float kf[DOT2 ? 1 : EPL];
       uint32_t kw[DOT2 ? EPL / 2 : 1];
-      if constexpr (DOT2) {
+      if constexpr (I8F16) {
+        // code + 128 (sign bit flipped) in the low byte of the f16 0x64xx = 1024 + byte
+        const uint32_t cw[4] = {kr[k].x, kr[k].y, kr[k].z, kr[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t u = cw[i] ^ 0x80808080u;
+          kw[2 * i] = __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u);
+          kw[2 * i + 1] = __builtin_amdgcn_perm(0x64646464u, u, 0x05030402u);
+        }
+      } else if constexpr (DOT2) {
         const u32x4 lo = codes8_to_bits16<DT, QT>(uint2{kr[k].x, kr[k].y});
         const u32x4 hi = codes8_to_bits16<DT, QT>(uint2{kr[k].z, kr[k].w});
         kw[0] = lo.x; kw[1] = lo.y; kw[2] = lo.z; kw[3] = lo.w;
@@ -1051,7 +1088,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
         if constexpr (DOT2) {
 #pragma unroll
           for (int i = 0; i < EPL / 2; ++i) {
-            if constexpr (DT == kBF16)
+            if constexpr (DT == kBF16 && !I8F16)
               d0 = __builtin_amdgcn_fdot2_f32_bf16(as_pair<bf16x2>(kw[i]),
                                                    as_pair<bf16x2>(qw[hh][i]), d0, false);
             else
@@ -1062,7 +1099,8 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
 #pragma unroll
           for (int e = 0; e < EPL; ++e) d0 = fmaf(qf[hh][e], kf[e], d0);
         }
-        const float dot = row_sum<LPH>(d0);
+        float dot = row_sum<LPH>(d0);
+        if constexpr (I8F16 && DT == kBF16) dot = ldexpf(dot, qex[hh]);
         const float z = fac[k].x * fmaf(-fac[k].y, qsum[hh], dot) * a.scale_log2;
         sc[hh][k] = valid ? z : -INFINITY;
       }
@@ -1481,7 +1519,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
   const uint32_t sub = wave / HPW;  // the wave's share of the partition's tiles
   Partition w;
   uint32_t k0 = 0;
-  if (!setup_pages<DT, D, HPW * GT, NTH, HPW>(a, grid_item<GT, (HPW > 1)>(a), kBias, s_page,
+  if (!setup_pages<DT, D, HPW * GT, NTH, HPW>(a, grid_item<GT, (HPW > 1)>(a), kBias, kBias, s_page,
                                               s_fac, w, k0))
     return;
   const uint32_t cnt = w.cnt;

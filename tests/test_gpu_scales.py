@@ -54,17 +54,13 @@ def test_decode_step_scales(shape, kind):
     assert r["worst_ratio"] <= 1.0
 
 
-QUANT_SHAPES = {"gqa": (16, 4), "mha": (8, 8)}
+QUANT_SHAPES = {"gqa": (16, 4), "g2": (16, 8), "mha": (8, 8)}
 
 
-@pytest.mark.parametrize("kind", sorted(SCALES))
-@pytest.mark.parametrize("kv", ["fp8", "i8"])
-@pytest.mark.parametrize("shape", sorted(QUANT_SHAPES))
-def test_quant_decode_scales(shape, kv, kind):
-    hq, hkv = QUANT_SHAPES[shape]
-    w = _decode_workload(f"qscale_{shape}_{kind}", "bf16", hq, hkv, 128, _scale(kind, 128), 402)
-    print(f"[scales quant] {shape} {kv} {kind} scale={w.scale:g}", flush=True)
+def _quant_decode_check(w, kv, qmul=1.0):
     t = workloads.make_tensors(w, DEV)
+    if qmul != 1.0:  # a power of two: exact in bf16
+        t.q.mul_(qmul)
     qt = workloads.make_quant_tensors(w, kv, DEV)
     used = torch.zeros(w.num_pages * w.page_size, dtype=torch.bool)
     used[torch.from_numpy(used_slots(w))] = True
@@ -88,6 +84,29 @@ def test_quant_decode_scales(shape, kv, kind):
         host_threads())
     max_err, ratio, finite = decode_errors(w.dtype, host_bits(out), ref)
     assert finite and ratio <= 1.0, max_err
+
+
+@pytest.mark.parametrize("kind", sorted(SCALES))
+@pytest.mark.parametrize("kv", ["fp8", "i8"])
+@pytest.mark.parametrize("shape", sorted(QUANT_SHAPES))
+def test_quant_decode_scales(shape, kv, kind):
+    hq, hkv = QUANT_SHAPES[shape]
+    w = _decode_workload(f"qscale_{shape}_{kind}", "bf16", hq, hkv, 128, _scale(kind, 128), 402)
+    print(f"[scales quant] {shape} {kv} {kind} scale={w.scale:g}", flush=True)
+    _quant_decode_check(w, kv)
+
+
+@pytest.mark.parametrize("qmul", [2.0 ** 24, 2.0 ** -24])
+@pytest.mark.parametrize("kv", ["fp8", "i8"])
+@pytest.mark.parametrize("shape", sorted(QUANT_SHAPES))
+def test_quant_decode_query_magnitudes(shape, kv, qmul):
+    """Queries far outside f16's range (the VALU kernel takes int8 products in f16 after
+    scaling a bf16 q by a power of two per head), with the scale divided by the same
+    factor so the weights stay those of an ordinary batch."""
+    hq, hkv = QUANT_SHAPES[shape]
+    w = _decode_workload(f"qmag_{shape}", "bf16", hq, hkv, 128, 128 ** -0.5 / qmul, 404)
+    print(f"[q magnitude quant] {shape} {kv} q x {qmul:g}", flush=True)
+    _quant_decode_check(w, kv, qmul)
 
 
 @pytest.mark.parametrize("kind", sorted(SCALES))
