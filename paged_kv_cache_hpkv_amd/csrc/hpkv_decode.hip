@@ -1391,10 +1391,10 @@ __global__ __launch_bounds__(HPW * SPLIT * 64, MINW) void decode_partition_mfma_
         float psum = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
-          const uint32_t b0 = round16<DT>(__builtin_amdgcn_exp2f(z[j] - mu));
-          const uint32_t b1 = round16<DT>(__builtin_amdgcn_exp2f(z[j + 1] - mu));
-          psum += widen_bits16<DT>(b0) + widen_bits16<DT>(b1);
-          pw[j / 2] = b0 | (b1 << 16);
+          const uint32_t b = pack16<DT>(__builtin_amdgcn_exp2f(z[j] - mu),
+                                        __builtin_amdgcn_exp2f(z[j + 1] - mu));
+          psum += widen_bits16<DT>(b & 0xffffu) + widen_bits16<DT>(b >> 16);
+          pw[j / 2] = b;
         }
         // Columns c >= ncol carry q = 0: scores 0 (or -inf past the context), finite
         // weights. A column of an MFMA result depends only on the same column of its B
@@ -1526,6 +1526,7 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
 
   const uint32_t q4 = lane / 16;
   const uint32_t col = lane % 16;
+  const bool pg4 = a.page_size % 4 == 0;
 
   // Scores are kept raw, ks * (q.value - kz * sum(q)), and scaled by
   // c = |scale| * log2(e) inside the exponent; a negative scale is a sign flip of q
@@ -1613,13 +1614,28 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
       }
       float sv[8];
       float4 fac[8];
+      if (pg4) {
+        // the lane's tokens 4*q4 .. +3 of each 16-token group start at a multiple of 4
+        // (partitions and tiles do), so they share one page
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t t = tb + 16 * h + 4 * q4;
+          const float4 f = s_fac[fastdiv(p0 + (FULL ? t : min(t, cnt - 1)), a.page_div) - k0][hw];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) fac[4 * h + r] = f;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t t = tb + 16 * (j / 4) + 4 * q4 + (j % 4);
+          fac[j] = s_fac[fastdiv(p0 + (FULL || t < cnt ? t : cnt - 1), a.page_div) - k0][hw];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t t = tb + 16 * (j / 4) + 4 * q4 + (j % 4);
-        fac[j] = s_fac[fastdiv(p0 + (FULL || t < cnt ? t : cnt - 1), a.page_div) - k0][hw];
         sv[j] = fac[j].x * fmaf(-fac[j].y, qsum, sacc[j / 4][j % 4]);
         if constexpr (!FULL) {
-          if (t >= cnt) sv[j] = -INFINITY;
+          if (tb + 16 * (j / 4) + 4 * q4 + (j % 4) >= cnt) sv[j] = -INFINITY;
         }
       }
       float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
@@ -1646,12 +1662,11 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_mfma_q
       for (int j = 0; j < 8; j += 2) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[j], c, -mc));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[j + 1], c, -mc));
-        const uint32_t b0 = round16<DT>(p0 * fac[j].z);
-        const uint32_t b1 = round16<DT>(p1 * fac[j + 1].z);
+        const uint32_t b = pack16<DT>(p0 * fac[j].z, p1 * fac[j + 1].z);
         psum += p0 + p1;
-        zsum = fmaf(widen_bits16<DT>(b0), fac[j].w, zsum);
-        zsum = fmaf(widen_bits16<DT>(b1), fac[j + 1].w, zsum);
-        pw[j / 2] = b0 | (b1 << 16);
+        zsum = fmaf(widen_bits16<DT>(b & 0xffffu), fac[j].w, zsum);
+        zsum = fmaf(widen_bits16<DT>(b >> 16), fac[j + 1].w, zsum);
+        pw[j / 2] = b;
       }
       l += psum;
       accz += zsum;

@@ -45,18 +45,20 @@ __device__ inline f32x4 mfma_16x16x32(const u32x4 a, const u32x4 b, const f32x4 
   }
 }
 
-// fp32 -> 16-bit input type, round to nearest even; returns the bits.
+// Two fp32 values rounded to nearest even in the 16-bit input type and packed, lo in
+// the low half: one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 on gfx950.
 template <int DT>
-__device__ inline uint32_t round16(float x) {
+__device__ inline uint32_t pack16(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  uint32_t r;
   if constexpr (DT == kBF16) {
-    const uint32_t u = __float_as_uint(x);  // x is a finite softmax weight in [0, 1]
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const bf16x2 b = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+    __builtin_memcpy(&r, &b, 4);
   } else {
-    const _Float16 h = _Float16(x);
-    uint16_t b;
-    __builtin_memcpy(&b, &h, 2);
-    return b;
+    const f16x2 h = __builtin_convertvector(f32x2{lo, hi}, f16x2);
+    __builtin_memcpy(&r, &h, 4);
   }
+  return r;
 }
 
 template <int DT>
