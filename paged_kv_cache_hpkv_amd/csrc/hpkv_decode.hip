@@ -1044,19 +1044,54 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
   const char* kbase = static_cast<const char*>(a.k_cache) + head0 + hw * D + c * 16;
   const char* vbase = static_cast<const char*>(a.v_cache) + head0 + hw * D + c * 16;
 
-  for (uint32_t tb = wave * TT; tb < cnt; tb += NW * TT) {
-    u32x4 kr[NLOAD], vr[NLOAD];
-    float4 fac[NLOAD];
+  // PF: the rows of the wave's next tile are loaded while the current one is computed
+  // (kn / vn and the rows' table entries pn hold the tile in flight). Measured on
+  // MI355X: int8 pools with two query heads per KV head gain (their v_dot2 K path leaves
+  // the loop shorter than its loads' latency), the other shapes lose slightly and load
+  // each tile at the top of its iteration instead.
+  constexpr bool PF = I8F16 && GT == 2;
+  u32x4 kn[NLOAD], vn[NLOAD];
+  uint32_t pn[NLOAD];
+  auto load_rows = [&](uint32_t t0) {
 #pragma unroll
     for (int k = 0; k < NLOAD; ++k) {
-      const uint32_t li = tb + k * RPL + row;
+      const uint32_t li = t0 + k * RPL + row;
       const uint32_t p = p0 + (li < cnt ? li : cnt - 1);
       const uint32_t kp = fastdiv(p, a.page_div);
       const uint64_t slot = uint64_t(s_page[kp - k0]) * a.page_size + (p - kp * a.page_size);
       const uint64_t off = slot * row_bytes;
-      kr[k] = load16<TU::NT>(kbase + off);
-      vr[k] = load16<TU::NT>(vbase + off);
-      fac[k] = s_fac[kp - k0][hw];
+      kn[k] = load16<TU::NT>(kbase + off);
+      vn[k] = load16<TU::NT>(vbase + off);
+      pn[k] = kp - k0;
+    }
+  };
+  if constexpr (PF) {
+    if (wave * TT < cnt) load_rows(wave * TT);
+  }
+  for (uint32_t tb = wave * TT; tb < cnt; tb += NW * TT) {
+    u32x4 kr[NLOAD], vr[NLOAD];
+    float4 fac[NLOAD];
+    if constexpr (PF) {
+#pragma unroll
+      for (int k = 0; k < NLOAD; ++k) {
+        kr[k] = kn[k];
+        vr[k] = vn[k];
+        fac[k] = s_fac[pn[k]][hw];
+      }
+      if (tb + NW * TT < cnt) load_rows(tb + NW * TT);
+    } else {
+      // (the same loads written inline: the compiler schedules this form better here)
+#pragma unroll
+      for (int k = 0; k < NLOAD; ++k) {
+        const uint32_t li = tb + k * RPL + row;
+        const uint32_t p = p0 + (li < cnt ? li : cnt - 1);
+        const uint32_t kp = fastdiv(p, a.page_div);
+        const uint64_t slot = uint64_t(s_page[kp - k0]) * a.page_size + (p - kp * a.page_size);
+        const uint64_t off = slot * row_bytes;
+        kr[k] = load16<TU::NT>(kbase + off);
+        vr[k] = load16<TU::NT>(vbase + off);
+        fac[k] = s_fac[kp - k0][hw];
+      }
     }
 
     float sc[GT][NLOAD];
@@ -1891,7 +1926,8 @@ hipError_t launch_quant(const DecodeKernelArgs& a, uint64_t nwg, hipStream_t str
   // 4-head tiles hold 64 q floats per lane, so they load two rows per lane. Two
   // adjacent KV heads per workgroup read 2*d contiguous bytes of each token row:
   // rows of one 128-byte line per head stream markedly slower on MI355X.
-  using TU = Tune<2, GT >= 4 ? 2 : 8, true, 2>;
+  // (int8 codes with a 16-bit q and two heads per tile: 4 rows, prefetched a tile ahead)
+  using TU = Tune<2, GT >= 4 ? 2 : (DT != kF32 && QT == kI8 && GT == 2 ? 4 : 8), true, 2>;
   switch (a.kv_per_wg) {
     case 1:
       hipLaunchKernelGGL((decode_partition_quant_kernel<DT, QT, D, GT, TU, 1>),
