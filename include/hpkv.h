@@ -480,7 +480,11 @@ int hpkv_store_kvcache_quant(int dtype, int kv_type, const void* key, const void
  * (code + 1152 times q, a bf16 q first scaled per head by the power of two
  * that puts its largest magnitude in [2^14, 2^15); elements under 2^-31 of
  * that magnitude then fall below f16's normal range and are truncated),
- * summed in fp32. The workspace, its size function
+ * summed in fp32; with fp8 codes, an f16 or bf16 q and two query heads per KV
+ * head there, each weight times its V scale is rounded (nearest-even) to bf16
+ * before it multiplies the V codes, the V zero-point correction uses those
+ * rounded products and the denominator sums the unrounded fp32 weights.
+ * The workspace, its size function
  * (hpkv_paged_attention_decode_workspace_size with the same dtype), the
  * tail masking, the malformed-input NaN results and the argument errors are
  * those of hpkv_paged_attention_decode. Requirements: head_dim in

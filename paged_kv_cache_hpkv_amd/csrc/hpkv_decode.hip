@@ -1050,6 +1050,9 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
   // the loop shorter than its loads' latency), the other shapes lose slightly and load
   // each tile at the top of its iteration instead.
   constexpr bool PF = I8F16 && GT == 2;
+  // VP2: fp8 V rows taken two at a time on v_dot2_f32_bf16 (16-bit q, two query heads
+  // per KV head; measured on MI355X: faster there, slower with one head per KV head)
+  constexpr bool VP2 = QT == kFP8 && DT != kF32 && GT == 2 && NLOAD % 2 == 0;
   u32x4 kn[NLOAD], vn[NLOAD];
   uint32_t pn[NLOAD];
   auto load_rows = [&](uint32_t t0) {
@@ -1156,18 +1159,58 @@ __global__ __launch_bounds__(TU::NW * 64, TU::MINW) void decode_partition_quant_
       for (int e = 0; e < EPL; ++e) acc[hh][e] *= corr;
       m[hh] = mn;
     }
+    if constexpr (VP2) {
+      // Two rows per v_dot2: element e of rows k and k+1 as a bf16 pair (their fp8
+      // codes interleaved by v_perm, then one packed conversion per two), against the
+      // two rows' weights times V scale rounded to a bf16 pair. The zero-point term
+      // takes the same rounded weights; the denominator sums the unrounded ones.
 #pragma unroll
-    for (int k = 0; k < NLOAD; ++k) {
-      float vf[EPL];
-      codes16<QT>(vr[k], vf);
+      for (int k = 0; k < NLOAD; k += 2) {
+        const uint32_t c0[4] = {vr[k].x, vr[k].y, vr[k].z, vr[k].w};
+        const uint32_t c1[4] = {vr[k + 1].x, vr[k + 1].y, vr[k + 1].z, vr[k + 1].w};
+        uint32_t vp[EPL];
 #pragma unroll
-      for (int hh = 0; hh < GT; ++hh) {
-        const float p = __builtin_amdgcn_exp2f(sc[hh][k] - mu[hh]);
-        l[hh] += p;
-        const float pv = p * fac[k].z;  // weight times the token's V scale
-        accz[hh] = fmaf(pv, fac[k].w, accz[hh]);
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = __builtin_amdgcn_perm(c1[i], c0[i], 0x05010400u);
+          const uint32_t hi = __builtin_amdgcn_perm(c1[i], c0[i], 0x07030602u);
+          const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+          const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+          const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+          const auto a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+          __builtin_memcpy(&vp[4 * i], &a0, 4);
+          __builtin_memcpy(&vp[4 * i + 1], &a1, 4);
+          __builtin_memcpy(&vp[4 * i + 2], &a2, 4);
+          __builtin_memcpy(&vp[4 * i + 3], &a3, 4);
+        }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pv, vf[e], acc[hh][e]);
+        for (int hh = 0; hh < GT; ++hh) {
+          const float p0 = __builtin_amdgcn_exp2f(sc[hh][k] - mu[hh]);
+          const float p1 = __builtin_amdgcn_exp2f(sc[hh][k + 1] - mu[hh]);
+          l[hh] += p0 + p1;
+          const uint32_t wp = pack16<kBF16>(p0 * fac[k].z, p1 * fac[k + 1].z);
+          accz[hh] = fmaf(__uint_as_float(wp << 16), fac[k].w, accz[hh]);
+          accz[hh] = fmaf(__uint_as_float(wp & 0xffff0000u), fac[k + 1].w, accz[hh]);
+          const bf16x2 w2 = as_pair<bf16x2>(wp);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            acc[hh][e] =
+                __builtin_amdgcn_fdot2_f32_bf16(w2, as_pair<bf16x2>(vp[e]), acc[hh][e], false);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NLOAD; ++k) {
+        float vf[EPL];
+        codes16<QT>(vr[k], vf);
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh) {
+          const float p = __builtin_amdgcn_exp2f(sc[hh][k] - mu[hh]);
+          l[hh] += p;
+          const float pv = p * fac[k].z;  // weight times the token's V scale
+          accz[hh] = fmaf(pv, fac[k].w, accz[hh]);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pv, vf[e], acc[hh][e]);
+        }
       }
     }
   }
