@@ -475,13 +475,14 @@ int hpkv_store_kvcache_quant(int dtype, int kv_type, const void* key, const void
  * multiple of 4) each weight times its V scale is rounded (nearest-even) to
  * dtype before it multiplies the V codes, and the V zero-point correction
  * uses those rounded products; the denominator sums the unrounded fp32
- * weights. Off the matrix cores, int8 K codes against an f16 or bf16 q with two
- * or more query heads per KV head enter the scores as exact f16 products
+ * weights. Off the matrix cores, int8 K codes against an f16 or bf16 q with an
+ * even num_q_heads / num_kv_heads enter the scores as exact f16 products
  * (code + 1152 times q, a bf16 q first scaled per head by the power of two
  * that puts its largest magnitude in [2^14, 2^15); elements under 2^-31 of
  * that magnitude then fall below f16's normal range and are truncated),
- * summed in fp32; with fp8 codes, an f16 or bf16 q and two query heads per KV
- * head there, each weight times its V scale is rounded (nearest-even) to bf16
+ * summed in fp32; with fp8 codes, an f16 or bf16 q and num_q_heads /
+ * num_kv_heads even but not a multiple of 4 there (tiles of two query heads),
+ * each weight times its V scale is rounded (nearest-even) to bf16
  * before it multiplies the V codes, the V zero-point correction uses those
  * rounded products and the denominator sums the unrounded fp32 weights.
  * The workspace, its size function
