@@ -57,11 +57,17 @@ def test_decode_step_scales(shape, kind):
 QUANT_SHAPES = {"gqa": (16, 4), "g2": (16, 8), "mha": (8, 8)}
 
 
-def _quant_decode_check(w, kv, qmul=1.0):
+def _quant_decode_check(w, kv, qmul=1.0, spread=None):
     t = workloads.make_tensors(w, DEV)
     if qmul != 1.0:  # a power of two: exact in bf16
         t.q.mul_(qmul)
     qt = workloads.make_quant_tensors(w, kv, DEV)
+    if spread is not None:  # per-page scales 2^-u, u uniform in the given ranges
+        g = torch.Generator(device="cpu")
+        g.manual_seed(405)
+        for sc, (lo, hi) in ((qt.k_scale, spread[0]), (qt.v_scale, spread[1])):
+            u = lo + (hi - lo) * torch.rand(sc.shape, generator=g)
+            sc.copy_(torch.exp2(-u).to(sc.device))
     used = torch.zeros(w.num_pages * w.page_size, dtype=torch.bool)
     used[torch.from_numpy(used_slots(w))] = True
     pages = used.view(w.num_pages, w.page_size).any(1).to(DEV)
@@ -107,6 +113,23 @@ def test_quant_decode_query_magnitudes(shape, kv, qmul):
     w = _decode_workload(f"qmag_{shape}", "bf16", hq, hkv, 128, 128 ** -0.5 / qmul, 404)
     print(f"[q magnitude quant] {shape} {kv} q x {qmul:g}", flush=True)
     _quant_decode_check(w, kv, qmul)
+
+
+# exponent ranges of the K and V page scales: V values stay within a few units, so the
+# 16-bit output rounding stays far inside the tolerance
+SPREAD = {"fp8": ((4.0, 12.0), (8.0, 20.0)), "i8": ((4.0, 12.0), (6.0, 20.0))}
+
+
+@pytest.mark.parametrize("kv", ["fp8", "i8"])
+@pytest.mark.parametrize("shape", sorted(QUANT_SHAPES))
+def test_quant_decode_page_scale_spread(shape, kv):
+    """Page scales that differ by up to 2^12 between the pages one partition reads (the
+    VALU kernel pairs rows of different pages in one v_dot2 with fp8 codes, each with its
+    own weight times V scale), against the oracle's per-page dequantization."""
+    hq, hkv = QUANT_SHAPES[shape]
+    w = _decode_workload(f"qspread_{shape}", "bf16", hq, hkv, 128, 128 ** -0.5, 406)
+    print(f"[page scale spread quant] {shape} {kv}", flush=True)
+    _quant_decode_check(w, kv, spread=SPREAD[kv])
 
 
 @pytest.mark.parametrize("kind", sorted(SCALES))
